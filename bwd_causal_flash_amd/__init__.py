@@ -1,0 +1,296 @@
+"""Causal attention forward/backward for one context-parallel rank, as HIP
+kernels for AMD Instinct MI355X (gfx950) behind a small C ABI
+(include/cpattn.h).
+
+This module is the Python binding: it turns torch tensors into the C
+descriptors (shapes, strides, device pointers, the current HIP stream) and
+calls libcpattn.so.  PyTorch only provides device memory and streams; every
+step of the computation runs in the library's kernels.  Entry points keep
+the C names: attn_fwd, attn_bwd, attn_merge_lse, pack_saved, unpack_saved.
+
+Tensor layouts
+  BSHD: q [B, Sq, Hq, Dqk], k [B, Sk, Hkv, Dqk], v [B, Sk, Hkv, Dv],
+        o/do [B, Sq, Hq, Dv], lse [B, Hq, Sq] (fp32)
+  THD : q [Tq, Hq, Dqk], ..., lse [Hq, Tq]; sequence n occupies physical
+        rows [cu_seqlens[n], cu_seqlens[n+1]) of which the first
+        seqused[n] are real (TransformerEngine PR 3149, "Enable FA4 for
+        context-parallel attention", Description).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import (CPA_BF16, CPA_FP32, CPA_FLAG_DETERMINISTIC, CpaError,  # noqa: F401
+                   MergeDesc, PackDesc, Problem, STATUS_CODE)
+
+__all__ = [
+    "attn_fwd", "attn_bwd", "attn_merge_lse", "pack_saved", "unpack_saved",
+    "pack_saved_size", "Varlen", "CpaError", "forward", "backward",
+    "workspace_error_flag", "library",
+]
+
+
+def library():
+    """The loaded libcpattn (raises if it has not been built)."""
+    return _lib.load()
+
+
+@dataclasses.dataclass
+class Varlen:
+    """Packed-THD metadata (device int32 tensors, host max lengths)."""
+    cu_seqlens_q: torch.Tensor
+    cu_seqlens_k: torch.Tensor
+    seqused_q: torch.Tensor
+    seqused_k: torch.Tensor
+    max_seqlen_q: int
+    max_seqlen_k: int
+    bottom_right: bool = False
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return CPA_BF16
+    if t.dtype == torch.float32:
+        return CPA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _strides3(t: torch.Tensor, thd: bool):
+    if t is None:
+        return (0, 0, 0)
+    st = t.stride()
+    if st[-1] != 1:
+        raise ValueError("the head dim must be contiguous")
+    return (0, st[0], st[1]) if thd else (st[0], st[1], st[2])
+
+
+def _fill_problem(q, k, v, *, causal, scale, out_dtype, q_segments, k_pos_begin,
+                  varlen: Optional[Varlen]) -> Problem:
+    p = Problem()
+    thd = q.dim() == 3
+    if thd != (varlen is not None):
+        raise ValueError("3-D (THD) tensors need varlen metadata, 4-D (BSHD) must not have it")
+    p.layout = 1 if thd else 0
+    p.in_dtype = _dtype_code(q)
+    p.out_dtype = out_dtype
+    if thd:
+        p.batch = 1
+        p.seqlen_q, p.heads_q, p.d_qk = q.shape
+        p.seqlen_k, p.heads_kv = k.shape[0], k.shape[1]
+        p.num_seqs = varlen.seqused_q.numel()
+        p.max_seqlen_q = int(varlen.max_seqlen_q)
+        p.max_seqlen_k = int(varlen.max_seqlen_k)
+        p.cu_seqlens_q = varlen.cu_seqlens_q.data_ptr()
+        p.cu_seqlens_k = varlen.cu_seqlens_k.data_ptr()
+        p.seqused_q = varlen.seqused_q.data_ptr()
+        p.seqused_k = varlen.seqused_k.data_ptr()
+        p.thd_bottom_right = int(bool(varlen.bottom_right))
+    else:
+        p.batch, p.seqlen_q, p.heads_q, p.d_qk = q.shape
+        p.seqlen_k, p.heads_kv = k.shape[1], k.shape[2]
+    p.d_v = v.shape[-1]
+    p.q_stride = _strides3(q, thd)
+    p.k_stride = _strides3(k, thd)
+    p.v_stride = _strides3(v, thd)
+    p.softmax_scale = float(1.0 / math.sqrt(p.d_qk) if scale is None else scale)
+    p.causal = int(bool(causal))
+    segs = list(q_segments or [])
+    if len(segs) > _lib.CPA_MAX_SEGMENTS:
+        raise ValueError("at most 8 query segments")
+    p.num_q_segments = len(segs)
+    for i, (r, pos) in enumerate(segs):
+        p.q_seg_row[i] = int(r)
+        p.q_seg_pos[i] = int(pos)
+    p.k_pos_begin = int(k_pos_begin)
+    return p
+
+
+def _lse_strides(lse: torch.Tensor, thd: bool):
+    st = lse.stride()
+    if st[-1] != 1:
+        raise ValueError("LSE rows must be contiguous")
+    return (0, st[0]) if thd else (st[0], st[1])
+
+
+def workspace_error_flag(ws: torch.Tensor) -> int:
+    """The device metadata error flag (first int32 of a workspace); syncs."""
+    return int(ws[:4].view(torch.int32).item())
+
+
+def attn_fwd(q, k, v, o, lse, *, causal=True, scale=None, q_segments=None, k_pos_begin=0,
+             varlen: Optional[Varlen] = None, workspace=None, stream=None) -> torch.Tensor:
+    """Forward into preallocated o (bf16 or fp32) and lse (fp32).
+
+    q_segments: BSHD query positions as [(row_begin, pos_begin), ...]
+    (default: one segment at 0, top-left causal); k_pos_begin: position of
+    key row 0.  Returns the workspace (its first int32 is the THD metadata
+    error flag).
+    """
+    lib = _lib.load()
+    p = _fill_problem(q, k, v, causal=causal, scale=scale, out_dtype=_dtype_code(o),
+                      q_segments=q_segments, k_pos_begin=k_pos_begin, varlen=varlen)
+    thd = p.layout == 1
+    p.o_stride = _strides3(o, thd)
+    p.lse_stride = _lse_strides(lse, thd)
+    need = lib.attn_fwd_workspace_size(ctypes.byref(p))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                      _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    _lib.check(st, "attn_fwd")
+    return workspace
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, *, causal=True, scale=None, q_segments=None,
+             k_pos_begin=0, varlen: Optional[Varlen] = None, workspace=None, flags=0,
+             stream=None) -> torch.Tensor:
+    """Backward into preallocated dq, dk, dv.  Returns the workspace."""
+    lib = _lib.load()
+    p = _fill_problem(q, k, v, causal=causal, scale=scale, out_dtype=_dtype_code(dq),
+                      q_segments=q_segments, k_pos_begin=k_pos_begin, varlen=varlen)
+    thd = p.layout == 1
+    p.o_stride = _strides3(o, thd)
+    p.do_stride = _strides3(dout, thd)
+    p.dq_stride = _strides3(dq, thd)
+    p.dk_stride = _strides3(dk, thd)
+    p.dv_stride = _strides3(dv, thd)
+    p.lse_stride = _lse_strides(lse, thd)
+    need = lib.attn_bwd_workspace_size(ctypes.byref(p))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                      _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                      workspace.numel(), int(flags), _stream_handle(stream))
+    _lib.check(st, "attn_bwd")
+    return workspace
+
+
+def bwd_workspace_bytes(q, k, v, *, varlen=None, **kw) -> int:
+    p = _fill_problem(q, k, v, causal=True, scale=None, out_dtype=0, q_segments=None,
+                      k_pos_begin=0, varlen=varlen)
+    return int(_lib.load().attn_bwd_workspace_size(ctypes.byref(p)))
+
+
+def _as4(o: torch.Tensor, lse: torch.Tensor):
+    """Merge/pack tensors as [B, S, H, D] and LSE as [B, H, S]."""
+    if o.dim() == 3:
+        o = o.unsqueeze(0)
+        lse = lse.unsqueeze(0)
+    return o, lse
+
+
+def attn_merge_lse(o_acc, lse_acc, o_part, lse_part, o_out=None, lse_out=None, *, stream=None):
+    """(o_out, lse_out) = LSE merge of (o_acc, lse_acc) and (o_part,
+    lse_part).  Defaults to in place on the accumulator.  O tensors are
+    [B, S, H, D] or [S, H, D]; LSE [B, H, S] or [H, S]."""
+    lib = _lib.load()
+    if o_out is None:
+        o_out = o_acc
+    if lse_out is None:
+        lse_out = lse_acc
+    a4, la = _as4(o_acc, lse_acc)
+    p4, lp = _as4(o_part, lse_part)
+    o4, lo = _as4(o_out, lse_out)
+    d = MergeDesc()
+    d.batch, d.seqlen, d.heads, d.d_v = a4.shape
+    d.acc_dtype, d.part_dtype, d.out_dtype = _dtype_code(a4), _dtype_code(p4), _dtype_code(o4)
+    for name, t in (("acc_stride", a4), ("part_stride", p4), ("out_stride", o4)):
+        if t.stride(-1) != 1:
+            raise ValueError("last dim must be contiguous")
+        setattr(d, name, tuple(t.stride()[:3]))
+    for name, t in (("lse_acc_stride", la), ("lse_part_stride", lp), ("lse_out_stride", lo)):
+        if t.stride(-1) != 1:
+            raise ValueError("LSE rows must be contiguous")
+        setattr(d, name, tuple(t.stride()[:2]))
+    st = lib.attn_merge_lse(ctypes.byref(d), _ptr(a4), _ptr(la), _ptr(p4), _ptr(lp), _ptr(o4),
+                            _ptr(lo), _stream_handle(stream))
+    _lib.check(st, "attn_merge_lse")
+    return o_out, lse_out
+
+
+def _pack_desc(o, lse, groups, force_int64):
+    o4, l3 = _as4(o, lse)
+    d = PackDesc()
+    d.batch, d.seqlen, d.heads, d.d_v = o4.shape
+    d.o_dtype = _dtype_code(o4)
+    d.groups = int(groups)
+    if o4.stride(-1) != 1 or l3.stride(-1) != 1:
+        raise ValueError("last dims must be contiguous")
+    d.o_stride = tuple(o4.stride()[:3])
+    d.lse_stride = tuple(l3.stride()[:2])
+    d.force_int64 = int(bool(force_int64))
+    return d, o4, l3
+
+
+def pack_saved_size(o, lse, groups) -> int:
+    d, _, _ = _pack_desc(o, lse, groups, False)
+    return int(_lib.load().pack_saved_size(ctypes.byref(d)))
+
+
+def pack_saved(o, lse, groups, buf=None, *, force_int64=False, stream=None) -> torch.Tensor:
+    """Pack O and the raw fp32 LSE into per-head-group segments; returns the
+    uint8 buffer."""
+    lib = _lib.load()
+    d, o4, l3 = _pack_desc(o, lse, groups, force_int64)
+    need = lib.pack_saved_size(ctypes.byref(d))
+    if buf is None:
+        buf = torch.empty(need, dtype=torch.uint8, device=o.device)
+    st = lib.pack_saved(ctypes.byref(d), _ptr(o4), _ptr(l3), _ptr(buf), buf.numel(),
+                        _stream_handle(stream))
+    _lib.check(st, "pack_saved")
+    return buf
+
+
+def unpack_saved(buf, o, lse, groups, *, force_int64=False, stream=None):
+    """Inverse of pack_saved, into preallocated o and lse."""
+    lib = _lib.load()
+    d, o4, l3 = _pack_desc(o, lse, groups, force_int64)
+    st = lib.unpack_saved(ctypes.byref(d), _ptr(buf), buf.numel(), _ptr(o4), _ptr(l3),
+                          _stream_handle(stream))
+    _lib.check(st, "unpack_saved")
+    return o, lse
+
+
+# ------------------------------------------------------------- allocating
+
+def _lse_shape(q, thd):
+    return (q.shape[1], q.shape[0]) if thd else (q.shape[0], q.shape[2], q.shape[1])
+
+
+def forward(q, k, v, *, out_dtype=None, causal=True, scale=None, q_segments=None,
+            k_pos_begin=0, varlen=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Allocate o, lse and run attn_fwd.  THD padding rows of the returned
+    tensors are uninitialised (the kernels never write them)."""
+    thd = q.dim() == 3
+    o = torch.empty(*q.shape[:-1], v.shape[-1], dtype=out_dtype or q.dtype, device=q.device)
+    lse = torch.empty(*_lse_shape(q, thd), dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, o, lse, causal=causal, scale=scale, q_segments=q_segments,
+             k_pos_begin=k_pos_begin, varlen=varlen, stream=stream)
+    return o, lse
+
+
+def backward(q, k, v, o, dout, lse, *, out_dtype=None, causal=True, scale=None,
+             q_segments=None, k_pos_begin=0, varlen=None, stream=None):
+    """Allocate dq, dk, dv and run attn_bwd."""
+    dt = out_dtype or q.dtype
+    dq = torch.empty(q.shape, dtype=dt, device=q.device)
+    dk = torch.empty(k.shape, dtype=dt, device=q.device)
+    dv = torch.empty(v.shape, dtype=dt, device=q.device)
+    attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, causal=causal, scale=scale,
+             q_segments=q_segments, k_pos_begin=k_pos_begin, varlen=varlen, stream=stream)
+    return dq, dk, dv

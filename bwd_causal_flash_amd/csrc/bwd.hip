@@ -1,0 +1,427 @@
+// Causal attention backward on gfx950: recompute P from the saved LSE,
+// D = rowsum(dO * O), then dQ, dK, dV.
+//
+// Three launches on the caller's stream:
+//   pre   D_i = <dO_i, O_i> in fp32 from the saved O, and zero the fp32 dQ
+//         accumulator (only real rows; padding is never touched);
+//   main  key-outer: one workgroup owns 128 keys of one kv head (32 keys
+//         per wave) and walks the query heads of its GQA group and the query
+//         tiles that can see those keys;
+//   post  dQ = s * acc, rounded to the output type.
+//
+// In the main kernel each wave computes S = Q K_w^T and dP = dO V_w^T for
+// its 32 keys (lane = key column; K_w and V_w stay in registers), forms
+// P = exp(S - LSE) (zero where masked or where LSE = -inf) and dS = P (dP -
+// D), and accumulates dV^T += dO^T P and dK^T += Q^T dS.  The reduction
+// operands dO^T and Q^T are read from the row-major LDS tiles with the
+// transpose reads; P and dS feed the products directly from the
+// accumulators because the Q rows were loaded in perm32 order.  dS^T goes
+// to LDS once, and the four waves then split the dQ tile (dS K over all 128
+// keys of the workgroup) and add it to the fp32 accumulator with atomics.
+// All five products are bf16 x bf16 -> fp32 on the matrix cores.
+//
+// Head dim 512: dK, dV and dQ are produced in two column chunks of 256 by
+// separate workgroups (S and dP are recomputed per chunk), and K_w, V_w are
+// read from global memory instead of registers.
+#include "device_common.h"
+
+namespace cpa {
+
+// ---------------------------------------------------------------- pre/post
+
+// One group of DV/8 lanes per (row, head).
+template <int DV, int DQK, typename TIn>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a) {
+  constexpr int G = DV / 8;            // lanes per (row, head)
+  constexpr int PER_BLOCK = 256 / G;
+  const int z = blockIdx.z;
+  const Seq s = load_seq(a, z);
+  const int gid = threadIdx.x / G, gl = threadIdx.x % G;
+  const int64_t pair = (int64_t)blockIdx.x * PER_BLOCK + gid;
+  const int64_t row = pair / a.heads_q;
+  const int h = (int)(pair % a.heads_q);
+  const bool valid = row < s.qlen;
+  const TIn* O = static_cast<const TIn*>(a.o);
+  const TIn* dO = static_cast<const TIn*>(a.dout);
+  float acc = 0.f;
+  if (valid) {
+    const int64_t prow = a.thd ? s.q_row0 + row : row;
+    const int64_t ob = (a.thd ? 0 : (int64_t)z * a.o_stride[0]) + prow * a.o_stride[1] +
+                       (int64_t)h * a.o_stride[2] + gl * 8;
+    const int64_t db = (a.thd ? 0 : (int64_t)z * a.do_stride[0]) + prow * a.do_stride[1] +
+                       (int64_t)h * a.do_stride[2] + gl * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += to_f32(O[ob + e]) * to_f32(dO[db + e]);
+  }
+#pragma unroll
+  for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, G);
+  if (!valid) return;
+  const int64_t prow = a.thd ? s.q_row0 + row : row;
+  if (gl == 0) {
+    const int64_t doff = (a.thd ? 0 : (int64_t)z * a.delta_stride[0]) +
+                         (int64_t)h * a.delta_stride[1] + prow;
+    a.delta[doff] = acc;
+  }
+  float* accrow = a.dq_acc + (a.thd ? 0 : (int64_t)z * a.acc_stride[0]) +
+                  prow * a.acc_stride[1] + (int64_t)h * a.acc_stride[2];
+  for (int c = gl; c < DQK / 4; c += G)
+    reinterpret_cast<float4*>(accrow)[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// Smallest power of two >= x (x <= 64).
+constexpr int pow2_at_least(int x) { return x <= 8 ? 8 : x <= 16 ? 16 : x <= 32 ? 32 : 64; }
+
+template <int DQK, typename TOut>
+__global__ __launch_bounds__(256) void bwd_post_kernel(const AttnArgs a) {
+  constexpr int G = pow2_at_least(DQK / 8);
+  constexpr int PER_BLOCK = 256 / G;
+  const int z = blockIdx.z;
+  const Seq s = load_seq(a, z);
+  const int gid = threadIdx.x / G, gl = threadIdx.x % G;
+  const int64_t pair = (int64_t)blockIdx.x * PER_BLOCK + gid;
+  const int64_t row = pair / a.heads_q;
+  const int h = (int)(pair % a.heads_q);
+  if (row >= s.qlen) return;
+  const int64_t prow = a.thd ? s.q_row0 + row : row;
+  const float* accrow = a.dq_acc + (a.thd ? 0 : (int64_t)z * a.acc_stride[0]) +
+                        prow * a.acc_stride[1] + (int64_t)h * a.acc_stride[2];
+  TOut* out = static_cast<TOut*>(a.dq) + (a.thd ? 0 : (int64_t)z * a.dq_stride[0]) +
+              prow * a.dq_stride[1] + (int64_t)h * a.dq_stride[2];
+  for (int c = gl; c < DQK / 8; c += G) {
+    const float4 x0 = reinterpret_cast<const float4*>(accrow)[2 * c];
+    const float4 x1 = reinterpret_cast<const float4*>(accrow)[2 * c + 1];
+    const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    if constexpr (sizeof(TOut) == 2) {
+      bf16x8 w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = (bf16)(v[e] * a.scale);
+      reinterpret_cast<bf16x8*>(out)[c] = w;
+    } else {
+      reinterpret_cast<float4*>(out)[2 * c] =
+          make_float4(v[0] * a.scale, v[1] * a.scale, v[2] * a.scale, v[3] * a.scale);
+      reinterpret_cast<float4*>(out)[2 * c + 1] =
+          make_float4(v[4] * a.scale, v[5] * a.scale, v[6] * a.scale, v[7] * a.scale);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- main
+
+template <int DQK, int DV, int OCK, int OCV, int BM, bool KVREG, typename TIn, typename TOut>
+__global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
+  constexpr int BN = 128;
+  constexpr int QP = DQK + 8, OP = DV + 8, SP = BM + 8, KP = OCK + 8;
+  constexpr int NQB = BM / 32;
+  constexpr int KSQ = DQK / 16, KSV = DV / 16;
+  constexpr int NDK = OCK / 32, NDV = OCV / 32;
+  __shared__ __attribute__((aligned(16))) bf16 Qs[BM * QP];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[BM * OP];
+  __shared__ __attribute__((aligned(16))) bf16 dSt[BN * SP];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KP];
+  __shared__ __attribute__((aligned(16))) float Ls[BM];
+  __shared__ __attribute__((aligned(16))) float Dl[BM];
+  __shared__ int64_t Ps[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
+  const int kvh = blockIdx.x % a.heads_kv;
+  const int ch = blockIdx.x / a.heads_kv;
+  const int kt = blockIdx.y;
+  const int z = blockIdx.z;
+  const Seq s = load_seq(a, z);
+  const int j0 = kt * BN;
+  if (j0 >= s.klen) return;
+  const int64_t kp0 = kpos0(a);
+
+  const int jw = j0 + wave * 32;
+  const int my_key = jw + lq;
+  const bool key_valid = my_key < s.klen;
+  const int64_t my_kpos = kp0 + my_key;
+  const bool wave_has_keys = jw < s.klen;
+  const int wk_last = min(jw + 31, s.klen - 1);
+  const int64_t wkpos_lo = kp0 + jw, wkpos_hi = kp0 + wk_last;
+  const int64_t gkpos_lo = kp0 + j0;
+
+  const TIn* Q = static_cast<const TIn*>(a.q);
+  const TIn* K = static_cast<const TIn*>(a.k);
+  const TIn* V = static_cast<const TIn*>(a.v);
+  const TIn* dO = static_cast<const TIn*>(a.dout);
+  const int64_t kbase = (a.thd ? s.k_row0 * a.k_stride[1] : (int64_t)z * a.k_stride[0]) +
+                        (int64_t)kvh * a.k_stride[2];
+  const int64_t vbase = (a.thd ? s.k_row0 * a.v_stride[1] : (int64_t)z * a.v_stride[0]) +
+                        (int64_t)kvh * a.v_stride[2];
+  const TIn* krow = K + kbase + (int64_t)(key_valid ? my_key : 0) * a.k_stride[1];
+  const TIn* vrow = V + vbase + (int64_t)(key_valid ? my_key : 0) * a.v_stride[1];
+
+  bf16x8 kreg[KVREG ? KSQ : 1], vreg[KVREG ? KSV : 1];
+  if constexpr (KVREG) {
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks)
+      kreg[ks] = key_valid ? Elem<TIn>::load8(krow + ks * 16 + hh * 8) : zero8();
+#pragma unroll
+    for (int ks = 0; ks < KSV; ++ks)
+      vreg[ks] = key_valid ? Elem<TIn>::load8(vrow + ks * 16 + hh * 8) : zero8();
+  }
+
+  // K tile (this workgroup's column chunk) for the dQ product.
+#pragma unroll
+  for (int c = tid; c < BN * OCK / 8; c += 256) {
+    const int r = c / (OCK / 8), cc = (c % (OCK / 8)) * 8;
+    const int j = j0 + r;
+    const bf16x8 val = j < s.klen
+        ? Elem<TIn>::load8(K + kbase + (int64_t)j * a.k_stride[1] + ch * OCK + cc) : zero8();
+    *reinterpret_cast<bf16x8*>(&Ks[r * KP + cc]) = val;
+  }
+
+  f32x16 dkacc[NDK], dvacc[NDV];
+#pragma unroll
+  for (int d = 0; d < NDK; ++d)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dkacc[d][v] = 0.f;
+#pragma unroll
+  for (int d = 0; d < NDV; ++d)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dvacc[d][v] = 0.f;
+
+  const int pr = perm32(lq);
+  const int nqt = (s.qlen + BM - 1) / BM;
+  for (int hg = 0; hg < a.group; ++hg) {
+    const int h = kvh * a.group + hg;
+    const int64_t qbase = (a.thd ? s.q_row0 * a.q_stride[1] : (int64_t)z * a.q_stride[0]) +
+                          (int64_t)h * a.q_stride[2];
+    const int64_t dobase = (a.thd ? s.q_row0 * a.do_stride[1] : (int64_t)z * a.do_stride[0]) +
+                           (int64_t)h * a.do_stride[2];
+    const int64_t lbase = (a.thd ? s.q_row0 : (int64_t)z * a.lse_stride[0]) +
+                          (int64_t)h * a.lse_stride[1];
+    const int64_t dlbase = (a.thd ? s.q_row0 : (int64_t)z * a.delta_stride[0]) +
+                           (int64_t)h * a.delta_stride[1];
+    float* accbase = a.dq_acc + (a.thd ? s.q_row0 * a.acc_stride[1] : (int64_t)z * a.acc_stride[0]) +
+                     (int64_t)h * a.acc_stride[2] + ch * OCK;
+
+    for (int qt = 0; qt < nqt; ++qt) {
+      const int i0 = qt * BM;
+      const int i1 = min(i0 + BM, s.qlen);
+      int64_t tlo, thi;
+      qpos_range(a, s, i0, i1, tlo, thi);
+      if (a.causal && thi < gkpos_lo) continue;   // no row here sees these keys
+      __syncthreads();
+#pragma unroll
+      for (int c = tid; c < BM * DQK / 8; c += 256) {
+        const int r = c / (DQK / 8), cc = (c % (DQK / 8)) * 8;
+        const int i = i0 + r;
+        const bf16x8 val = i < s.qlen
+            ? Elem<TIn>::load8(Q + qbase + (int64_t)i * a.q_stride[1] + cc) : zero8();
+        *reinterpret_cast<bf16x8*>(&Qs[r * QP + cc]) = val;
+      }
+#pragma unroll
+      for (int c = tid; c < BM * DV / 8; c += 256) {
+        const int r = c / (DV / 8), cc = (c % (DV / 8)) * 8;
+        const int i = i0 + r;
+        const bf16x8 val = i < s.qlen
+            ? Elem<TIn>::load8(dO + dobase + (int64_t)i * a.do_stride[1] + cc) : zero8();
+        *reinterpret_cast<bf16x8*>(&dOs[r * OP + cc]) = val;
+      }
+      if (tid < BM) {
+        const int i = i0 + tid;
+        const bool ok = i < s.qlen;
+        const float l = ok ? a.lse[lbase + i] : -kInf;
+        // rows past the end or without any key: P must be exactly 0
+        Ls[tid] = (l == -kInf) ? kInf : l * kLog2e;
+        Dl[tid] = ok ? a.delta[dlbase + i] : 0.f;
+        Ps[tid] = qpos(a, s, i);
+      }
+      __syncthreads();
+
+      const bool wave_on = wave_has_keys && (!a.causal || thi >= wkpos_lo);
+      if (wave_on) {
+        f32x16 sacc[NQB], pacc[NQB];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) { sacc[qb][v] = 0.f; pacc[qb][v] = 0.f; }
+#pragma unroll
+        for (int ks = 0; ks < KSQ; ++ks) {
+          bf16x8 b;
+          if constexpr (KVREG) b = kreg[ks];
+          else b = key_valid ? Elem<TIn>::load8(krow + ks * 16 + hh * 8) : zero8();
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb)
+            sacc[qb] = mfma32(lds_row8(Qs, QP, qb * 32 + pr, ks * 16 + hh * 8), b, sacc[qb]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KSV; ++ks) {
+          bf16x8 b;
+          if constexpr (KVREG) b = vreg[ks];
+          else b = key_valid ? Elem<TIn>::load8(vrow + ks * 16 + hh * 8) : zero8();
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb)
+            pacc[qb] = mfma32(lds_row8(dOs, OP, qb * 32 + pr, ks * 16 + hh * 8), b, pacc[qb]);
+        }
+        const bool need_mask = (jw + 32 > s.klen) || (a.causal && tlo < wkpos_hi);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = qb * 32 + acc_row_perm(v, hh);
+            float p = fast_exp2(sacc[qb][v] * a.scale_log2 - Ls[r]);
+            if (need_mask) {
+              const bool vis = key_valid && (!a.causal || my_kpos <= Ps[r]);
+              p = vis ? p : 0.f;
+            }
+            sacc[qb][v] = p;
+            pacc[qb][v] = p * (pacc[qb][v] - Dl[r]);
+          }
+#pragma unroll
+        for (int t = 0; t < BM / 16; ++t) {
+          bf16x8 pb, sb;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pb[e] = (bf16)sacc[t >> 1][8 * (t & 1) + e];
+            sb[e] = (bf16)pacc[t >> 1][8 * (t & 1) + e];
+          }
+          const int k0 = 16 * t + 8 * (grp >> 1);
+#pragma unroll
+          for (int db = 0; db < NDV; ++db)
+            dvacc[db] = mfma32(lds_tr8(dOs, OP, k0, ch * OCV + db * 32 + 16 * (grp & 1), gl), pb,
+                               dvacc[db]);
+#pragma unroll
+          for (int db = 0; db < NDK; ++db)
+            dkacc[db] = mfma32(lds_tr8(Qs, QP, k0, ch * OCK + db * 32 + 16 * (grp & 1), gl), sb,
+                               dkacc[db]);
+        }
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int hv = 0; hv < 2; ++hv) {
+            bf16x8 w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = (bf16)pacc[qb][8 * hv + e];
+            *reinterpret_cast<bf16x8*>(&dSt[(wave * 32 + lq) * SP + qb * 32 + 16 * hv + 8 * hh]) = w;
+          }
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int hv = 0; hv < 2; ++hv)
+            *reinterpret_cast<bf16x8*>(&dSt[(wave * 32 + lq) * SP + qb * 32 + 16 * hv + 8 * hh]) =
+                zero8();
+      }
+      __syncthreads();
+
+      // dQ tile (BM x OCK) = dS (BM x 128 keys) K (128 keys x OCK), split
+      // into 32x32 blocks over the four waves.
+      for (int b = wave; b < NQB * NDK; b += 4) {
+        const int qb = b / NDK, db = b % NDK;
+        f32x16 acc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+        for (int t = 0; t < BN / 16; ++t) {
+          const int k0 = 16 * t + 8 * (grp >> 1);
+          acc = mfma32(lds_tr8(dSt, SP, k0, qb * 32 + 16 * (grp & 1), gl),
+                       lds_tr8(Ks, KP, k0, db * 32 + 16 * (grp & 1), gl), acc);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int i = i0 + qb * 32 + acc_row(v, hh);
+          if (i < s.qlen)
+            atomicAdd(accbase + (int64_t)i * a.acc_stride[1] + db * 32 + lq, acc[v]);
+        }
+      }
+    }
+  }
+
+  if (!key_valid) return;
+  TOut* dK = static_cast<TOut*>(a.dk) +
+             (a.thd ? (s.k_row0 + my_key) * a.dk_stride[1]
+                    : (int64_t)z * a.dk_stride[0] + (int64_t)my_key * a.dk_stride[1]) +
+             (int64_t)kvh * a.dk_stride[2] + ch * OCK;
+  TOut* dV = static_cast<TOut*>(a.dv) +
+             (a.thd ? (s.k_row0 + my_key) * a.dv_stride[1]
+                    : (int64_t)z * a.dv_stride[0] + (int64_t)my_key * a.dv_stride[1]) +
+             (int64_t)kvh * a.dv_stride[2] + ch * OCV;
+#pragma unroll
+  for (int db = 0; db < NDK; ++db)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int d = db * 32 + 8 * a4 + 4 * hh;
+      if constexpr (sizeof(TOut) == 2) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(dkacc[db][4 * a4 + e] * a.scale);
+        *reinterpret_cast<bf16x4*>(dK + d) = w;
+      } else {
+        *reinterpret_cast<float4*>(dK + d) =
+            make_float4(dkacc[db][4 * a4] * a.scale, dkacc[db][4 * a4 + 1] * a.scale,
+                        dkacc[db][4 * a4 + 2] * a.scale, dkacc[db][4 * a4 + 3] * a.scale);
+      }
+    }
+#pragma unroll
+  for (int db = 0; db < NDV; ++db)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int d = db * 32 + 8 * a4 + 4 * hh;
+      if constexpr (sizeof(TOut) == 2) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)dvacc[db][4 * a4 + e];
+        *reinterpret_cast<bf16x4*>(dV + d) = w;
+      } else {
+        *reinterpret_cast<float4*>(dV + d) = make_float4(
+            dvacc[db][4 * a4], dvacc[db][4 * a4 + 1], dvacc[db][4 * a4 + 2], dvacc[db][4 * a4 + 3]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------- launch
+
+template <int DQK, int DV, typename TIn, typename TOut>
+static hipError_t bwd_variant(const AttnArgs& a, hipStream_t st) {
+  constexpr bool BIG = DQK > 256 || DV > 256;
+  constexpr int OCK = BIG ? DQK / 2 : DQK;
+  constexpr int OCV = BIG ? DV / 2 : DV;
+  constexpr int NCH = DQK / OCK;
+  constexpr int BM = DQK + DV > 320 ? 32 : 64;
+  constexpr bool KVREG = DQK + DV <= 320;
+  const int qrows = a.thd ? a.max_q : (int)a.seqlen_q;
+  const int krows = a.thd ? a.max_k : (int)a.seqlen_k;
+  if (a.nseq == 0) return hipSuccess;
+  if (qrows > 0) {
+    constexpr int PB = 256 / (DV / 8);
+    const int64_t pairs = (int64_t)qrows * a.heads_q;
+    dim3 g((unsigned)((pairs + PB - 1) / PB), 1, a.nseq);
+    hipLaunchKernelGGL((bwd_pre_kernel<DV, DQK, TIn>), g, dim3(256), 0, st, a);
+  }
+  if (krows > 0) {
+    dim3 g(a.heads_kv * NCH, (krows + 127) / 128, a.nseq);
+    hipLaunchKernelGGL((bwd_main_kernel<DQK, DV, OCK, OCV, BM, KVREG, TIn, TOut>), g, dim3(256), 0,
+                       st, a);
+  }
+  if (qrows > 0) {
+    constexpr int PB = 256 / pow2_at_least(DQK / 8);
+    const int64_t pairs = (int64_t)qrows * a.heads_q;
+    dim3 g((unsigned)((pairs + PB - 1) / PB), 1, a.nseq);
+    hipLaunchKernelGGL((bwd_post_kernel<DQK, TOut>), g, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int DQK, int DV>
+static hipError_t bwd_dtypes(const AttnArgs& a, int in_dt, int out_dt, hipStream_t st) {
+  if (in_dt == CPA_BF16 && out_dt == CPA_BF16) return bwd_variant<DQK, DV, bf16, bf16>(a, st);
+  if (in_dt == CPA_BF16 && out_dt == CPA_FP32) return bwd_variant<DQK, DV, bf16, float>(a, st);
+  if (in_dt == CPA_FP32 && out_dt == CPA_BF16) return bwd_variant<DQK, DV, float, bf16>(a, st);
+  return bwd_variant<DQK, DV, float, float>(a, st);
+}
+
+hipError_t launch_bwd(const AttnArgs& a, int d_qk, int d_v, int in_dt, int out_dt,
+                      hipStream_t st) {
+  if (d_qk == 64 && d_v == 64) return bwd_dtypes<64, 64>(a, in_dt, out_dt, st);
+  if (d_qk == 128 && d_v == 128) return bwd_dtypes<128, 128>(a, in_dt, out_dt, st);
+  if (d_qk == 192 && d_v == 128) return bwd_dtypes<192, 128>(a, in_dt, out_dt, st);
+  if (d_qk == 256 && d_v == 256) return bwd_dtypes<256, 256>(a, in_dt, out_dt, st);
+  if (d_qk == 512 && d_v == 512) return bwd_dtypes<512, 512>(a, in_dt, out_dt, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace cpa

@@ -1,0 +1,254 @@
+// Causal attention forward with online softmax on gfx950.
+//
+// One workgroup = 4 waves = 128 query rows of one head (32 rows per wave);
+// KV tiles of 64 keys are staged row-major in LDS.  Each wave computes
+// S^T = K Q^T with the 32x32x16 bf16 matrix-core product, so that every lane
+// owns one query row: a row's max and sum need only an in-lane reduction
+// plus one swap with lane l^32.  The K rows are fed in a permuted order
+// (perm32) so the fp32 scores a lane holds are exactly the bf16 B operand of
+// the next product, O^T += V^T P^T, with no shuffles; V^T comes straight
+// from the row-major V tile through the LDS transpose reads.
+//
+// The softmax runs in base 2 (scores pre-multiplied by s*log2 e) with a
+// running max and sum per row; the epilogue writes O = acc / sum and the
+// natural-log LSE = (max + log2 sum) * ln 2 in fp32, the convention that
+// makes LSE merges of ring-step partials valid (PR 3527, commit adding
+// frost_attention.py).  Rows with no visible key end with sum = 0 and get
+// O = 0, LSE = -inf.
+//
+// Work skipping: KV tiles entirely above the workgroup's last query position
+// are never loaded (causal tile skipping); a wave whose rows all precede a
+// tile skips its products; the position mask is evaluated only on tiles
+// that straddle a wave's diagonal or the end of the keys.
+#include "device_common.h"
+
+namespace cpa {
+
+template <int DQK, int DVC, int NCH, typename TIn, typename TOut>
+__global__ __launch_bounds__(256) void fwd_kernel(const AttnArgs a) {
+  constexpr int BM = 128, BN = 64;
+  constexpr int KP = DQK + 8, VP = DVC + 8;
+  constexpr int KS = DQK / 16;
+  constexpr int NDB = DVC / 32;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[BN * VP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
+  const int h = blockIdx.x % a.heads_q;
+  const int ch = blockIdx.x / a.heads_q;
+  const int tile = gridDim.y - 1 - blockIdx.y;   // heaviest tiles first
+  const int z = blockIdx.z;
+  const Seq s = load_seq(a, z);
+  const int i0 = tile * BM;
+  if (i0 >= s.qlen) return;
+  const int kvh = h / a.group;
+
+  const TIn* Q = static_cast<const TIn*>(a.q);
+  const TIn* K = static_cast<const TIn*>(a.k);
+  const TIn* V = static_cast<const TIn*>(a.v);
+  TOut* O = static_cast<TOut*>(a.out_o);
+  const int64_t qbase = a.thd ? s.q_row0 * a.q_stride[1] : (int64_t)z * a.q_stride[0];
+  const int64_t kbase = (a.thd ? s.k_row0 * a.k_stride[1] : (int64_t)z * a.k_stride[0]) +
+                        (int64_t)kvh * a.k_stride[2];
+  const int64_t vbase = (a.thd ? s.k_row0 * a.v_stride[1] : (int64_t)z * a.v_stride[0]) +
+                        (int64_t)kvh * a.v_stride[2] + ch * DVC;
+  const int64_t obase = a.thd ? s.q_row0 * a.o_stride[1] : (int64_t)z * a.o_stride[0];
+
+  const int qi = i0 + wave * 32 + lq;
+  const bool qvalid = qi < s.qlen;
+  const int64_t my_pos = qpos(a, s, qi);
+  const int wr0 = i0 + wave * 32;
+  const bool wave_active = wr0 < s.qlen;
+  int64_t wlo = 0, whi = -1;
+  if (wave_active) qpos_range(a, s, wr0, min(wr0 + 32, s.qlen), wlo, whi);
+  int64_t glo, ghi;
+  qpos_range(a, s, i0, min(i0 + BM, s.qlen), glo, ghi);
+  const int64_t kp0 = kpos0(a);
+  int kend = s.klen;
+  if (a.causal) {
+    const int64_t lim = ghi - kp0 + 1;
+    kend = (int)(lim < 0 ? 0 : (lim < kend ? lim : kend));
+  }
+  const int ntiles = (kend + BN - 1) / BN;
+
+  // This lane's query row as the B operand of S^T = K Q^T, for all k-steps.
+  bf16x8 qreg[KS];
+  {
+    const TIn* qrow = Q + qbase + (int64_t)qi * a.q_stride[1] + (int64_t)h * a.q_stride[2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qreg[ks] = qvalid ? Elem<TIn>::load8(qrow + ks * 16 + hh * 8) : zero8();
+  }
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
+  float m_run = -kInf, l_run = 0.f;
+  const int kr = perm32(lq);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * BN;
+    __syncthreads();
+#pragma unroll
+    for (int c = tid; c < BN * DQK / 8; c += 256) {
+      const int r = c / (DQK / 8), cc = (c % (DQK / 8)) * 8;
+      const int j = j0 + r;
+      const bf16x8 val = j < s.klen
+          ? Elem<TIn>::load8(K + kbase + (int64_t)j * a.k_stride[1] + cc) : zero8();
+      *reinterpret_cast<bf16x8*>(&Ks[r * KP + cc]) = val;
+    }
+#pragma unroll
+    for (int c = tid; c < BN * DVC / 8; c += 256) {
+      const int r = c / (DVC / 8), cc = (c % (DVC / 8)) * 8;
+      const int j = j0 + r;
+      const bf16x8 val = j < s.klen
+          ? Elem<TIn>::load8(V + vbase + (int64_t)j * a.v_stride[1] + cc) : zero8();
+      *reinterpret_cast<bf16x8*>(&Vs[r * VP + cc]) = val;
+    }
+    __syncthreads();
+    if (!wave_active || (a.causal && kp0 + j0 > whi)) continue;
+
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sacc[kb] = mfma32(lds_row8(Ks, KP, kb * 32 + kr, ks * 16 + hh * 8), qreg[ks], sacc[kb]);
+
+    const bool need_mask = (j0 + BN > s.klen) || (a.causal && kp0 + j0 + BN - 1 > wlo);
+    float x[2][16];
+    float mx = -kInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float val = sacc[kb][v] * a.scale_log2;
+        if (need_mask) {
+          const int j = j0 + kb * 32 + acc_row_perm(v, hh);
+          const bool vis = j < s.klen && (!a.causal || kp0 + j <= my_pos);
+          val = vis ? val : -kInf;
+        }
+        x[kb][v] = val;
+        mx = fmaxf(mx, val);
+      }
+    mx = fmaxf(mx, xhalf(mx));
+    const float m_new = fmaxf(m_run, mx);
+    const float base = (m_new == -kInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - base);
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        x[kb][v] = fast_exp2(x[kb][v] - base);
+        rs += x[kb][v];
+      }
+    rs += xhalf(rs);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+
+#pragma unroll
+    for (int st = 0; st < BN / 16; ++st) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = (bf16)x[st >> 1][8 * (st & 1) + e];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = mfma32(lds_tr8(Vs, VP, 16 * st + 8 * (grp >> 1), db * 32 + 16 * (grp & 1), gl),
+                          pb, oacc[db]);
+    }
+  }
+
+  if (!qvalid) return;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  TOut* orow = O + obase + (int64_t)qi * a.o_stride[1] + (int64_t)h * a.o_stride[2] + ch * DVC;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int d = db * 32 + 8 * a4 + 4 * hh;
+      if constexpr (sizeof(TOut) == 2) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(oacc[db][4 * a4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + d) = w;
+      } else {
+        float4 w = make_float4(oacc[db][4 * a4 + 0] * inv, oacc[db][4 * a4 + 1] * inv,
+                               oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv);
+        *reinterpret_cast<float4*>(orow + d) = w;
+      }
+    }
+  if (hh == 0 && ch == 0) {
+    const int64_t lrow = a.thd ? s.q_row0 + qi : (int64_t)qi;
+    const int64_t loff = (a.thd ? 0 : (int64_t)z * a.lse_stride[0]) + (int64_t)h * a.lse_stride[1] + lrow;
+    a.out_lse[loff] = l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -kInf;
+  }
+}
+
+// THD metadata check: writes 0 to the flag, or 1 if any sequence's offsets
+// or lengths are out of range (the kernels then treat it as empty).
+__global__ __launch_bounds__(256) void meta_check_kernel(const AttnArgs a) {
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  if (a.thd) {
+    for (int n = threadIdx.x; n < a.nseq; n += blockDim.x) {
+      const int cq0 = a.cu_q[n], cq1 = a.cu_q[n + 1], uq = a.used_q[n];
+      const int ck0 = a.cu_k[n], ck1 = a.cu_k[n + 1], uk = a.used_k[n];
+      const bool ok = cq0 >= 0 && cq0 <= cq1 && cq1 <= a.seqlen_q && uq >= 0 &&
+                      uq <= cq1 - cq0 && uq <= a.max_q && ck0 >= 0 && ck0 <= ck1 &&
+                      ck1 <= a.seqlen_k && uk >= 0 && uk <= ck1 - ck0 && uk <= a.max_k;
+      if (!ok) atomicOr(&bad, 1);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) *a.err_flag = bad;
+}
+
+template <int DQK, int DV, typename TIn, typename TOut>
+static hipError_t fwd_variant(const AttnArgs& a, hipStream_t st) {
+  constexpr int DVC = DV > 256 ? 256 : DV;
+  constexpr int NCH = DV / DVC;
+  const int qrows = a.thd ? a.max_q : (int)a.seqlen_q;
+  const int ntile = (qrows + 127) / 128;
+  if (ntile == 0 || a.nseq == 0) return hipSuccess;
+  dim3 grid(a.heads_q * NCH, ntile, a.nseq);
+  hipLaunchKernelGGL((fwd_kernel<DQK, DVC, NCH, TIn, TOut>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DQK, int DV>
+static hipError_t fwd_dtypes(const AttnArgs& a, int in_dt, int out_dt, hipStream_t st) {
+  if (in_dt == CPA_BF16 && out_dt == CPA_BF16) return fwd_variant<DQK, DV, bf16, bf16>(a, st);
+  if (in_dt == CPA_BF16 && out_dt == CPA_FP32) return fwd_variant<DQK, DV, bf16, float>(a, st);
+  if (in_dt == CPA_FP32 && out_dt == CPA_BF16) return fwd_variant<DQK, DV, float, bf16>(a, st);
+  return fwd_variant<DQK, DV, float, float>(a, st);
+}
+
+hipError_t launch_meta_check(const AttnArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(meta_check_kernel, dim3(1), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const AttnArgs& a, int d_qk, int d_v, int in_dt, int out_dt,
+                      hipStream_t st) {
+  if (d_qk == 64 && d_v == 64) return fwd_dtypes<64, 64>(a, in_dt, out_dt, st);
+  if (d_qk == 128 && d_v == 128) return fwd_dtypes<128, 128>(a, in_dt, out_dt, st);
+  if (d_qk == 192 && d_v == 128) return fwd_dtypes<192, 128>(a, in_dt, out_dt, st);
+  if (d_qk == 256 && d_v == 256) return fwd_dtypes<256, 256>(a, in_dt, out_dt, st);
+  if (d_qk == 512 && d_v == 512) return fwd_dtypes<512, 512>(a, in_dt, out_dt, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace cpa

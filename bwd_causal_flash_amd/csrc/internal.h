@@ -1,0 +1,93 @@
+// Internal structures shared by the host entry points and the kernels.
+// Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/cpattn.h"
+
+namespace cpa {
+
+// Everything a forward or backward kernel needs, resolved on the host.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;      // bwd: saved O (in dtype)
+  const void* dout;   // bwd: dO
+  const float* lse;   // bwd: saved LSE
+  void* out_o;        // fwd: O
+  float* out_lse;     // fwd: LSE
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;      // bwd workspace: fp32 [rows][heads_q][d_qk]
+  float* delta;       // bwd workspace: fp32, indexed like LSE
+  int* err_flag;      // workspace word 0
+
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3], do_stride[3];
+  int64_t dq_stride[3], dk_stride[3], dv_stride[3];
+  int64_t lse_stride[2];
+  int64_t acc_stride[3];    // dq_acc strides [batch, row, head]
+  int64_t delta_stride[2];  // delta strides [batch, head]
+
+  int thd;            // 1: packed varlen
+  int nseq;           // BSHD batch or THD sequence count
+  int heads_q, heads_kv, group;
+  int64_t seqlen_q, seqlen_k;     // BSHD per-batch rows; THD physical rows
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* used_q;
+  const int32_t* used_k;
+  int max_q, max_k;
+
+  float scale;        // softmax scale s
+  float scale_log2;   // s * log2(e)
+  int causal;
+  int bottom_right;
+  int nseg;
+  int64_t seg_row[CPA_MAX_SEGMENTS];
+  int64_t seg_pos[CPA_MAX_SEGMENTS];
+  int64_t k_pos0;
+};
+
+struct MergeArgs {
+  const void* o_acc;
+  const float* lse_acc;
+  const void* o_part;
+  const float* lse_part;
+  void* o_out;
+  float* lse_out;
+  int batch, heads, d_v;
+  int64_t seqlen;
+  int64_t acc_stride[3], part_stride[3], out_stride[3];
+  int64_t lse_acc_stride[2], lse_part_stride[2], lse_out_stride[2];
+};
+
+struct PackArgs {
+  const void* src_o;
+  const float* src_lse;
+  void* dst_o;
+  float* dst_lse;
+  const void* buf_in;
+  void* buf_out;
+  int batch, heads, d_v, groups, elem_bytes;
+  int64_t seqlen;
+  int64_t o_stride[3];
+  int64_t lse_stride[2];
+  int64_t seg_bytes, lse_off;
+};
+
+// Launchers (defined in the .hip files).  Return hipSuccess or the launch
+// error.
+hipError_t launch_fwd(const AttnArgs& a, int d_qk, int d_v, int in_dt,
+                      int out_dt, hipStream_t s);
+hipError_t launch_bwd(const AttnArgs& a, int d_qk, int d_v, int in_dt,
+                      int out_dt, hipStream_t s);
+hipError_t launch_meta_check(const AttnArgs& a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& m, int acc_dt, int part_dt,
+                        int out_dt, hipStream_t s);
+hipError_t launch_pack(const PackArgs& p, bool wide, bool unpack,
+                       hipStream_t s);
+
+}  // namespace cpa

@@ -1,0 +1,246 @@
+/*
+ * cpattn.h - causal attention forward/backward for one context-parallel
+ * rank, on AMD Instinct MI355X (gfx950).  Plain C ABI: every pointer is a
+ * device pointer unless marked "host", sizes are plain integers, and every
+ * compute call is enqueued on the caller's HIP stream and returns without
+ * synchronising.
+ *
+ * What is computed (softmax attention and its exact gradient; the pages
+ * print no formulas, so these are the textbook definitions):
+ *
+ *   S   = s * Q K^T over the visible keys        (s = softmax_scale)
+ *   LSE = natural-log logsumexp of each row of S, in fp32
+ *   P   = exp(S - LSE),  O = P V
+ *   D   = rowsum(dO * O)
+ *   dS  = P * (dO V^T - D)
+ *   dQ  = s dS K,  dK = s dS^T Q,  dV = P^T dO
+ *
+ * The natural-log fp32 LSE is what makes merging ring-step partials valid
+ * (TransformerEngine PR 3527 "cuDNN FROST attention backend for head_dim in
+ * (256, 512], with context parallelism", commit adding frost_attention.py).
+ * The backward consumes the saved Q, K, V, O, dO and LSE (TransformerEngine
+ * PR 3510 "Add head-parallel FA4 backward for cuDNN CP attention", Diagram).
+ *
+ * Visibility.  Key j is visible to query i iff it is a real key of the same
+ * sequence and, when causal, pos_k(j) <= pos_q(i).  Positions make top-left
+ * causal (the default), bottom-right causal (PR 3699 "Add cuDNN OSS backward
+ * dispatch for context parallel attention", Implementation and supported
+ * scope) and the dual-chunk query rows of a load-balanced CP rank (PR 3510,
+ * Changes) one rule.  Rows with no visible key get O = 0, LSE = -inf and
+ * exactly zero dQ (PR 3699, Review follow-up); keys no query sees get
+ * dK = dV = 0.
+ *
+ * Layouts.  BSHD: element (b, s, h, d) of a tensor X is at
+ *   X + b*stride[0] + s*stride[1] + h*stride[2] + d
+ * (strides in elements; the head dim is contiguous).  THD (packed varlen):
+ * element (t, h, d) is at X + t*stride[1] + h*stride[2] + d and stride[0]
+ * is ignored; sequence n occupies physical rows [cu_seqlens[n],
+ * cu_seqlens[n+1]) of which the first seqused[n] are real (physical padded
+ * offsets plus visible lengths, PR 3149 "Enable FA4 for context-parallel
+ * attention", Description).  Padding rows are never read for compute and
+ * never written.
+ * LSE is fp32: BSHD element (b, h, s) at lse + b*lse_stride[0] +
+ * h*lse_stride[1] + s; THD element (h, t) at lse + h*lse_stride[1] + t.
+ *
+ * Data types.  Inputs are bf16 or fp32 (fp32 inputs are rounded to bf16,
+ * round-to-nearest-even, as they are loaded: the matrix products always run
+ * as bf16 x bf16 -> fp32 on the matrix cores).  Softmax statistics and all
+ * accumulation are fp32.  Outputs are bf16 or fp32.
+ *
+ * Ownership and errors.  The caller owns every buffer, the workspace and
+ * the stream; the library allocates nothing and keeps no per-call state, so
+ * calls are reentrant.  Argument errors are reported by the returned status
+ * before anything is enqueued (no partial writes).  Malformed THD metadata
+ * lives on the device, so it is checked there: an offending sequence is
+ * treated as empty (never read or written out of bounds) and a nonzero
+ * int32 is written to the first 4 bytes of the workspace, which the caller
+ * reads after synchronising (PR 3699, Implementation and supported scope: a
+ * GPU check of lengths and origins on every execution).
+ *
+ * Unsupported configurations are refused with CPA_ERR_UNSUPPORTED rather
+ * than approximated (PR 3527, commit adding frost_attention.py).
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same object as hipStream_t; NULL is the null (default) stream. */
+typedef struct ihipStream_t* cpa_stream_t;
+
+typedef enum cpa_status {
+  CPA_OK = 0,
+  CPA_ERR_NULL = 1,        /* a required pointer is NULL */
+  CPA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
+  CPA_ERR_DTYPE = 3,       /* unknown dtype code */
+  CPA_ERR_STRIDE = 4,      /* stride not a multiple of 8 elements, or K/V mismatch */
+  CPA_ERR_ALIGN = 5,       /* a base pointer is not 16-byte aligned */
+  CPA_ERR_UNSUPPORTED = 6, /* valid request this library declines */
+  CPA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than required */
+  CPA_ERR_OVERLAP = 8,     /* buffers that must be disjoint overlap */
+  CPA_ERR_LAUNCH = 9       /* the HIP runtime reported a launch error */
+} cpa_status;
+
+enum { CPA_BF16 = 0, CPA_FP32 = 1 };
+enum { CPA_LAYOUT_BSHD = 0, CPA_LAYOUT_THD = 1 };
+enum { CPA_MAX_SEGMENTS = 8 };
+enum { CPA_FLAG_DETERMINISTIC = 1 };
+
+/*
+ * One attention problem.  Supported head dims (d_qk, d_v): (64, 64),
+ * (128, 128), (192, 128), (256, 256), (512, 512); others are declined
+ * (head dims on the pages: 192/128 in PR 3510, D128/D256 in PR 3699,
+ * symmetric 512 in PR 3527).  heads_q must be a multiple of heads_kv
+ * (GQA: query head h reads kv head h / (heads_q / heads_kv)).
+ */
+typedef struct cpa_problem {
+  int32_t layout;      /* CPA_LAYOUT_BSHD or CPA_LAYOUT_THD */
+  int32_t in_dtype;    /* dtype of q, k, v, dO, and of o read by attn_bwd */
+  int32_t out_dtype;   /* dtype of o written by attn_fwd; of dq, dk, dv */
+  int32_t batch;       /* BSHD batch count (>= 1); ignored for THD */
+  int32_t heads_q, heads_kv, d_qk, d_v;
+  int64_t seqlen_q;    /* BSHD: query rows per batch; THD: physical rows */
+  int64_t seqlen_k;    /* BSHD: key rows per batch;   THD: physical rows */
+
+  /* THD only: device int32 arrays of num_seqs+1 (cu_*) and num_seqs
+   * (seqused_*) entries; max_seqlen_* are host upper bounds of seqused_*. */
+  int32_t num_seqs;
+  int32_t max_seqlen_q, max_seqlen_k;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  const int32_t* seqused_q;
+  const int32_t* seqused_k;
+
+  /* Strides in elements: [batch, row, head]; multiples of 8. */
+  int64_t q_stride[3], k_stride[3], v_stride[3];
+  int64_t o_stride[3], do_stride[3];
+  int64_t dq_stride[3], dk_stride[3], dv_stride[3];
+  int64_t lse_stride[2];   /* [batch, head]; rows are contiguous */
+
+  float softmax_scale;     /* s; usually 1/sqrt(d_qk) */
+  int32_t causal;          /* 0: every real key visible */
+  int32_t thd_bottom_right;/* THD: pos_q(i) = i + seqused_k - seqused_q */
+
+  /* BSHD query positions: rows [q_seg_row[t], q_seg_row[t+1]) have
+   * positions q_seg_pos[t] + (row - q_seg_row[t]).  num_q_segments = 0
+   * means one segment at position 0 (top-left).  q_seg_row[0] must be 0
+   * and rows must increase.  Key row j has position k_pos_begin + j. */
+  int32_t num_q_segments;
+  int64_t q_seg_row[CPA_MAX_SEGMENTS];
+  int64_t q_seg_pos[CPA_MAX_SEGMENTS];
+  int64_t k_pos_begin;
+} cpa_problem;
+
+/* Human-readable name of a status code (host, static string). */
+const char* attn_status_string(cpa_status status);
+
+/* Bytes of workspace attn_fwd needs (host, pure): room for the device
+ * metadata error flag.  Same problem -> same size. */
+size_t attn_fwd_workspace_size(const cpa_problem* p);
+
+/*
+ * Forward.  Writes O (out_dtype) and LSE (fp32) for every real query row;
+ * keyless rows get O = 0, LSE = -inf; THD padding rows are untouched.
+ * Bitwise deterministic (no atomics, fixed reduction order), also across
+ * streams.  q, k, v, o, lse: device, 16-byte aligned; o must not overlap the
+ * inputs.  ws: device workspace of attn_fwd_workspace_size(p) bytes; its
+ * first int32 is zeroed and then set nonzero if THD metadata is malformed.
+ * For ring-step partials pass out_dtype = CPA_FP32 and merge with
+ * attn_merge_lse.
+ */
+cpa_status attn_fwd(const cpa_problem* p, const void* q, const void* k,
+                    const void* v, void* o, float* lse, void* ws,
+                    size_t ws_bytes, cpa_stream_t stream);
+
+/* Bytes of workspace attn_bwd needs (host, pure): the error flag, D =
+ * rowsum(dO*O) and an fp32 dQ accumulator. */
+size_t attn_bwd_workspace_size(const cpa_problem* p);
+
+/*
+ * Backward.  Given the saved q, k, v, o (in_dtype), lse (fp32) and dout,
+ * writes dq, dk, dv (out_dtype) for every real row, with exact zeros where a
+ * row or key has no visible partner; THD padding rows are untouched.  dQ is
+ * accumulated in fp32 with atomics, so its low bits may vary from run to run
+ * (the pages' backward kernels are nondeterministic too, PR 3699).  flags:
+ * CPA_FLAG_DETERMINISTIC is declined with CPA_ERR_UNSUPPORTED.  Outputs must
+ * not overlap each other or the inputs; ws holds attn_bwd_workspace_size(p)
+ * bytes (first int32 = THD metadata error flag, as for attn_fwd).
+ */
+cpa_status attn_bwd(const cpa_problem* p, const void* q, const void* k,
+                    const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, void* ws,
+                    size_t ws_bytes, uint32_t flags, cpa_stream_t stream);
+
+/*
+ * LSE merge of two partial attentions over disjoint key sets (the per-ring-
+ * step combine of PR 3527's context-parallel commits: per-step kernel calls
+ * interleaved with KV exchange and LSE correction).  Per (b, s, h):
+ *   M = max(lse_acc, lse_part);  M = -inf -> O = 0, LSE = -inf;  else
+ *   LSE = M + ln(exp(lse_acc - M) + exp(lse_part - M)),
+ *   O = exp(lse_acc - LSE) o_acc + exp(lse_part - LSE) o_part   (fp32 math)
+ * A partial with LSE = -inf leaves the other operand's O and LSE bitwise
+ * unchanged (converted to out dtype).  o_out may be o_acc itself and lse_out
+ * may be lse_acc itself (in place); any other overlap is CPA_ERR_OVERLAP.
+ * Tensors are BSHD-strided [batch, rows, heads, d_v]; LSE strides are
+ * [batch, head] with contiguous rows.
+ */
+typedef struct cpa_merge_desc {
+  int32_t batch, heads, d_v;
+  int64_t seqlen;
+  int32_t acc_dtype, part_dtype, out_dtype;    /* CPA_BF16 / CPA_FP32 */
+  int64_t acc_stride[3], part_stride[3], out_stride[3];
+  int64_t lse_acc_stride[2], lse_part_stride[2], lse_out_stride[2];
+} cpa_merge_desc;
+
+cpa_status attn_merge_lse(const cpa_merge_desc* d, const void* o_acc,
+                          const float* lse_acc, const void* o_part,
+                          const float* lse_part, void* o_out, float* lse_out,
+                          cpa_stream_t stream);
+
+/*
+ * Bit-exact pack / unpack of the saved forward outputs O and fp32 LSE into
+ * one contiguous exchange buffer (PR 3510, Description: the saved tensors
+ * are packed for one all-to-all and the FP32 log-sum-exp values are
+ * preserved; the receiver may unpack into the send allocation).
+ *
+ * Buffer layout: heads are cut into `groups` groups of Hg = heads/groups
+ * consecutive heads; group g is segment g, at byte g*segment_bytes.  A
+ * segment holds O of its heads, element (b, s, hh, d) at ((b*seqlen + s)*Hg
+ * + hh)*d_v + d in O's element type, then at the next multiple of 256 bytes
+ * the LSE of its heads, element (b, hh, s) at (b*Hg + hh)*seqlen + s (raw
+ * fp32 bits); segment_bytes is a multiple of 256.  Pad bytes are left as
+ * they were.  Offsets are computed in 64-bit arithmetic when any byte offset
+ * can reach 2^31 (or when force_int64 is set), else in 32-bit.
+ */
+typedef struct cpa_pack_desc {
+  int32_t batch, heads, d_v, o_dtype, groups;
+  int64_t seqlen;
+  int64_t o_stride[3];     /* elements: [batch, row, head] */
+  int64_t lse_stride[2];   /* elements: [batch, head]; rows contiguous */
+  int32_t force_int64;
+} cpa_pack_desc;
+
+/* Total buffer bytes (host, pure); 0 for an invalid descriptor. */
+size_t pack_saved_size(const cpa_pack_desc* d);
+
+/* o, lse -> buf.  buf must hold pack_saved_size(d) bytes and must not
+ * overlap o or lse (CPA_ERR_OVERLAP). */
+cpa_status pack_saved(const cpa_pack_desc* d, const void* o,
+                      const float* lse, void* buf, size_t buf_bytes,
+                      cpa_stream_t stream);
+
+/* buf -> o, lse (exact inverse of pack_saved).  o and lse must not overlap
+ * buf; they may live in a reused send allocation. */
+cpa_status unpack_saved(const cpa_pack_desc* d, const void* buf,
+                        size_t buf_bytes, void* o, float* lse,
+                        cpa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CPATTN_H */

@@ -1,0 +1,130 @@
+"""Validation cases for the C ABI, run in a child process with no GPU
+visible (HIP_VISIBLE_DEVICES=-1): every case must be rejected by host
+validation before anything is enqueued; a case that slipped through would
+only reach a launch error, never a device.  Prints one JSON object mapping
+case name -> [expected status name, returned status name].
+"""
+import ctypes
+import json
+import os
+import sys
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+from bwd_causal_flash_amd import _lib  # noqa: E402
+
+A = 1 << 20   # fake, 16-byte aligned device addresses (never dereferenced)
+
+
+def good_problem(d_qk=128, d_v=128):
+    p = _lib.Problem()
+    p.layout, p.in_dtype, p.out_dtype = 0, 0, 0
+    p.batch, p.heads_q, p.heads_kv, p.d_qk, p.d_v = 1, 4, 2, d_qk, d_v
+    p.seqlen_q = p.seqlen_k = 256
+    for name, d in (("q_stride", d_qk), ("k_stride", d_qk), ("v_stride", d_v),
+                    ("o_stride", d_v), ("do_stride", d_v), ("dq_stride", d_qk),
+                    ("dk_stride", d_qk), ("dv_stride", d_v)):
+        h = 4 if name[0] in "qod" and name not in ("dk_stride", "dv_stride") else 2
+        setattr(p, name, (256 * h * d, h * d, d))
+    p.lse_stride = (4 * 256, 256)
+    p.softmax_scale = 0.1
+    p.causal = 1
+    return p
+
+
+def main():
+    lib = _lib.load()
+    out = {}
+    ptr = lambda i: ctypes.c_void_p(A * (i + 1))  # disjoint 1 MiB-apart fakes
+
+    def fwd(p, q=1, k=2, v=3, o=40, l=60, ws=80, wsb=256):
+        args = [None if x is None else ptr(x) for x in (q, k, v, o, l, ws)]
+        return lib.attn_fwd(ctypes.byref(p), *args[:5], args[5], wsb, None)
+
+    def case(name, expect, status):
+        out[name] = [expect, _lib.STATUS.get(status, str(status))]
+
+    p = good_problem()
+    case("null_q", "CPA_ERR_NULL", fwd(p, q=None))
+    case("null_problem", "CPA_ERR_NULL",
+         lib.attn_fwd(None, ptr(1), ptr(2), ptr(3), ptr(4), ptr(5), ptr(6), 256, None))
+    p = good_problem(); p.in_dtype = 7
+    case("bad_dtype", "CPA_ERR_DTYPE", fwd(p))
+    p = good_problem(); p.heads_q = 3
+    case("gqa_not_divisible", "CPA_ERR_SHAPE", fwd(p))
+    p = good_problem(d_qk=96, d_v=96)
+    case("head_dim_96_declined", "CPA_ERR_UNSUPPORTED", fwd(p))
+    p = good_problem(d_qk=260, d_v=260)
+    case("head_dim_not_multiple_of_8", "CPA_ERR_UNSUPPORTED", fwd(p))
+    p = good_problem(d_qk=128, d_v=64)
+    case("head_dims_pair_declined", "CPA_ERR_UNSUPPORTED", fwd(p))
+    p = good_problem(); p.k_stride = (256 * 2 * 128, 2 * 128 + 4, 128)
+    case("stride_not_multiple_of_8", "CPA_ERR_STRIDE", fwd(p))
+    p = good_problem()
+    case("misaligned_q", "CPA_ERR_ALIGN",
+         lib.attn_fwd(ctypes.byref(p), ctypes.c_void_p(A + 8), ptr(2), ptr(3), ptr(40),
+                      ptr(60), ptr(80), 256, None))
+    p = good_problem()
+    case("workspace_small", "CPA_ERR_WORKSPACE", fwd(p, wsb=16))
+    case("workspace_null", "CPA_ERR_WORKSPACE", fwd(p, ws=None))
+    p = good_problem()
+    case("output_overlaps_input", "CPA_ERR_OVERLAP", fwd(p, o=1))
+    p = good_problem(); p.num_q_segments = 2; p.q_seg_row[0] = 0; p.q_seg_row[1] = 0
+    case("segments_not_increasing", "CPA_ERR_SHAPE", fwd(p))
+    p = good_problem(); p.num_q_segments = 9
+    case("too_many_segments", "CPA_ERR_SHAPE", fwd(p))
+    p = good_problem(); p.softmax_scale = float("nan")
+    case("nan_scale", "CPA_ERR_SHAPE", fwd(p))
+    p = good_problem(); p.layout = 1; p.num_seqs = 2
+    case("thd_missing_metadata", "CPA_ERR_NULL", fwd(p))
+    p = good_problem(); p.seqlen_q = 1 << 31
+    case("seqlen_too_large", "CPA_ERR_SHAPE", fwd(p))
+
+    def bwd(p, flags=0, wsb=1 << 30, dq=100, dk=120, dv=140):
+        return lib.attn_bwd(ctypes.byref(p), ptr(1), ptr(2), ptr(3), ptr(40), ptr(50), ptr(60),
+                            ptr(dq), ptr(dk), ptr(dv), ptr(200), wsb, flags, None)
+
+    p = good_problem()
+    case("bwd_deterministic_declined", "CPA_ERR_UNSUPPORTED", bwd(p, flags=1))
+    case("bwd_unknown_flag", "CPA_ERR_UNSUPPORTED", bwd(p, flags=2))
+    need = lib.attn_bwd_workspace_size(ctypes.byref(p))
+    case("bwd_workspace_small", "CPA_ERR_WORKSPACE", bwd(p, wsb=need - 1))
+    case("bwd_outputs_overlap", "CPA_ERR_OVERLAP", bwd(p, dk=100))
+    case("bwd_output_overlaps_input", "CPA_ERR_OVERLAP", bwd(p, dq=2))
+    out["bwd_workspace_bytes"] = ["int", int(need)]
+
+    md = _lib.MergeDesc()
+    md.batch, md.heads, md.d_v, md.seqlen = 1, 4, 128, 64
+    md.acc_stride = md.part_stride = md.out_stride = (64 * 4 * 128, 4 * 128, 128)
+    md.lse_acc_stride = md.lse_part_stride = md.lse_out_stride = (4 * 64, 64)
+    md.acc_dtype = md.part_dtype = md.out_dtype = 1
+    st = lib.attn_merge_lse(ctypes.byref(md), ptr(1), ptr(2), ptr(3), ptr(4), ptr(3), ptr(5), None)
+    case("merge_out_overlaps_part", "CPA_ERR_OVERLAP", st)
+    md.out_dtype = 0
+    st = lib.attn_merge_lse(ctypes.byref(md), ptr(1), ptr(2), ptr(3), ptr(4), ptr(1), ptr(2), None)
+    case("merge_inplace_dtype_change", "CPA_ERR_OVERLAP", st)
+    md.out_dtype = 9
+    st = lib.attn_merge_lse(ctypes.byref(md), ptr(1), ptr(2), ptr(3), ptr(4), ptr(5), ptr(6), None)
+    case("merge_bad_dtype", "CPA_ERR_DTYPE", st)
+
+    pd = _lib.PackDesc()
+    pd.batch, pd.heads, pd.d_v, pd.o_dtype, pd.groups, pd.seqlen = 1, 6, 128, 0, 4, 64
+    pd.o_stride = (64 * 6 * 128, 6 * 128, 128)
+    pd.lse_stride = (6 * 64, 64)
+    case("pack_heads_not_divisible", "CPA_ERR_SHAPE",
+         lib.pack_saved(ctypes.byref(pd), ptr(1), ptr(2), ptr(3), 1 << 24, None))
+    out["pack_size_invalid_is_zero"] = ["int", int(lib.pack_saved_size(ctypes.byref(pd)))]
+    pd.groups = 3
+    n = lib.pack_saved_size(ctypes.byref(pd))
+    out["pack_size_valid"] = ["int", int(n)]
+    case("pack_buffer_small", "CPA_ERR_SHAPE",
+         lib.pack_saved(ctypes.byref(pd), ptr(1), ptr(2), ptr(3), n - 1, None))
+    case("pack_buffer_overlaps_o", "CPA_ERR_OVERLAP",
+         lib.pack_saved(ctypes.byref(pd), ptr(1), ptr(2), ptr(1), n, None))
+    case("unpack_buffer_overlaps_lse", "CPA_ERR_OVERLAP",
+         lib.unpack_saved(ctypes.byref(pd), ptr(2), n, ptr(1), ptr(2), None))
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,90 @@
+"""Pass/fail criteria for GPU results against the fp64 oracle.
+
+The accuracy bar is the one TransformerEngine PR 3527 ("cuDNN FROST
+attention backend for head_dim in (256, 512]", Verification and the test
+commits) applies: the error of the kernel against an fp64 reference must be
+at most twice the error the reference itself incurs from reduced-precision
+inputs, measured per case:
+
+    err(gpu, true) <= 2 * err(naive, true)
+
+where ``true`` is the oracle on the fp32 draws (promoted to fp64),
+``naive`` is the oracle on the bf16-rounded inputs, and err is the maximum
+absolute difference over real (non-padding, finite) elements.  Gradients
+must also have relative L2 distance below 0.008 from the oracle on the
+kernel's own inputs (PR 3510, "Add head-parallel FA4 backward for cuDNN CP
+attention", Validation).  No absolute slack is added.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def as64(x):
+    import torch
+    if isinstance(x, torch.Tensor):
+        return x.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _mask(*arrs, mask=None):
+    m = np.ones(arrs[0].shape, dtype=bool) if mask is None else np.asarray(mask, bool)
+    for a in arrs:
+        m = m & np.isfinite(a)
+    return m
+
+
+def max_err(a, b, mask=None):
+    a, b = as64(a), as64(b)
+    m = _mask(b, mask=mask)
+    if not m.any():
+        return 0.0
+    d = np.abs(a[m] - b[m])
+    return float(np.max(d)) if np.all(np.isfinite(d)) else float("inf")
+
+
+def rel_l2(a, b, mask=None):
+    a, b = as64(a), as64(b)
+    m = _mask(b, mask=mask)
+    num = np.linalg.norm((a - b)[m])
+    den = np.linalg.norm(b[m])
+    return float(num / den) if den > 0 else float(num)
+
+
+def evaluate(gpu, true, naive, *, mask=None, grad=False):
+    """Return a dict with err, floor, ratio (= err / (2*floor)), rel_l2 and
+    pass flags."""
+    g, t, n = as64(gpu), as64(true), as64(naive)
+    err = max_err(g, t, mask)
+    floor = max_err(n, t, mask)
+    res = {"err": err, "floor": floor,
+           "ratio": err / (2 * floor) if floor > 0 else (0.0 if err == 0 else float("inf")),
+           "pass_floor": err <= 2 * floor}
+    if grad:
+        res["rel_l2"] = rel_l2(g, n, mask)
+        res["pass_l2"] = res["rel_l2"] < 0.008
+    return res
+
+
+def check(name, gpu, true, naive, *, mask=None, grad=False, log=None):
+    r = evaluate(gpu, true, naive, mask=mask, grad=grad)
+    if log is not None:
+        log[name] = r
+    assert r["pass_floor"], f"{name}: err {r['err']:.3e} > 2 x floor {r['floor']:.3e}"
+    if grad:
+        assert r["pass_l2"], f"{name}: rel L2 {r['rel_l2']:.4f} >= 0.008"
+    return r
+
+
+def check_lse(name, gpu, true, naive, *, mask=None, log=None):
+    """LSE: -inf exactly where the oracle has -inf (keyless rows), the
+    criterion on the finite entries, and |gpu - naive| <= 1e-4 (an O(1)
+    error such as a wrong log base or scale is far above this)."""
+    g, t, n = as64(gpu), as64(true), as64(naive)
+    m = np.ones(t.shape, bool) if mask is None else np.asarray(mask, bool)
+    assert np.array_equal(np.isneginf(g[m]), np.isneginf(t[m])), f"{name}: -inf rows differ"
+    fin = m & np.isfinite(t)
+    r = check(name, g, t, n, mask=fin, log=log)
+    dev = max_err(g, n, fin)
+    assert dev <= 1e-4, f"{name}: |lse - lse_naive| = {dev:.3e}"
+    return r

@@ -1,0 +1,147 @@
+"""GPU forward/backward vs the fp64 oracle, element by element, at sizes
+that span several tiles with ragged tails, for every head-dim variant,
+dtype path, GQA, causal alignment, query segments and KV-block offsets.
+
+Criterion per output (tests/criteria.py): err(gpu, true) <= 2 err(naive,
+true); gradients also rel-L2 < 0.008; LSE -inf exactly on keyless rows.
+A 1% softmax-scale error must fail (PR 3527, commit on the fp64
+reference: a deliberate 1% scale error is rejected in every combination).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import criteria
+from tests.gpu_util import dev, naive64, say, true64
+
+pytestmark = pytest.mark.gpu
+
+import bwd_causal_flash_amd as cpa  # noqa: E402
+
+# name, B, Sq, Sk, Hq, Hkv, Dqk, Dv, in, out, causal, segments, k_pos_begin
+CASES = [
+    ("d64_fp32_io", 1, 200, 200, 2, 2, 64, 64, "fp32", "fp32", True, None, 0),
+    ("d128_ragged_b2", 2, 300, 300, 4, 4, 128, 128, "bf16", "bf16", True, None, 0),
+    ("d192_128_dual_chunk", 1, 256, 1024, 4, 4, 192, 128, "bf16", "bf16", True,
+     [(0, 0), (128, 896)], 0),
+    ("d128_gqa_bottom_right", 1, 150, 390, 8, 2, 128, 128, "bf16", "bf16", True, [(0, 240)], 0),
+    ("d128_q_longer_keyless", 1, 300, 100, 4, 4, 128, 128, "bf16", "bf16", True, [(0, -200)], 0),
+    ("d256_gqa", 1, 270, 270, 4, 2, 256, 256, "bf16", "bf16", True, None, 0),
+    ("d512_gqa", 1, 260, 260, 4, 2, 512, 512, "bf16", "bf16", True, None, 0),
+    ("d128_noncausal_rect", 1, 130, 190, 2, 2, 128, 128, "bf16", "bf16", False, None, 0),
+    ("d192_kv_block_partial_fp32out", 1, 200, 256, 2, 2, 192, 128, "bf16", "fp32", True,
+     [(0, 700)], 512),
+    ("d64_fp32_in_bf16_out", 1, 190, 190, 2, 1, 64, 64, "fp32", "bf16", True, None, 0),
+]
+
+DT = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+def _draw(case, seed):
+    name, b, sq, sk, hq, hkv, dqk, dv = case[:8]
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(b, sq, hq, dqk, generator=g)
+    k = torch.randn(b, sk, hkv, dqk, generator=g)
+    v = torch.randn(b, sk, hkv, dv, generator=g)
+    do = torch.randn(b, sq, hq, dv, generator=g)
+    return q, k, v, do
+
+
+def _oracle(case, q, k, v, do):
+    name, b, sq, sk, hq, hkv, dqk, dv, _, _, causal, segs, kp0 = case
+    scale = 1.0 / math.sqrt(dqk)
+    res = {}
+    for kind, f in (("true", true64), ("naive", naive64)):
+        o, lse = oracle.bshd_forward(f(q), f(k), f(v), scale, segs, kp0, causal)
+        dq, dk, dv_ = oracle.bshd_backward(f(q), f(k), f(v), f(do), scale, segs, kp0, causal)
+        res[kind] = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv_)
+    return res
+
+
+def _gpu(case, q, k, v, do, scale_mult=1.0):
+    name, b, sq, sk, hq, hkv, dqk, dv, idt, odt, causal, segs, kp0 = case
+    d = dev()
+    qi, ki, vi, doi = (x.to(DT[idt]).to(d) for x in (q, k, v, do))
+    scale = scale_mult / math.sqrt(dqk)
+    say(f"fwd {name} scale x{scale_mult}")
+    o, lse = cpa.forward(qi, ki, vi, out_dtype=DT[odt], causal=causal, scale=scale,
+                         q_segments=segs, k_pos_begin=kp0)
+    o_in = o.to(DT[idt])            # the backward reads O in the input dtype
+    say(f"bwd {name} scale x{scale_mult}")
+    dq, dk, dv_ = cpa.backward(qi, ki, vi, o_in, doi, lse, out_dtype=DT[odt], causal=causal,
+                               scale=scale, q_segments=segs, k_pos_begin=kp0)
+    torch.cuda.synchronize()
+    return dict(o=o.permute(0, 1, 2, 3), lse=lse, dq=dq, dk=dk, dv=dv_)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_fwd_bwd_matches_oracle(case):
+    q, k, v, do = _draw(case, 100 + CASES.index(case))
+    ref = _oracle(case, q, k, v, do)
+    out = _gpu(case, q, k, v, do)
+    log = {}
+    criteria.check("O", out["o"], ref["true"]["o"], ref["naive"]["o"], log=log)
+    criteria.check_lse("LSE", out["lse"], ref["true"]["lse"], ref["naive"]["lse"], log=log)
+    for g in ("dq", "dk", "dv"):
+        criteria.check(g, out[g], ref["true"][g], ref["naive"][g], grad=True, log=log)
+    print(case[0], {k_: {kk: round(vv, 4) if isinstance(vv, float) else vv
+                         for kk, vv in v_.items()} for k_, v_ in log.items()})
+    # keyless rows: exact zeros
+    if case[0] == "d128_q_longer_keyless":
+        assert (out["o"][:, :200].float() == 0).all()
+        assert (out["dq"][:, :200].float() == 0).all()
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[3], CASES[6]], ids=lambda c: c[0])
+def test_one_percent_scale_error_is_rejected(case):
+    q, k, v, do = _draw(case, 100 + CASES.index(case))
+    ref = _oracle(case, q, k, v, do)
+    out = _gpu(case, q, k, v, do, scale_mult=1.01)
+    r = criteria.evaluate(out["o"], ref["true"]["o"], ref["naive"]["o"])
+    assert not r["pass_floor"], r
+    for g in ("dq", "dk"):
+        r = criteria.evaluate(out[g], ref["true"][g], ref["naive"][g], grad=True)
+        assert not (r["pass_floor"] and r["pass_l2"]), (g, r)
+
+
+def test_forward_bitwise_deterministic_and_stream_independent():
+    case = CASES[2]
+    q, k, v, do = _draw(case, 7)
+    d = dev()
+    qi, ki, vi = (x.to(torch.bfloat16).to(d) for x in (q, k, v))
+    segs = case[11]
+    say("fwd determinism x50")
+    o0, l0 = cpa.forward(qi, ki, vi, q_segments=segs)
+    for _ in range(49):
+        o1, l1 = cpa.forward(qi, ki, vi, q_segments=segs)
+        assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+        assert torch.equal(l0.view(torch.int32), l1.view(torch.int32))
+    side = torch.cuda.Stream()
+    say("fwd on side stream")
+    with torch.cuda.stream(side):
+        o2, l2 = cpa.forward(qi, ki, vi, q_segments=segs)
+    side.synchronize()
+    assert torch.equal(o0.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l0.view(torch.int32), l2.view(torch.int32))
+
+
+def test_gpu_closed_form_zero_query():
+    """Q = 0: O_i is the mean of V_0..V_i and LSE_i = ln(i+1) (up to bf16
+    rounding of the output)."""
+    d = dev()
+    s, h, dd = 333, 2, 128
+    g = torch.Generator().manual_seed(3)
+    q = torch.zeros(1, s, h, dd)
+    k = torch.randn(1, s, h, dd, generator=g)
+    v = torch.randn(1, s, h, dd, generator=g)
+    say("fwd zero query")
+    o, lse = cpa.forward(q.to(torch.bfloat16).to(d), k.to(torch.bfloat16).to(d),
+                         v.to(torch.bfloat16).to(d), out_dtype=torch.float32)
+    vb = v.to(torch.bfloat16).double()
+    mean = torch.cumsum(vb, dim=1) / torch.arange(1, s + 1, dtype=torch.float64)[None, :, None, None]
+    assert torch.allclose(o.double().cpu(), mean, atol=1e-5, rtol=0)
+    ln = torch.log(torch.arange(1, s + 1, dtype=torch.float64))
+    assert torch.allclose(lse.double().cpu()[0], ln[None].expand(h, s), atol=2e-6, rtol=0)

@@ -1,0 +1,132 @@
+"""Packed THD varlen on the GPU: per-document parity with the oracle,
+NaN-poisoned padding inputs, sentinel-filled padding outputs left bit for
+bit unchanged, empty documents, bottom-right alignment with different query
+and key lengths, and the device metadata check.
+
+Padded THD = physical padded offsets plus visible lengths (PR 3149, "Enable
+FA4 for context-parallel attention", Description); padding canaries and an
+empty sequence follow PR 3699's review ("Add cuDNN OSS backward dispatch for
+context parallel attention": physical gaps and an empty sequence).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import criteria
+from tests.gpu_util import bits, dev, naive64, say, true64
+
+pytestmark = pytest.mark.gpu
+
+import bwd_causal_flash_amd as cpa  # noqa: E402
+
+SENT_BF16 = 0x7FC1
+SENT_F32 = 0x7FC00001
+
+
+def _layout(lens, pitch=64):
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + (L + pitch - 1) // pitch * pitch + (0 if L % pitch else 0))
+    return np.asarray(lens, np.int32), np.asarray(cu, np.int32)
+
+
+def _sentinel(shape, dtype, d):
+    if dtype == torch.bfloat16:
+        return torch.full(shape, SENT_BF16, dtype=torch.int16, device=d).view(torch.bfloat16)
+    return torch.full(shape, SENT_F32, dtype=torch.int32, device=d).view(torch.float32)
+
+
+def _pad_rows(cu, used):
+    rows = []
+    for n in range(len(used)):
+        rows.extend(range(int(cu[n]) + int(used[n]), int(cu[n + 1])))
+    return np.asarray(rows, np.int64)
+
+
+@pytest.mark.parametrize("bottom_right", [False, True])
+def test_thd_parity_and_padding_untouched(bottom_right):
+    used_q = np.array([37, 0, 130, 1, 200, 64, 5], np.int32)
+    used_k = used_q.copy() if not bottom_right else np.array([50, 3, 100, 70, 200, 64, 0], np.int32)
+    pitch = 64
+    cu_q = np.concatenate([[0], np.cumsum([max(1, (max(a, b) + pitch - 1) // pitch) * pitch
+                                           for a, b in zip(used_q, used_k)])]).astype(np.int32)
+    cu_k = cu_q.copy()
+    T = int(cu_q[-1])
+    hq, hkv, d = 4, 2, 128
+    g = torch.Generator().manual_seed(11 + bottom_right)
+    q = torch.randn(T, hq, d, generator=g)
+    k = torch.randn(T, hkv, d, generator=g)
+    v = torch.randn(T, hkv, d, generator=g)
+    do = torch.randn(T, hq, d, generator=g)
+    dv_ = dev()
+    pad_q = _pad_rows(cu_q, used_q)
+    pad_k = _pad_rows(cu_k, used_k)
+    qi, ki, vi, doi = (x.to(torch.bfloat16).to(dv_) for x in (q, k, v, do))
+    # poison the padding rows of every input
+    qi[pad_q] = float("nan"); doi[pad_q] = float("nan")
+    ki[pad_k] = float("nan"); vi[pad_k] = float("nan")
+    vl = cpa.Varlen(torch.tensor(cu_q, device=dv_), torch.tensor(cu_k, device=dv_),
+                    torch.tensor(used_q, device=dv_), torch.tensor(used_k, device=dv_),
+                    int(used_q.max()), int(used_k.max()), bottom_right)
+    o = _sentinel((T, hq, d), torch.bfloat16, dv_)
+    lse = _sentinel((hq, T), torch.float32, dv_)
+    say(f"thd fwd br={bottom_right}")
+    ws = cpa.attn_fwd(qi, ki, vi, o, lse, varlen=vl)
+    dq = _sentinel((T, hq, d), torch.bfloat16, dv_)
+    dk = _sentinel((T, hkv, d), torch.bfloat16, dv_)
+    dvv = _sentinel((T, hkv, d), torch.bfloat16, dv_)
+    say(f"thd bwd br={bottom_right}")
+    ws2 = cpa.attn_bwd(qi, ki, vi, o, doi, lse, dq, dk, dvv, varlen=vl)
+    torch.cuda.synchronize()
+    assert cpa.workspace_error_flag(ws) == 0 and cpa.workspace_error_flag(ws2) == 0
+    for t, rows in ((o, pad_q), (dq, pad_q), (dk, pad_k), (dvv, pad_k)):
+        assert (bits(t)[rows] == np.int16(SENT_BF16)).all()
+    assert (bits(lse)[:, pad_q] == np.int32(SENT_F32)).all()
+
+    scale = 1 / math.sqrt(d)
+    ref = {}
+    for kind, f in (("true", true64), ("naive", naive64)):
+        oo, ll = oracle.thd_forward(f(q), f(k), f(v), scale, cu_q, cu_k, used_q, used_k, True,
+                                    bottom_right)
+        a, b_, c = oracle.thd_backward(f(q), f(k), f(v), f(do), scale, cu_q, cu_k, used_q,
+                                       used_k, True, bottom_right)
+        ref[kind] = dict(o=oo, lse=ll, dq=a, dk=b_, dv=c)
+    real_q = np.ones(T, bool); real_q[pad_q] = False
+    real_k = np.ones(T, bool); real_k[pad_k] = False
+    mq = np.broadcast_to(real_q[:, None, None], (T, hq, d))
+    mk = np.broadcast_to(real_k[:, None, None], (T, hkv, d))
+    log = {}
+    criteria.check("O", o, ref["true"]["o"], ref["naive"]["o"], mask=mq, log=log)
+    criteria.check_lse("LSE", lse, ref["true"]["lse"], ref["naive"]["lse"],
+                       mask=np.broadcast_to(real_q[None], (hq, T)), log=log)
+    criteria.check("dq", dq, ref["true"]["dq"], ref["naive"]["dq"], mask=mq, grad=True, log=log)
+    criteria.check("dk", dk, ref["true"]["dk"], ref["naive"]["dk"], mask=mk, grad=True, log=log)
+    criteria.check("dv", dvv, ref["true"]["dv"], ref["naive"]["dv"], mask=mk, grad=True, log=log)
+    print(log)
+
+
+def test_thd_malformed_metadata_sets_flag_and_skips_sequence():
+    """A sequence whose visible length exceeds its physical span is treated
+    as empty (nothing read or written) and the workspace flag is raised; the
+    other sequences are still computed."""
+    d = dev()
+    hq, dd = 2, 64
+    cu = np.array([0, 64, 128], np.int32)
+    used = np.array([40, 100], np.int32)       # 100 > 64: malformed
+    T = 128
+    g = torch.Generator().manual_seed(1)
+    q, k, v = (torch.randn(T, hq, dd, generator=g) for _ in range(3))
+    vl = cpa.Varlen(torch.tensor(cu, device=d), torch.tensor(cu, device=d),
+                    torch.tensor(used, device=d), torch.tensor(used, device=d), 100, 100)
+    o = _sentinel((T, hq, dd), torch.bfloat16, d)
+    lse = _sentinel((hq, T), torch.float32, d)
+    say("thd malformed metadata")
+    ws = cpa.attn_fwd(q.to(torch.bfloat16).to(d), k.to(torch.bfloat16).to(d),
+                      v.to(torch.bfloat16).to(d), o, lse, varlen=vl)
+    torch.cuda.synchronize()
+    assert cpa.workspace_error_flag(ws) == 1
+    assert (bits(o)[64:] == np.int16(SENT_BF16)).all()
+    assert not (bits(o)[:40] == np.int16(SENT_BF16)).any()
