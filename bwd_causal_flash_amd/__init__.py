@@ -30,7 +30,7 @@ from ._lib import (CPA_BF16, CPA_FP32, CPA_FLAG_DETERMINISTIC, CpaError,  # noqa
                    MergeDesc, PackDesc, Problem, STATUS_CODE)
 
 __all__ = [
-    "attn_fwd", "attn_bwd", "attn_merge_lse", "pack_saved", "unpack_saved",
+    "attn_fwd", "attn_bwd", "bwd_workspace_bytes", "attn_merge_lse", "pack_saved", "unpack_saved",
     "pack_saved_size", "Varlen", "CpaError", "forward", "backward",
     "workspace_error_flag", "library",
 ]
@@ -158,8 +158,15 @@ def attn_fwd(q, k, v, o, lse, *, causal=True, scale=None, q_segments=None, k_pos
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, *, causal=True, scale=None, q_segments=None,
              k_pos_begin=0, varlen: Optional[Varlen] = None, workspace=None, flags=0,
-             stream=None) -> torch.Tensor:
-    """Backward into preallocated dq, dk, dv.  Returns the workspace."""
+             stream=None, step: str = "attn_bwd") -> torch.Tensor:
+    """Backward into preallocated dq, dk, dv.  Returns the workspace.
+
+    ``step`` selects the C entry point: "attn_bwd" (all three steps), or one
+    of "attn_bwd_pre", "attn_bwd_main", "attn_bwd_post"."""
+    if step not in ("attn_bwd", "attn_bwd_pre", "attn_bwd_main", "attn_bwd_post"):
+        raise ValueError(step)
+    if o.dtype != q.dtype or dout.dtype != q.dtype:
+        raise TypeError("o and dout must have q's dtype")
     lib = _lib.load()
     p = _fill_problem(q, k, v, causal=causal, scale=scale, out_dtype=_dtype_code(dq),
                       q_segments=q_segments, k_pos_begin=k_pos_begin, varlen=varlen)
@@ -173,10 +180,11 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, *, causal=True, scale=None, q_se
     need = lib.attn_bwd_workspace_size(ctypes.byref(p))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    st = lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
-                      _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                      workspace.numel(), int(flags), _stream_handle(stream))
-    _lib.check(st, "attn_bwd")
+    fn = getattr(lib, step)
+    st = fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), int(flags),
+            _stream_handle(stream))
+    _lib.check(st, step)
     return workspace
 
 

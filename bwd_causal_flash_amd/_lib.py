@@ -85,6 +85,12 @@ EXPORTS = {
                  [ctypes.c_size_t, ctypes.c_void_p]),
     "attn_bwd": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 +
                  [ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]),
+    "attn_bwd_pre": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 +
+                     [ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]),
+    "attn_bwd_main": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 +
+                      [ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]),
+    "attn_bwd_post": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 +
+                      [ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]),
     "attn_merge_lse": (ctypes.c_int, [ctypes.POINTER(MergeDesc)] + [ctypes.c_void_p] * 7),
     "pack_saved_size": (ctypes.c_size_t, [ctypes.POINTER(PackDesc)]),
     "pack_saved": (ctypes.c_int, [ctypes.POINTER(PackDesc), ctypes.c_void_p, ctypes.c_void_p,

@@ -240,9 +240,13 @@ cpa_status attn_fwd(const cpa_problem* p, const void* q, const void* k, const vo
   return CPA_OK;
 }
 
-cpa_status attn_bwd(const cpa_problem* p, const void* q, const void* k, const void* v,
-                    const void* o, const void* dout, const float* lse, void* dq, void* dk,
-                    void* dv, void* ws, size_t ws_bytes, uint32_t flags, cpa_stream_t stream) {
+}  // extern "C"
+
+namespace {
+// Validation shared by attn_bwd and its three steps; fills the kernel args.
+cpa_status bwd_prepare(const cpa_problem* p, const void* q, const void* k, const void* v,
+                       const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                       void* dv, void* ws, size_t ws_bytes, uint32_t flags, AttnArgs& a) {
   cpa_status st = check_problem(p);
   if (st != CPA_OK) return st;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return CPA_ERR_NULL;
@@ -274,8 +278,7 @@ cpa_status attn_bwd(const cpa_problem* p, const void* q, const void* k, const vo
   for (int i = 0; i < 4; ++i)
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outs[j])) return CPA_ERR_OVERLAP;
-
-  AttnArgs a = make_args(p);
+  a = make_args(p);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -286,11 +289,50 @@ cpa_status attn_bwd(const cpa_problem* p, const void* q, const void* k, const vo
   a.dk = dk;
   a.dv = dv;
   set_bwd_ws(a, p, ws);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (launch_meta_check(a, s) != hipSuccess) return CPA_ERR_LAUNCH;
-  if (launch_bwd(a, p->d_qk, p->d_v, p->in_dtype, p->out_dtype, s) != hipSuccess)
-    return CPA_ERR_LAUNCH;
   return CPA_OK;
+}
+
+// steps: bit 0 = pre (with the metadata check), bit 1 = main, bit 2 = post.
+cpa_status bwd_run(const cpa_problem* p, const void* q, const void* k, const void* v,
+                   const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   void* ws, size_t ws_bytes, uint32_t flags, cpa_stream_t stream, int steps) {
+  AttnArgs a;
+  const cpa_status st = bwd_prepare(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, flags, a);
+  if (st != CPA_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((steps & 1) && launch_meta_check(a, s) != hipSuccess) return CPA_ERR_LAUNCH;
+  for (int step = 0; step < 3; ++step)
+    if ((steps >> step) & 1)
+      if (launch_bwd(a, p->d_qk, p->d_v, p->in_dtype, p->out_dtype, step, s) != hipSuccess)
+        return CPA_ERR_LAUNCH;
+  return CPA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+cpa_status attn_bwd(const cpa_problem* p, const void* q, const void* k, const void* v,
+                    const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                    void* dv, void* ws, size_t ws_bytes, uint32_t flags, cpa_stream_t stream) {
+  return bwd_run(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, flags, stream, 7);
+}
+
+cpa_status attn_bwd_pre(const cpa_problem* p, const void* q, const void* k, const void* v,
+                        const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                        void* dv, void* ws, size_t ws_bytes, uint32_t flags, cpa_stream_t stream) {
+  return bwd_run(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, flags, stream, 1);
+}
+
+cpa_status attn_bwd_main(const cpa_problem* p, const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                         void* dv, void* ws, size_t ws_bytes, uint32_t flags, cpa_stream_t stream) {
+  return bwd_run(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, flags, stream, 2);
+}
+
+cpa_status attn_bwd_post(const cpa_problem* p, const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                         void* dv, void* ws, size_t ws_bytes, uint32_t flags, cpa_stream_t stream) {
+  return bwd_run(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, flags, stream, 4);
 }
 
 cpa_status attn_merge_lse(const cpa_merge_desc* d, const void* o_acc, const float* lse_acc,

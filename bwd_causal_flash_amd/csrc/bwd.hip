@@ -50,8 +50,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a) {
                        (int64_t)h * a.o_stride[2] + gl * 8;
     const int64_t db = (a.thd ? 0 : (int64_t)z * a.do_stride[0]) + prow * a.do_stride[1] +
                        (int64_t)h * a.do_stride[2] + gl * 8;
+    // dO enters the products rounded to bf16, so D uses the same rounded dO:
+    // then D_i = sum_j P_ij dP_ij holds for the kernel's own dP.
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += to_f32(O[ob + e]) * to_f32(dO[db + e]);
+    for (int e = 0; e < 8; ++e) acc += to_f32(O[ob + e]) * (float)(bf16)dO[db + e];
   }
 #pragma unroll
   for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, G);
@@ -375,29 +377,34 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
 
 // ---------------------------------------------------------------- launch
 
+template <int DQK, int DV>
+struct BwdCfg {
+  static constexpr bool BIG = DQK > 256 || DV > 256;
+  static constexpr int OCK = BIG ? DQK / 2 : DQK;
+  static constexpr int OCV = BIG ? DV / 2 : DV;
+  static constexpr int NCH = DQK / OCK;
+  static constexpr int BM = DQK + DV > 320 ? 32 : 64;
+  static constexpr bool KVREG = DQK + DV <= 320;
+};
+
 template <int DQK, int DV, typename TIn, typename TOut>
-static hipError_t bwd_variant(const AttnArgs& a, hipStream_t st) {
-  constexpr bool BIG = DQK > 256 || DV > 256;
-  constexpr int OCK = BIG ? DQK / 2 : DQK;
-  constexpr int OCV = BIG ? DV / 2 : DV;
-  constexpr int NCH = DQK / OCK;
-  constexpr int BM = DQK + DV > 320 ? 32 : 64;
-  constexpr bool KVREG = DQK + DV <= 320;
+static hipError_t bwd_variant(const AttnArgs& a, int step, hipStream_t st) {
+  using C = BwdCfg<DQK, DV>;
   const int qrows = a.thd ? a.max_q : (int)a.seqlen_q;
   const int krows = a.thd ? a.max_k : (int)a.seqlen_k;
   if (a.nseq == 0) return hipSuccess;
-  if (qrows > 0) {
+  if (step == 0 && qrows > 0) {
     constexpr int PB = 256 / (DV / 8);
     const int64_t pairs = (int64_t)qrows * a.heads_q;
     dim3 g((unsigned)((pairs + PB - 1) / PB), 1, a.nseq);
     hipLaunchKernelGGL((bwd_pre_kernel<DV, DQK, TIn>), g, dim3(256), 0, st, a);
   }
-  if (krows > 0) {
-    dim3 g(a.heads_kv * NCH, (krows + 127) / 128, a.nseq);
-    hipLaunchKernelGGL((bwd_main_kernel<DQK, DV, OCK, OCV, BM, KVREG, TIn, TOut>), g, dim3(256), 0,
-                       st, a);
+  if (step == 1 && krows > 0) {
+    dim3 g(a.heads_kv * C::NCH, (krows + 127) / 128, a.nseq);
+    hipLaunchKernelGGL((bwd_main_kernel<DQK, DV, C::OCK, C::OCV, C::BM, C::KVREG, TIn, TOut>), g,
+                       dim3(256), 0, st, a);
   }
-  if (qrows > 0) {
+  if (step == 2 && qrows > 0) {
     constexpr int PB = 256 / pow2_at_least(DQK / 8);
     const int64_t pairs = (int64_t)qrows * a.heads_q;
     dim3 g((unsigned)((pairs + PB - 1) / PB), 1, a.nseq);
@@ -407,20 +414,21 @@ static hipError_t bwd_variant(const AttnArgs& a, hipStream_t st) {
 }
 
 template <int DQK, int DV>
-static hipError_t bwd_dtypes(const AttnArgs& a, int in_dt, int out_dt, hipStream_t st) {
-  if (in_dt == CPA_BF16 && out_dt == CPA_BF16) return bwd_variant<DQK, DV, bf16, bf16>(a, st);
-  if (in_dt == CPA_BF16 && out_dt == CPA_FP32) return bwd_variant<DQK, DV, bf16, float>(a, st);
-  if (in_dt == CPA_FP32 && out_dt == CPA_BF16) return bwd_variant<DQK, DV, float, bf16>(a, st);
-  return bwd_variant<DQK, DV, float, float>(a, st);
+static hipError_t bwd_dtypes(const AttnArgs& a, int in_dt, int out_dt, int step, hipStream_t st) {
+  if (in_dt == CPA_BF16 && out_dt == CPA_BF16) return bwd_variant<DQK, DV, bf16, bf16>(a, step, st);
+  if (in_dt == CPA_BF16 && out_dt == CPA_FP32) return bwd_variant<DQK, DV, bf16, float>(a, step, st);
+  if (in_dt == CPA_FP32 && out_dt == CPA_BF16) return bwd_variant<DQK, DV, float, bf16>(a, step, st);
+  return bwd_variant<DQK, DV, float, float>(a, step, st);
 }
 
-hipError_t launch_bwd(const AttnArgs& a, int d_qk, int d_v, int in_dt, int out_dt,
+// step 0: D and dQ-accumulator zeroing; 1: main; 2: dQ cast.
+hipError_t launch_bwd(const AttnArgs& a, int d_qk, int d_v, int in_dt, int out_dt, int step,
                       hipStream_t st) {
-  if (d_qk == 64 && d_v == 64) return bwd_dtypes<64, 64>(a, in_dt, out_dt, st);
-  if (d_qk == 128 && d_v == 128) return bwd_dtypes<128, 128>(a, in_dt, out_dt, st);
-  if (d_qk == 192 && d_v == 128) return bwd_dtypes<192, 128>(a, in_dt, out_dt, st);
-  if (d_qk == 256 && d_v == 256) return bwd_dtypes<256, 256>(a, in_dt, out_dt, st);
-  if (d_qk == 512 && d_v == 512) return bwd_dtypes<512, 512>(a, in_dt, out_dt, st);
+  if (d_qk == 64 && d_v == 64) return bwd_dtypes<64, 64>(a, in_dt, out_dt, step, st);
+  if (d_qk == 128 && d_v == 128) return bwd_dtypes<128, 128>(a, in_dt, out_dt, step, st);
+  if (d_qk == 192 && d_v == 128) return bwd_dtypes<192, 128>(a, in_dt, out_dt, step, st);
+  if (d_qk == 256 && d_v == 256) return bwd_dtypes<256, 256>(a, in_dt, out_dt, step, st);
+  if (d_qk == 512 && d_v == 512) return bwd_dtypes<512, 512>(a, in_dt, out_dt, step, st);
   return hipErrorInvalidValue;
 }
 

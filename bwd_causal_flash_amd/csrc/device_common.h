@@ -98,11 +98,19 @@ __device__ __forceinline__ bf16x8 lds_row8(const bf16* tile, int pitch, int r,
   return *reinterpret_cast<const bf16x8*>(tile + r * pitch + c);
 }
 
-// Swap values between lanes l and l^32.
-__device__ __forceinline__ float xhalf(float x) {
+// Combine a per-lane value over the two 32-lane halves of a wave.  With the
+// same value in both operands, v_permlane32_swap returns the low half's
+// values in every lane of its first result and the high half's in every
+// lane of its second, so both halves see the identical combination.
+__device__ __forceinline__ float sum_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
                                             __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                            __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) {

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const AttnArgs a) {
         x[kb][v] = val;
         mx = fmaxf(mx, val);
       }
-    mx = fmaxf(mx, xhalf(mx));
+    mx = max_halves(mx);
     const float m_new = fmaxf(m_run, mx);
     const float base = (m_new == -kInf) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - base);
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const AttnArgs a) {
         x[kb][v] = fast_exp2(x[kb][v] - base);
         rs += x[kb][v];
       }
-    rs += xhalf(rs);
+    rs = sum_halves(rs);
     l_run = l_run * alpha + rs;
     m_run = m_new;
 #pragma unroll

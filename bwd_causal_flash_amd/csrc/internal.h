@@ -82,8 +82,10 @@ struct PackArgs {
 // error.
 hipError_t launch_fwd(const AttnArgs& a, int d_qk, int d_v, int in_dt,
                       int out_dt, hipStream_t s);
+// step 0: D = rowsum(dO*O) and zeroing of the dQ accumulator; step 1: the
+// main key-outer kernel; step 2: dQ = s * accumulator in the output dtype.
 hipError_t launch_bwd(const AttnArgs& a, int d_qk, int d_v, int in_dt,
-                      int out_dt, hipStream_t s);
+                      int out_dt, int step, hipStream_t s);
 hipError_t launch_meta_check(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& m, int acc_dt, int part_dt,
                         int out_dt, hipStream_t s);

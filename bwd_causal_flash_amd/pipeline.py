@@ -132,10 +132,19 @@ class RankStep:
                                out_o, out_l, stream=stream)
         return self.o, self.lse
 
-    def backward(self, stream=None):
-        attn_bwd(self.q, self.k, self.v, self.o, self.dout, self.lse, self.dq, self.dk, self.dv,
-                 causal=True, scale=self.scale, q_segments=self.segments, k_pos_begin=0,
-                 workspace=self.bwd_ws, stream=stream)
+    def backward(self, stream=None, main_events=None):
+        """One backward over all query rows and keys.  ``main_events`` =
+        (start, end) HIP events recorded around the main kernel only."""
+        kw = dict(causal=True, scale=self.scale, q_segments=self.segments, k_pos_begin=0,
+                  workspace=self.bwd_ws, stream=stream)
+        args = (self.q, self.k, self.v, self.o, self.dout, self.lse, self.dq, self.dk, self.dv)
+        attn_bwd(*args, step="attn_bwd_pre", **kw)
+        if main_events:
+            main_events[0].record(stream)
+        attn_bwd(*args, step="attn_bwd_main", **kw)
+        if main_events:
+            main_events[1].record(stream)
+        attn_bwd(*args, step="attn_bwd_post", **kw)
         return self.dq, self.dk, self.dv
 
     def pack_roundtrip(self, stream=None):
@@ -143,10 +152,10 @@ class RankStep:
         unpack_saved(self.pack_buf, self.o_recv, self.lse_recv, self.pack_groups, stream=stream)
         return self.pack_buf
 
-    def step(self, stream=None):
+    def step(self, stream=None, main_events=None):
         self.forward(stream)
         self.pack_roundtrip(stream)
-        self.backward(stream)
+        self.backward(stream, main_events)
 
 
 def cp_chunks(seq_len: int, cp: int, rank: int):

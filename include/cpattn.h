@@ -177,6 +177,37 @@ cpa_status attn_bwd(const cpa_problem* p, const void* q, const void* k,
                     size_t ws_bytes, uint32_t flags, cpa_stream_t stream);
 
 /*
+ * The three steps attn_bwd enqueues, callable one by one with the same
+ * arguments (the backward helper chain of PR 3699, "Add cuDNN OSS backward
+ * dispatch for context parallel attention", Implementation and supported
+ * scope).  They must run in this order on one stream, with the same problem,
+ * tensors and workspace:
+ *   attn_bwd_pre   writes the metadata flag, D = rowsum(dO*O) (fp32, from
+ *                  the given O) and zeroes the fp32 dQ accumulator;
+ *   attn_bwd_main  recomputes P from the LSE and accumulates dK, dV (written
+ *                  to dk, dv) and dQ (into the workspace accumulator);
+ *   attn_bwd_post  writes dq = softmax_scale * accumulator.
+ * attn_bwd_main may be called several times between one pre and one post,
+ * with K/V (and k_pos_begin) of different key blocks, to accumulate dQ over
+ * the blocks of a ring while each call writes its own block's dK, dV.
+ */
+cpa_status attn_bwd_pre(const cpa_problem* p, const void* q, const void* k,
+                        const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv,
+                        void* ws, size_t ws_bytes, uint32_t flags,
+                        cpa_stream_t stream);
+cpa_status attn_bwd_main(const cpa_problem* p, const void* q, const void* k,
+                         const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv,
+                         void* ws, size_t ws_bytes, uint32_t flags,
+                         cpa_stream_t stream);
+cpa_status attn_bwd_post(const cpa_problem* p, const void* q, const void* k,
+                         const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv,
+                         void* ws, size_t ws_bytes, uint32_t flags,
+                         cpa_stream_t stream);
+
+/*
  * LSE merge of two partial attentions over disjoint key sets (the per-ring-
  * step combine of PR 3527's context-parallel commits: per-step kernel calls
  * interleaved with KV exchange and LSE correction).  Per (b, s, h):
@@ -228,8 +259,8 @@ typedef struct cpa_pack_desc {
 /* Total buffer bytes (host, pure); 0 for an invalid descriptor. */
 size_t pack_saved_size(const cpa_pack_desc* d);
 
-/* o, lse -> buf.  buf must hold pack_saved_size(d) bytes and must not
- * overlap o or lse (CPA_ERR_OVERLAP). */
+/* o, lse -> buf.  buf must hold pack_saved_size(d) bytes (else
+ * CPA_ERR_SHAPE) and must not overlap o or lse (CPA_ERR_OVERLAP). */
 cpa_status pack_saved(const cpa_pack_desc* d, const void* o,
                       const float* lse, void* buf, size_t buf_bytes,
                       cpa_stream_t stream);

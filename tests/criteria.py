@@ -9,11 +9,14 @@ inputs, measured per case:
     err(gpu, true) <= 2 * err(naive, true)
 
 where ``true`` is the oracle on the fp32 draws (promoted to fp64),
-``naive`` is the oracle on the bf16-rounded inputs, and err is the maximum
-absolute difference over real (non-padding, finite) elements.  Gradients
-must also have relative L2 distance below 0.008 from the oracle on the
-kernel's own inputs (PR 3510, "Add head-parallel FA4 backward for cuDNN CP
-attention", Validation).  No absolute slack is added.
+``naive`` is the oracle on the bf16-rounded inputs with its results stored
+in the output dtype (a bf16 reference takes bf16 in and gives bf16 out;
+for fp32 outputs nothing is rounded), and err is the maximum absolute
+difference over real (non-padding, finite) elements.  Gradients must also
+have relative L2 distance below 0.008 from the oracle on the kernel's own
+inputs (PR 3510, "Add head-parallel FA4 backward for cuDNN CP attention",
+Validation).  No absolute slack is added.  The ratio against the unrounded
+naive reference is reported too ("ratio_in"), as a diagnostic.
 """
 from __future__ import annotations
 
@@ -51,14 +54,26 @@ def rel_l2(a, b, mask=None):
     return float(num / den) if den > 0 else float(num)
 
 
-def evaluate(gpu, true, naive, *, mask=None, grad=False):
+def round_bf16(x):
+    """Round to bfloat16 (nearest even) and return fp64."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(as64(x))).to(torch.bfloat16).double().numpy()
+
+
+def _ratio(err, floor):
+    return err / (2 * floor) if floor > 0 else (0.0 if err == 0 else float("inf"))
+
+
+def evaluate(gpu, true, naive, *, mask=None, grad=False, out_bf16=False):
     """Return a dict with err, floor, ratio (= err / (2*floor)), rel_l2 and
-    pass flags."""
+    pass flags.  ``out_bf16``: the kernel's output dtype is bf16, so the
+    naive reference's results are stored in bf16 too."""
     g, t, n = as64(gpu), as64(true), as64(naive)
+    n_out = round_bf16(n) if out_bf16 else n
     err = max_err(g, t, mask)
-    floor = max_err(n, t, mask)
-    res = {"err": err, "floor": floor,
-           "ratio": err / (2 * floor) if floor > 0 else (0.0 if err == 0 else float("inf")),
+    floor = max_err(n_out, t, mask)
+    res = {"err": err, "floor": floor, "ratio": _ratio(err, floor),
+           "ratio_in": _ratio(err, max_err(n, t, mask)),
            "pass_floor": err <= 2 * floor}
     if grad:
         res["rel_l2"] = rel_l2(g, n, mask)
@@ -66,8 +81,12 @@ def evaluate(gpu, true, naive, *, mask=None, grad=False):
     return res
 
 
-def check(name, gpu, true, naive, *, mask=None, grad=False, log=None):
-    r = evaluate(gpu, true, naive, mask=mask, grad=grad)
+def passes(r):
+    return r["pass_floor"] and r.get("pass_l2", True)
+
+
+def check(name, gpu, true, naive, *, mask=None, grad=False, log=None, out_bf16=False):
+    r = evaluate(gpu, true, naive, mask=mask, grad=grad, out_bf16=out_bf16)
     if log is not None:
         log[name] = r
     assert r["pass_floor"], f"{name}: err {r['err']:.3e} > 2 x floor {r['floor']:.3e}"

@@ -99,12 +99,12 @@ def test_thd_parity_and_padding_untouched(bottom_right):
     mq = np.broadcast_to(real_q[:, None, None], (T, hq, d))
     mk = np.broadcast_to(real_k[:, None, None], (T, hkv, d))
     log = {}
-    criteria.check("O", o, ref["true"]["o"], ref["naive"]["o"], mask=mq, log=log)
+    criteria.check("O", o, ref["true"]["o"], ref["naive"]["o"], mask=mq, log=log, out_bf16=True)
     criteria.check_lse("LSE", lse, ref["true"]["lse"], ref["naive"]["lse"],
                        mask=np.broadcast_to(real_q[None], (hq, T)), log=log)
-    criteria.check("dq", dq, ref["true"]["dq"], ref["naive"]["dq"], mask=mq, grad=True, log=log)
-    criteria.check("dk", dk, ref["true"]["dk"], ref["naive"]["dk"], mask=mk, grad=True, log=log)
-    criteria.check("dv", dvv, ref["true"]["dv"], ref["naive"]["dv"], mask=mk, grad=True, log=log)
+    criteria.check("dq", dq, ref["true"]["dq"], ref["naive"]["dq"], mask=mq, grad=True, log=log, out_bf16=True)
+    criteria.check("dk", dk, ref["true"]["dk"], ref["naive"]["dk"], mask=mk, grad=True, log=log, out_bf16=True)
+    criteria.check("dv", dvv, ref["true"]["dv"], ref["naive"]["dv"], mask=mk, grad=True, log=log, out_bf16=True)
     print(log)
 
 
