@@ -84,6 +84,12 @@ cpa_status check_problem(const cpa_problem* p) {
       for (int t = 1; t < p->num_q_segments; ++t)
         if (p->q_seg_row[t] <= p->q_seg_row[t - 1]) return CPA_ERR_SHAPE;
     }
+    // positions are held in int32 by the kernels: keep |pos| < 2^30
+    const int64_t lim = 1ll << 30;
+    if (p->seqlen_q >= lim || p->seqlen_k >= lim) return CPA_ERR_SHAPE;
+    for (int t = 0; t < p->num_q_segments; ++t)
+      if (p->q_seg_pos[t] <= -lim || p->q_seg_pos[t] + p->seqlen_q >= lim) return CPA_ERR_SHAPE;
+    if (p->k_pos_begin <= -lim || p->k_pos_begin + p->seqlen_k >= lim) return CPA_ERR_SHAPE;
   } else {
     if (p->num_seqs < 0 || p->num_seqs > 65535) return CPA_ERR_SHAPE;
     if (p->max_seqlen_q < 0 || p->max_seqlen_k < 0) return CPA_ERR_SHAPE;
@@ -129,15 +135,15 @@ AttnArgs make_args(const cpa_problem* p) {
   if (p->layout == CPA_LAYOUT_BSHD && p->num_q_segments > 0) {
     a.nseg = p->num_q_segments;
     for (int t = 0; t < a.nseg; ++t) {
-      a.seg_row[t] = p->q_seg_row[t];
-      a.seg_pos[t] = p->q_seg_pos[t];
+      a.seg_row[t] = (int)p->q_seg_row[t];
+      a.seg_pos[t] = (int)p->q_seg_pos[t];
     }
   } else {
     a.nseg = 1;
     a.seg_row[0] = 0;
     a.seg_pos[0] = 0;
   }
-  a.k_pos0 = p->layout == CPA_LAYOUT_BSHD ? p->k_pos_begin : 0;
+  a.k_pos0 = p->layout == CPA_LAYOUT_BSHD ? (int)p->k_pos_begin : 0;
   return a;
 }
 

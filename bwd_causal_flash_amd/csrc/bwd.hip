@@ -109,20 +109,32 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(const AttnArgs a) {
 
 // ---------------------------------------------------------------- main
 
-template <int DQK, int DV, int OCK, int OCV, int BM, bool KVREG, typename TIn, typename TOut>
+template <int DQK, int DV, int OCK, int OCV, int BM, typename TIn, typename TOut>
 __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
   constexpr int BN = 128;
-  constexpr int QP = DQK + 8, OP = DV + 8, SP = BM + 8, KP = OCK + 8;
+  constexpr int QP = lds_pitch(DQK), OP = lds_pitch(DV), SP = lds_pitch(BM), KP = lds_pitch(OCK);
   constexpr int NQB = BM / 32;
   constexpr int KSQ = DQK / 16, KSV = DV / 16;
   constexpr int NDK = OCK / 32, NDV = OCV / 32;
+  // The workgroup's K tile in LDS serves both the dQ product and, read
+  // along rows, the B operand of S = Q K^T.  For small head dims the V tile
+  // is staged too (B operand of dP = dO V^T) and the next query tile is
+  // prefetched into registers during the current one; large head dims lack
+  // the registers and LDS for that and read V (and K, when only a column
+  // chunk of it is staged) from global memory.
+  constexpr bool SMALL = DQK + DV <= 320;
+  constexpr bool K_FROM_LDS = OCK == DQK;
+  constexpr bool V_FROM_LDS = SMALL;
+  constexpr bool PREFETCH = SMALL;
+  constexpr int VP = lds_pitch(DV);
   __shared__ __attribute__((aligned(16))) bf16 Qs[BM * QP];
   __shared__ __attribute__((aligned(16))) bf16 dOs[BM * OP];
   __shared__ __attribute__((aligned(16))) bf16 dSt[BN * SP];
   __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[V_FROM_LDS ? BN * VP : 8];
   __shared__ __attribute__((aligned(16))) float Ls[BM];
   __shared__ __attribute__((aligned(16))) float Dl[BM];
-  __shared__ int64_t Ps[BM];
+  __shared__ int Ps[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
@@ -133,16 +145,16 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
   const Seq s = load_seq(a, z);
   const int j0 = kt * BN;
   if (j0 >= s.klen) return;
-  const int64_t kp0 = kpos0(a);
+  const int kp0 = kpos0(a);
 
   const int jw = j0 + wave * 32;
   const int my_key = jw + lq;
   const bool key_valid = my_key < s.klen;
-  const int64_t my_kpos = kp0 + my_key;
+  const int my_kpos = kp0 + my_key;
   const bool wave_has_keys = jw < s.klen;
   const int wk_last = min(jw + 31, s.klen - 1);
-  const int64_t wkpos_lo = kp0 + jw, wkpos_hi = kp0 + wk_last;
-  const int64_t gkpos_lo = kp0 + j0;
+  const int wkpos_lo = kp0 + jw, wkpos_hi = kp0 + wk_last;
+  const int gkpos_lo = kp0 + j0;
 
   const TIn* Q = static_cast<const TIn*>(a.q);
   const TIn* K = static_cast<const TIn*>(a.k);
@@ -155,25 +167,10 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
   const TIn* krow = K + kbase + (int64_t)(key_valid ? my_key : 0) * a.k_stride[1];
   const TIn* vrow = V + vbase + (int64_t)(key_valid ? my_key : 0) * a.v_stride[1];
 
-  bf16x8 kreg[KVREG ? KSQ : 1], vreg[KVREG ? KSV : 1];
-  if constexpr (KVREG) {
-#pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks)
-      kreg[ks] = key_valid ? Elem<TIn>::load8(krow + ks * 16 + hh * 8) : zero8();
-#pragma unroll
-    for (int ks = 0; ks < KSV; ++ks)
-      vreg[ks] = key_valid ? Elem<TIn>::load8(vrow + ks * 16 + hh * 8) : zero8();
-  }
-
-  // K tile (this workgroup's column chunk) for the dQ product.
-#pragma unroll
-  for (int c = tid; c < BN * OCK / 8; c += 256) {
-    const int r = c / (OCK / 8), cc = (c % (OCK / 8)) * 8;
-    const int j = j0 + r;
-    const bf16x8 val = j < s.klen
-        ? Elem<TIn>::load8(K + kbase + (int64_t)j * a.k_stride[1] + ch * OCK + cc) : zero8();
-    *reinterpret_cast<bf16x8*>(&Ks[r * KP + cc]) = val;
-  }
+  // K tile (this workgroup's column chunk) for the dQ product; V tile.
+  TileStage<BN, OCK, TIn>::copy(K + kbase + ch * OCK, a.k_stride[1], j0, s.klen, Ks, KP, tid);
+  if constexpr (V_FROM_LDS)
+    TileStage<BN, DV, TIn>::copy(V + vbase, a.v_stride[1], j0, s.klen, Vs, VP, tid);
 
   f32x16 dkacc[NDK], dvacc[NDV];
 #pragma unroll
@@ -187,150 +184,198 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
 
   const int pr = perm32(lq);
   const int nqt = (s.qlen + BM - 1) / BM;
-  for (int hg = 0; hg < a.group; ++hg) {
+  const int total = a.group * nqt;
+  // Query tiles whose last position precedes this workgroup's first key see
+  // none of its keys and are skipped (causal tile skipping).
+  auto visible = [&](int u) -> bool {
+    if (!a.causal) return true;
+    const int i0 = (u % nqt) * BM;
+    int lo, hi;
+    qpos_range(a, s, i0, min(i0 + BM, s.qlen), lo, hi);
+    return hi >= gkpos_lo;
+  };
+  auto next_visible = [&](int u) -> int {
+    while (u < total && !visible(u)) ++u;
+    return u;
+  };
+
+  TileStage<PREFETCH ? BM : 32, PREFETCH ? DQK : 64, TIn> qst;
+  TileStage<PREFETCH ? BM : 32, PREFETCH ? DV : 64, TIn> dost;
+  float pre_l = 0.f, pre_d = 0.f;
+  int pre_p = 0;
+  // Fetch query tile u: into registers (prefetch) or straight into LDS.
+  auto fetch = [&](int u) {
+    const int h = kvh * a.group + u / nqt;
+    const int i0 = (u % nqt) * BM;
+    const int64_t qb = (a.thd ? s.q_row0 * a.q_stride[1] : (int64_t)z * a.q_stride[0]) +
+                       (int64_t)h * a.q_stride[2];
+    const int64_t dob = (a.thd ? s.q_row0 * a.do_stride[1] : (int64_t)z * a.do_stride[0]) +
+                        (int64_t)h * a.do_stride[2];
+    if constexpr (PREFETCH) {
+      qst.load(Q + qb, a.q_stride[1], i0, s.qlen, tid);
+      dost.load(dO + dob, a.do_stride[1], i0, s.qlen, tid);
+    } else {
+      TileStage<BM, DQK, TIn>::copy(Q + qb, a.q_stride[1], i0, s.qlen, Qs, QP, tid);
+      TileStage<BM, DV, TIn>::copy(dO + dob, a.do_stride[1], i0, s.qlen, dOs, OP, tid);
+    }
+    if (tid < BM) {
+      const int i = i0 + tid;
+      const bool ok = i < s.qlen;
+      const int64_t lb = (a.thd ? s.q_row0 : (int64_t)z * a.lse_stride[0]) +
+                         (int64_t)h * a.lse_stride[1];
+      const int64_t db = (a.thd ? s.q_row0 : (int64_t)z * a.delta_stride[0]) +
+                         (int64_t)h * a.delta_stride[1];
+      const float l = ok ? a.lse[lb + i] : -kInf;
+      // rows past the end or without any key: P must be exactly 0
+      pre_l = (l == -kInf) ? kInf : l * kLog2e;
+      pre_d = ok ? a.delta[db + i] : 0.f;
+      pre_p = qpos(a, s, i);
+    }
+  };
+
+  int u = next_visible(0);
+  if (PREFETCH && u < total) fetch(u);
+  while (u < total) {
+    const int hg = u / nqt;
     const int h = kvh * a.group + hg;
-    const int64_t qbase = (a.thd ? s.q_row0 * a.q_stride[1] : (int64_t)z * a.q_stride[0]) +
-                          (int64_t)h * a.q_stride[2];
-    const int64_t dobase = (a.thd ? s.q_row0 * a.do_stride[1] : (int64_t)z * a.do_stride[0]) +
-                           (int64_t)h * a.do_stride[2];
-    const int64_t lbase = (a.thd ? s.q_row0 : (int64_t)z * a.lse_stride[0]) +
-                          (int64_t)h * a.lse_stride[1];
-    const int64_t dlbase = (a.thd ? s.q_row0 : (int64_t)z * a.delta_stride[0]) +
-                           (int64_t)h * a.delta_stride[1];
-    float* accbase = a.dq_acc + (a.thd ? s.q_row0 * a.acc_stride[1] : (int64_t)z * a.acc_stride[0]) +
-                     (int64_t)h * a.acc_stride[2] + ch * OCK;
+    const int i0 = (u % nqt) * BM;
+    const int i1 = min(i0 + BM, s.qlen);
+    int tlo, thi;
+    qpos_range(a, s, i0, i1, tlo, thi);
+    __syncthreads();
+    if constexpr (PREFETCH) {
+      qst.store(Qs, QP, tid);
+      dost.store(dOs, OP, tid);
+    } else {
+      fetch(u);
+    }
+    if (tid < BM) {
+      Ls[tid] = pre_l;
+      Dl[tid] = pre_d;
+      Ps[tid] = pre_p;
+    }
+    const int un = next_visible(u + 1);
+    if (PREFETCH && un < total) fetch(un);
+    __syncthreads();
 
-    for (int qt = 0; qt < nqt; ++qt) {
-      const int i0 = qt * BM;
-      const int i1 = min(i0 + BM, s.qlen);
-      int64_t tlo, thi;
-      qpos_range(a, s, i0, i1, tlo, thi);
-      if (a.causal && thi < gkpos_lo) continue;   // no row here sees these keys
-      __syncthreads();
+    const bool wave_on = wave_has_keys && (!a.causal || thi >= wkpos_lo);
+    if (wave_on) {
+      f32x16 sacc[NQB], pacc[NQB];
 #pragma unroll
-      for (int c = tid; c < BM * DQK / 8; c += 256) {
-        const int r = c / (DQK / 8), cc = (c % (DQK / 8)) * 8;
-        const int i = i0 + r;
-        const bf16x8 val = i < s.qlen
-            ? Elem<TIn>::load8(Q + qbase + (int64_t)i * a.q_stride[1] + cc) : zero8();
-        *reinterpret_cast<bf16x8*>(&Qs[r * QP + cc]) = val;
-      }
+      for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-      for (int c = tid; c < BM * DV / 8; c += 256) {
-        const int r = c / (DV / 8), cc = (c % (DV / 8)) * 8;
-        const int i = i0 + r;
-        const bf16x8 val = i < s.qlen
-            ? Elem<TIn>::load8(dO + dobase + (int64_t)i * a.do_stride[1] + cc) : zero8();
-        *reinterpret_cast<bf16x8*>(&dOs[r * OP + cc]) = val;
-      }
-      if (tid < BM) {
-        const int i = i0 + tid;
-        const bool ok = i < s.qlen;
-        const float l = ok ? a.lse[lbase + i] : -kInf;
-        // rows past the end or without any key: P must be exactly 0
-        Ls[tid] = (l == -kInf) ? kInf : l * kLog2e;
-        Dl[tid] = ok ? a.delta[dlbase + i] : 0.f;
-        Ps[tid] = qpos(a, s, i);
-      }
-      __syncthreads();
-
-      const bool wave_on = wave_has_keys && (!a.causal || thi >= wkpos_lo);
-      if (wave_on) {
-        f32x16 sacc[NQB], pacc[NQB];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) { sacc[qb][v] = 0.f; pacc[qb][v] = 0.f; }
+        for (int v = 0; v < 16; ++v) { sacc[qb][v] = 0.f; pacc[qb][v] = 0.f; }
+      if constexpr (K_FROM_LDS) {
 #pragma unroll
         for (int ks = 0; ks < KSQ; ++ks) {
-          bf16x8 b;
-          if constexpr (KVREG) b = kreg[ks];
-          else b = key_valid ? Elem<TIn>::load8(krow + ks * 16 + hh * 8) : zero8();
+          const bf16x8 b = lds_row8(Ks, KP, wave * 32 + lq, ks * 16 + hh * 8);
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb)
             sacc[qb] = mfma32(lds_row8(Qs, QP, qb * 32 + pr, ks * 16 + hh * 8), b, sacc[qb]);
         }
+      } else {
+#pragma unroll 4
+        for (int ks = 0; ks < KSQ; ++ks) {
+          const bf16x8 b = key_valid ? Elem<TIn>::load8(krow + ks * 16 + hh * 8) : zero8();
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb)
+            sacc[qb] = mfma32(lds_row8(Qs, QP, qb * 32 + pr, ks * 16 + hh * 8), b, sacc[qb]);
+        }
+      }
+      if constexpr (V_FROM_LDS) {
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks) {
-          bf16x8 b;
-          if constexpr (KVREG) b = vreg[ks];
-          else b = key_valid ? Elem<TIn>::load8(vrow + ks * 16 + hh * 8) : zero8();
+          const bf16x8 b = lds_row8(Vs, VP, wave * 32 + lq, ks * 16 + hh * 8);
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb)
             pacc[qb] = mfma32(lds_row8(dOs, OP, qb * 32 + pr, ks * 16 + hh * 8), b, pacc[qb]);
         }
-        const bool need_mask = (jw + 32 > s.klen) || (a.causal && tlo < wkpos_hi);
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = qb * 32 + acc_row_perm(v, hh);
-            float p = fast_exp2(sacc[qb][v] * a.scale_log2 - Ls[r]);
-            if (need_mask) {
-              const bool vis = key_valid && (!a.causal || my_kpos <= Ps[r]);
-              p = vis ? p : 0.f;
-            }
-            sacc[qb][v] = p;
-            pacc[qb][v] = p * (pacc[qb][v] - Dl[r]);
-          }
-#pragma unroll
-        for (int t = 0; t < BM / 16; ++t) {
-          bf16x8 pb, sb;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            pb[e] = (bf16)sacc[t >> 1][8 * (t & 1) + e];
-            sb[e] = (bf16)pacc[t >> 1][8 * (t & 1) + e];
-          }
-          const int k0 = 16 * t + 8 * (grp >> 1);
-#pragma unroll
-          for (int db = 0; db < NDV; ++db)
-            dvacc[db] = mfma32(lds_tr8(dOs, OP, k0, ch * OCV + db * 32 + 16 * (grp & 1), gl), pb,
-                               dvacc[db]);
-#pragma unroll
-          for (int db = 0; db < NDK; ++db)
-            dkacc[db] = mfma32(lds_tr8(Qs, QP, k0, ch * OCK + db * 32 + 16 * (grp & 1), gl), sb,
-                               dkacc[db]);
-        }
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int hv = 0; hv < 2; ++hv) {
-            bf16x8 w;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] = (bf16)pacc[qb][8 * hv + e];
-            *reinterpret_cast<bf16x8*>(&dSt[(wave * 32 + lq) * SP + qb * 32 + 16 * hv + 8 * hh]) = w;
-          }
       } else {
+#pragma unroll 4
+        for (int ks = 0; ks < KSV; ++ks) {
+          const bf16x8 b = key_valid ? Elem<TIn>::load8(vrow + ks * 16 + hh * 8) : zero8();
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int hv = 0; hv < 2; ++hv)
-            *reinterpret_cast<bf16x8*>(&dSt[(wave * 32 + lq) * SP + qb * 32 + 16 * hv + 8 * hh]) =
-                zero8();
-      }
-      __syncthreads();
-
-      // dQ tile (BM x OCK) = dS (BM x 128 keys) K (128 keys x OCK), split
-      // into 32x32 blocks over the four waves.
-      for (int b = wave; b < NQB * NDK; b += 4) {
-        const int qb = b / NDK, db = b % NDK;
-        f32x16 acc;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-#pragma unroll
-        for (int t = 0; t < BN / 16; ++t) {
-          const int k0 = 16 * t + 8 * (grp >> 1);
-          acc = mfma32(lds_tr8(dSt, SP, k0, qb * 32 + 16 * (grp & 1), gl),
-                       lds_tr8(Ks, KP, k0, db * 32 + 16 * (grp & 1), gl), acc);
+          for (int qb = 0; qb < NQB; ++qb)
+            pacc[qb] = mfma32(lds_row8(dOs, OP, qb * 32 + pr, ks * 16 + hh * 8), b, pacc[qb]);
         }
+      }
+      const bool need_mask = (jw + 32 > s.klen) || (a.causal && tlo < wkpos_hi);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int i = i0 + qb * 32 + acc_row(v, hh);
-          if (i < s.qlen)
-            atomicAdd(accbase + (int64_t)i * a.acc_stride[1] + db * 32 + lq, acc[v]);
+          const int r = qb * 32 + acc_row_perm(v, hh);
+          float p = fast_exp2(sacc[qb][v] * a.scale_log2 - Ls[r]);
+          if (need_mask) {
+            const bool vis = key_valid && (!a.causal || my_kpos <= Ps[r]);
+            p = vis ? p : 0.f;
+          }
+          sacc[qb][v] = p;
+          pacc[qb][v] = p * (pacc[qb][v] - Dl[r]);
         }
+#pragma unroll
+      for (int t = 0; t < BM / 16; ++t) {
+        bf16x8 pb, sb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pb[e] = (bf16)sacc[t >> 1][8 * (t & 1) + e];
+          sb[e] = (bf16)pacc[t >> 1][8 * (t & 1) + e];
+        }
+        const int k0 = 16 * t + 8 * (grp >> 1);
+#pragma unroll
+        for (int db = 0; db < NDV; ++db)
+          dvacc[db] = mfma32(lds_tr8(dOs, OP, k0, ch * OCV + db * 32 + 16 * (grp & 1), gl), pb,
+                             dvacc[db]);
+#pragma unroll
+        for (int db = 0; db < NDK; ++db)
+          dkacc[db] = mfma32(lds_tr8(Qs, QP, k0, ch * OCK + db * 32 + 16 * (grp & 1), gl), sb,
+                             dkacc[db]);
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv) {
+          bf16x8 w;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[e] = (bf16)pacc[qb][8 * hv + e];
+          *reinterpret_cast<bf16x8*>(&dSt[(wave * 32 + lq) * SP + qb * 32 + 16 * hv + 8 * hh]) = w;
+        }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv)
+          *reinterpret_cast<bf16x8*>(&dSt[(wave * 32 + lq) * SP + qb * 32 + 16 * hv + 8 * hh]) =
+              zero8();
+    }
+    __syncthreads();
+
+    // dQ tile (BM x OCK) = dS (BM x 128 keys) K (128 keys x OCK), split into
+    // 32x32 blocks over the four waves, added to the fp32 accumulator.
+    float* accbase = a.dq_acc +
+                     (a.thd ? s.q_row0 * a.acc_stride[1] : (int64_t)z * a.acc_stride[0]) +
+                     (int64_t)h * a.acc_stride[2] + ch * OCK + lq;
+    const bool full_rows = i0 + BM <= s.qlen;
+    for (int b = wave; b < NQB * NDK; b += 4) {
+      const int qb = b / NDK, db = b % NDK;
+      f32x16 acc;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+      for (int t = 0; t < BN / 16; ++t) {
+        const int k0 = 16 * t + 8 * (grp >> 1);
+        acc = mfma32(lds_tr8(dSt, SP, k0, qb * 32 + 16 * (grp & 1), gl),
+                     lds_tr8(Ks, KP, k0, db * 32 + 16 * (grp & 1), gl), acc);
+      }
+      float* p0 = accbase + (int64_t)(i0 + qb * 32 + 4 * hh) * a.acc_stride[1] + db * 32;
+      const int64_t rs = a.acc_stride[1];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int dr = 8 * (v >> 2) + (v & 3);
+        if (full_rows || i0 + qb * 32 + 4 * hh + dr < s.qlen) atomicAdd(p0 + dr * rs, acc[v]);
       }
     }
+    u = un;
   }
 
   if (!key_valid) return;
@@ -384,7 +429,6 @@ struct BwdCfg {
   static constexpr int OCV = BIG ? DV / 2 : DV;
   static constexpr int NCH = DQK / OCK;
   static constexpr int BM = DQK + DV > 320 ? 32 : 64;
-  static constexpr bool KVREG = DQK + DV <= 320;
 };
 
 template <int DQK, int DV, typename TIn, typename TOut>
@@ -401,7 +445,7 @@ static hipError_t bwd_variant(const AttnArgs& a, int step, hipStream_t st) {
   }
   if (step == 1 && krows > 0) {
     dim3 g(a.heads_kv * C::NCH, (krows + 127) / 128, a.nseq);
-    hipLaunchKernelGGL((bwd_main_kernel<DQK, DV, C::OCK, C::OCV, C::BM, C::KVREG, TIn, TOut>), g,
+    hipLaunchKernelGGL((bwd_main_kernel<DQK, DV, C::OCK, C::OCV, C::BM, TIn, TOut>), g,
                        dim3(256), 0, st, a);
   }
   if (step == 2 && qrows > 0) {

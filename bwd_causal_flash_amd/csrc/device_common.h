@@ -44,6 +44,33 @@ __device__ __forceinline__ int acc_row(int v, int hh) {
   return 8 * (v >> 2) + 4 * hh + (v & 3);
 }
 
+// LDS row pitch (elements) for a bf16 tile whose rows hold d elements.
+// P/8 is odd, so 16-byte reads of 16 consecutive rows hit 16 distinct 16-byte
+// bank groups, and 4 consecutive rows start at least 32 bytes apart modulo
+// 256, so the 32-byte row windows of a transpose read never share a bank.
+constexpr bool pitch_ok(int p) {
+  if ((p / 8) % 2 == 0) return false;
+  for (int a = 0; a < 4; ++a)
+    for (int b = a + 1; b < 4; ++b) {
+      const int d = ((a - b) * 2 * p % 256 + 256) % 256;
+      if (d < 32 || d > 256 - 32) return false;
+    }
+  bool seen[16] = {};
+  for (int r = 0; r < 16; ++r) {
+    const int g = (r * 2 * p % 256) / 16;
+    if (seen[g]) return false;
+    seen[g] = true;
+  }
+  return true;
+}
+constexpr int lds_pitch(int d) {
+  int p = d + 8;
+  while (!pitch_ok(p)) p += 16;
+  return p;
+}
+static_assert(lds_pitch(128) == 152 && lds_pitch(192) == 200 && lds_pitch(64) == 72,
+              "pitch rule");
+
 // ------------------------------------------------------------------ loads
 
 template <typename T>
@@ -120,11 +147,12 @@ __device__ __forceinline__ float fast_exp2(float x) {
 // ---------------------------------------------------------- sequences
 
 // One sequence (BSHD batch entry or THD document) as the kernels see it.
+// Positions fit in int32 (the host checks |position| < 2^30).
 struct Seq {
   int64_t q_row0;   // physical row of local row 0 (THD), 0 for BSHD
   int64_t k_row0;
   int qlen, klen;   // real rows
-  int64_t qpos_thd; // THD: query position offset (bottom-right)
+  int qpos_thd;     // THD: query position offset (bottom-right)
 };
 
 // Resolve sequence z; malformed THD metadata makes the sequence empty.
@@ -148,15 +176,14 @@ __device__ __forceinline__ Seq load_seq(const AttnArgs& a, int z) {
   s.k_row0 = ok ? ck0 : 0;
   s.qlen = ok ? uq : 0;
   s.klen = ok ? uk : 0;
-  s.qpos_thd = a.bottom_right ? (int64_t)(s.klen - s.qlen) : 0;
+  s.qpos_thd = a.bottom_right ? s.klen - s.qlen : 0;
   return s;
 }
 
 // Position of local query row i.
-__device__ __forceinline__ int64_t qpos(const AttnArgs& a, const Seq& s,
-                                        int64_t i) {
+__device__ __forceinline__ int qpos(const AttnArgs& a, const Seq& s, int i) {
   if (a.thd) return i + s.qpos_thd;
-  int64_t p = a.seg_pos[0] + i;
+  int p = a.seg_pos[0] + i;
 #pragma unroll
   for (int t = 1; t < CPA_MAX_SEGMENTS; ++t)
     if (t < a.nseg && i >= a.seg_row[t]) p = a.seg_pos[t] + (i - a.seg_row[t]);
@@ -164,32 +191,74 @@ __device__ __forceinline__ int64_t qpos(const AttnArgs& a, const Seq& s,
 }
 
 // Min and max query position over local rows [r0, r1) (r1 > r0).
-__device__ __forceinline__ void qpos_range(const AttnArgs& a, const Seq& s,
-                                           int64_t r0, int64_t r1,
-                                           int64_t& lo, int64_t& hi) {
+__device__ __forceinline__ void qpos_range(const AttnArgs& a, const Seq& s, int r0, int r1,
+                                           int& lo, int& hi) {
   if (a.thd) {
     lo = r0 + s.qpos_thd;
     hi = r1 - 1 + s.qpos_thd;
     return;
   }
-  lo = INT64_MAX;
-  hi = INT64_MIN;
+  lo = INT32_MAX;
+  hi = INT32_MIN;
   for (int t = 0; t < a.nseg; ++t) {
-    const int64_t b0 = a.seg_row[t];
-    const int64_t b1 = (t + 1 < a.nseg) ? a.seg_row[t + 1] : INT64_MAX;
-    const int64_t x0 = r0 > b0 ? r0 : b0;
-    const int64_t x1 = r1 < b1 ? r1 : b1;
+    const int b0 = a.seg_row[t];
+    const int b1 = (t + 1 < a.nseg) ? a.seg_row[t + 1] : INT32_MAX;
+    const int x0 = r0 > b0 ? r0 : b0;
+    const int x1 = r1 < b1 ? r1 : b1;
     if (x0 < x1) {
-      const int64_t p0 = a.seg_pos[t] + (x0 - b0);
-      const int64_t p1 = a.seg_pos[t] + (x1 - 1 - b0);
+      const int p0 = a.seg_pos[t] + (x0 - b0);
+      const int p1 = a.seg_pos[t] + (x1 - 1 - b0);
       lo = p0 < lo ? p0 : lo;
       hi = p1 > hi ? p1 : hi;
     }
   }
 }
 
-__device__ __forceinline__ int64_t kpos0(const AttnArgs& a) {
-  return a.thd ? 0 : a.k_pos0;
-}
+__device__ __forceinline__ int kpos0(const AttnArgs& a) { return a.thd ? 0 : a.k_pos0; }
+
+// Cooperative staging of a [ROWS x D] bf16 tile through registers: thread
+// t owns rows (t/8) + 32*i and 16-byte column chunks (t%8) + 8*j, so eight
+// neighbouring threads read one row's 128 contiguous bytes and every offset
+// is a compile-time immediate.  load() fetches rows [r0, r0+ROWS) of the
+// source (zeros past `limit`), store() writes them to a padded LDS tile.
+template <int ROWS, int D, typename TIn>
+struct TileStage {
+  static constexpr int RI = ROWS / 32, CJ = D / 64;
+  static_assert(ROWS % 32 == 0 && D % 64 == 0, "tile shape");
+  bf16x8 v[RI][CJ];
+  __device__ __forceinline__ void load(const TIn* base, int64_t row_stride, int r0, int limit,
+                                       int tid) {
+    const int rg = tid >> 3, cp = (tid & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < RI; ++i) {
+      const int r = r0 + rg + 32 * i;
+      const TIn* p = base + (int64_t)r * row_stride + cp;
+#pragma unroll
+      for (int j = 0; j < CJ; ++j) v[i][j] = r < limit ? Elem<TIn>::load8(p + 64 * j) : zero8();
+    }
+  }
+  // Direct copy with few registers live (at most two chunks in flight).
+  static __device__ __forceinline__ void copy(const TIn* base, int64_t row_stride, int r0,
+                                              int limit, bf16* tile, int pitch, int tid) {
+    const int rg = tid >> 3, cp = (tid & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < RI; ++i) {
+      const int r = r0 + rg + 32 * i;
+      const TIn* p = base + (int64_t)r * row_stride + cp;
+      bf16* t = tile + (rg + 32 * i) * pitch + cp;
+#pragma unroll 2
+      for (int j = 0; j < CJ; ++j)
+        *reinterpret_cast<bf16x8*>(t + 64 * j) = r < limit ? Elem<TIn>::load8(p + 64 * j) : zero8();
+    }
+  }
+  __device__ __forceinline__ void store(bf16* tile, int pitch, int tid) const {
+    const int rg = tid >> 3, cp = (tid & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < RI; ++i)
+#pragma unroll
+      for (int j = 0; j < CJ; ++j)
+        *reinterpret_cast<bf16x8*>(tile + (rg + 32 * i) * pitch + cp + 64 * j) = v[i][j];
+  }
+};
 
 }  // namespace cpa

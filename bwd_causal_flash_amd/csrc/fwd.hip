@@ -27,7 +27,7 @@ namespace cpa {
 template <int DQK, int DVC, int NCH, typename TIn, typename TOut>
 __global__ __launch_bounds__(256) void fwd_kernel(const AttnArgs a) {
   constexpr int BM = 128, BN = 64;
-  constexpr int KP = DQK + 8, VP = DVC + 8;
+  constexpr int KP = lds_pitch(DQK), VP = lds_pitch(DVC);
   constexpr int KS = DQK / 16;
   constexpr int NDB = DVC / 32;
   __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KP];
@@ -49,25 +49,25 @@ __global__ __launch_bounds__(256) void fwd_kernel(const AttnArgs a) {
   const TIn* V = static_cast<const TIn*>(a.v);
   TOut* O = static_cast<TOut*>(a.out_o);
   const int64_t qbase = a.thd ? s.q_row0 * a.q_stride[1] : (int64_t)z * a.q_stride[0];
-  const int64_t kbase = (a.thd ? s.k_row0 * a.k_stride[1] : (int64_t)z * a.k_stride[0]) +
-                        (int64_t)kvh * a.k_stride[2];
-  const int64_t vbase = (a.thd ? s.k_row0 * a.v_stride[1] : (int64_t)z * a.v_stride[0]) +
-                        (int64_t)kvh * a.v_stride[2] + ch * DVC;
+  const TIn* Kb = K + (a.thd ? s.k_row0 * a.k_stride[1] : (int64_t)z * a.k_stride[0]) +
+                  (int64_t)kvh * a.k_stride[2];
+  const TIn* Vb = V + (a.thd ? s.k_row0 * a.v_stride[1] : (int64_t)z * a.v_stride[0]) +
+                  (int64_t)kvh * a.v_stride[2] + ch * DVC;
   const int64_t obase = a.thd ? s.q_row0 * a.o_stride[1] : (int64_t)z * a.o_stride[0];
 
   const int qi = i0 + wave * 32 + lq;
   const bool qvalid = qi < s.qlen;
-  const int64_t my_pos = qpos(a, s, qi);
+  const int my_pos = qpos(a, s, qi);
   const int wr0 = i0 + wave * 32;
   const bool wave_active = wr0 < s.qlen;
-  int64_t wlo = 0, whi = -1;
+  int wlo = 0, whi = -1;
   if (wave_active) qpos_range(a, s, wr0, min(wr0 + 32, s.qlen), wlo, whi);
-  int64_t glo, ghi;
+  int glo, ghi;
   qpos_range(a, s, i0, min(i0 + BM, s.qlen), glo, ghi);
-  const int64_t kp0 = kpos0(a);
+  const int kp0 = kpos0(a);
   int kend = s.klen;
   if (a.causal) {
-    const int64_t lim = ghi - kp0 + 1;
+    const int64_t lim = (int64_t)ghi - kp0 + 1;
     kend = (int)(lim < 0 ? 0 : (lim < kend ? lim : kend));
   }
   const int ntiles = (kend + BN - 1) / BN;
@@ -89,24 +89,23 @@ __global__ __launch_bounds__(256) void fwd_kernel(const AttnArgs a) {
   float m_run = -kInf, l_run = 0.f;
   const int kr = perm32(lq);
 
+  // K/V tiles go global -> registers -> LDS; tile t+1 is fetched while
+  // tile t is being computed.
+  TileStage<BN, DQK, TIn> kst;
+  TileStage<BN, DVC, TIn> vst;
+  if (ntiles > 0) {
+    kst.load(Kb, a.k_stride[1], 0, s.klen, tid);
+    vst.load(Vb, a.v_stride[1], 0, s.klen, tid);
+  }
+
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t * BN;
     __syncthreads();
-#pragma unroll
-    for (int c = tid; c < BN * DQK / 8; c += 256) {
-      const int r = c / (DQK / 8), cc = (c % (DQK / 8)) * 8;
-      const int j = j0 + r;
-      const bf16x8 val = j < s.klen
-          ? Elem<TIn>::load8(K + kbase + (int64_t)j * a.k_stride[1] + cc) : zero8();
-      *reinterpret_cast<bf16x8*>(&Ks[r * KP + cc]) = val;
-    }
-#pragma unroll
-    for (int c = tid; c < BN * DVC / 8; c += 256) {
-      const int r = c / (DVC / 8), cc = (c % (DVC / 8)) * 8;
-      const int j = j0 + r;
-      const bf16x8 val = j < s.klen
-          ? Elem<TIn>::load8(V + vbase + (int64_t)j * a.v_stride[1] + cc) : zero8();
-      *reinterpret_cast<bf16x8*>(&Vs[r * VP + cc]) = val;
+    kst.store(Ks, KP, tid);
+    vst.store(Vs, VP, tid);
+    if (t + 1 < ntiles) {
+      kst.load(Kb, a.k_stride[1], j0 + BN, s.klen, tid);
+      vst.load(Vb, a.v_stride[1], j0 + BN, s.klen, tid);
     }
     __syncthreads();
     if (!wave_active || (a.causal && kp0 + j0 > whi)) continue;
@@ -125,19 +124,25 @@ __global__ __launch_bounds__(256) void fwd_kernel(const AttnArgs a) {
     const bool need_mask = (j0 + BN > s.klen) || (a.causal && kp0 + j0 + BN - 1 > wlo);
     float x[2][16];
     float mx = -kInf;
+    if (need_mask) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float val = sacc[kb][v] * a.scale_log2;
-        if (need_mask) {
+        for (int v = 0; v < 16; ++v) {
           const int j = j0 + kb * 32 + acc_row_perm(v, hh);
           const bool vis = j < s.klen && (!a.causal || kp0 + j <= my_pos);
-          val = vis ? val : -kInf;
+          x[kb][v] = vis ? sacc[kb][v] * a.scale_log2 : -kInf;
+          mx = fmaxf(mx, x[kb][v]);
         }
-        x[kb][v] = val;
-        mx = fmaxf(mx, val);
-      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          x[kb][v] = sacc[kb][v] * a.scale_log2;
+          mx = fmaxf(mx, x[kb][v]);
+        }
+    }
     mx = max_halves(mx);
     const float m_new = fmaxf(m_run, mx);
     const float base = (m_new == -kInf) ? 0.f : m_new;

@@ -46,9 +46,9 @@ struct AttnArgs {
   int causal;
   int bottom_right;
   int nseg;
-  int64_t seg_row[CPA_MAX_SEGMENTS];
-  int64_t seg_pos[CPA_MAX_SEGMENTS];
-  int64_t k_pos0;
+  int seg_row[CPA_MAX_SEGMENTS];   // positions and rows fit in int32
+  int seg_pos[CPA_MAX_SEGMENTS];
+  int k_pos0;
 };
 
 struct MergeArgs {
