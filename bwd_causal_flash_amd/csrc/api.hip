@@ -76,6 +76,7 @@ cpa_status check_problem(const cpa_problem* p) {
       p->seqlen_k >= (1ll << 31))
     return CPA_ERR_SHAPE;
   if (!isfinite(p->softmax_scale)) return CPA_ERR_SHAPE;
+  if (!(p->softmax_scale > 0.f)) return CPA_ERR_UNSUPPORTED;
   if (p->layout == CPA_LAYOUT_BSHD) {
     if (p->batch < 0 || p->batch > 65535) return CPA_ERR_SHAPE;
     if (p->num_q_segments < 0 || p->num_q_segments > CPA_MAX_SEGMENTS) return CPA_ERR_SHAPE;

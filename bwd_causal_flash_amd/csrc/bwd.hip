@@ -194,9 +194,13 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
     qpos_range(a, s, i0, min(i0 + BM, s.qlen), lo, hi);
     return hi >= gkpos_lo;
   };
-  auto next_visible = [&](int u) -> int {
-    while (u < total && !visible(u)) ++u;
-    return u;
+  // Workgroups of one head that run at the same time walk the query tiles
+  // from different starting points, so their dQ atomics hit different rows.
+  const int rot = (int)(((int64_t)kt * 37) % (total > 0 ? total : 1));
+  auto tile_of = [&](int k) -> int { return k + rot < total ? k + rot : k + rot - total; };
+  auto next_visible = [&](int k) -> int {
+    while (k < total && !visible(tile_of(k))) ++k;
+    return k;
   };
 
   TileStage<PREFETCH ? BM : 32, PREFETCH ? DQK : 64, TIn> qst;
@@ -233,9 +237,10 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
     }
   };
 
-  int u = next_visible(0);
-  if (PREFETCH && u < total) fetch(u);
-  while (u < total) {
+  int k = next_visible(0);
+  if (PREFETCH && k < total) fetch(tile_of(k));
+  while (k < total) {
+    const int u = tile_of(k);
     const int hg = u / nqt;
     const int h = kvh * a.group + hg;
     const int i0 = (u % nqt) * BM;
@@ -254,92 +259,89 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
       Dl[tid] = pre_d;
       Ps[tid] = pre_p;
     }
-    const int un = next_visible(u + 1);
-    if (PREFETCH && un < total) fetch(un);
+    const int kn = next_visible(k + 1);
+    if (PREFETCH && kn < total) fetch(tile_of(kn));
     __syncthreads();
 
     const bool wave_on = wave_has_keys && (!a.causal || thi >= wkpos_lo);
     if (wave_on) {
-      f32x16 sacc[NQB], pacc[NQB];
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) { sacc[qb][v] = 0.f; pacc[qb][v] = 0.f; }
-      if constexpr (K_FROM_LDS) {
-#pragma unroll
-        for (int ks = 0; ks < KSQ; ++ks) {
-          const bf16x8 b = lds_row8(Ks, KP, wave * 32 + lq, ks * 16 + hh * 8);
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb)
-            sacc[qb] = mfma32(lds_row8(Qs, QP, qb * 32 + pr, ks * 16 + hh * 8), b, sacc[qb]);
-        }
-      } else {
-#pragma unroll 4
-        for (int ks = 0; ks < KSQ; ++ks) {
-          const bf16x8 b = key_valid ? Elem<TIn>::load8(krow + ks * 16 + hh * 8) : zero8();
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb)
-            sacc[qb] = mfma32(lds_row8(Qs, QP, qb * 32 + pr, ks * 16 + hh * 8), b, sacc[qb]);
-        }
-      }
-      if constexpr (V_FROM_LDS) {
-#pragma unroll
-        for (int ks = 0; ks < KSV; ++ks) {
-          const bf16x8 b = lds_row8(Vs, VP, wave * 32 + lq, ks * 16 + hh * 8);
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb)
-            pacc[qb] = mfma32(lds_row8(dOs, OP, qb * 32 + pr, ks * 16 + hh * 8), b, pacc[qb]);
-        }
-      } else {
-#pragma unroll 4
-        for (int ks = 0; ks < KSV; ++ks) {
-          const bf16x8 b = key_valid ? Elem<TIn>::load8(vrow + ks * 16 + hh * 8) : zero8();
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb)
-            pacc[qb] = mfma32(lds_row8(dOs, OP, qb * 32 + pr, ks * 16 + hh * 8), b, pacc[qb]);
-        }
-      }
       const bool need_mask = (jw + 32 > s.klen) || (a.causal && tlo < wkpos_hi);
+      // One 32-row query block at a time keeps a single block's S and dP
+      // live; the unrolled loop lets block qb+1's products overlap block
+      // qb's exponentials.
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
+      for (int qb = 0; qb < NQB; ++qb) {
+        f32x16 sacc, pacc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
+        if constexpr (K_FROM_LDS) {
+#pragma unroll
+          for (int ks = 0; ks < KSQ; ++ks)
+            sacc = mfma32(lds_row8(Qs, QP, qb * 32 + pr, ks * 16 + hh * 8),
+                          lds_row8(Ks, KP, wave * 32 + lq, ks * 16 + hh * 8), sacc);
+        } else {
+#pragma unroll 4
+          for (int ks = 0; ks < KSQ; ++ks) {
+            const bf16x8 b = key_valid ? Elem<TIn>::load8(krow + ks * 16 + hh * 8) : zero8();
+            sacc = mfma32(lds_row8(Qs, QP, qb * 32 + pr, ks * 16 + hh * 8), b, sacc);
+          }
+        }
+        if constexpr (V_FROM_LDS) {
+#pragma unroll
+          for (int ks = 0; ks < KSV; ++ks)
+            pacc = mfma32(lds_row8(dOs, OP, qb * 32 + pr, ks * 16 + hh * 8),
+                          lds_row8(Vs, VP, wave * 32 + lq, ks * 16 + hh * 8), pacc);
+        } else {
+#pragma unroll 4
+          for (int ks = 0; ks < KSV; ++ks) {
+            const bf16x8 b = key_valid ? Elem<TIn>::load8(vrow + ks * 16 + hh * 8) : zero8();
+            pacc = mfma32(lds_row8(dOs, OP, qb * 32 + pr, ks * 16 + hh * 8), b, pacc);
+          }
+        }
+        // This lane's 16 rows are two runs of 8: qb*32 + 16*vh + 8*hh + e.
+        float lrow[16], drow[16];
+#pragma unroll
+        for (int vh = 0; vh < 2; ++vh) {
+          const int r0 = qb * 32 + 16 * vh + 8 * hh;
+          const float4 l0 = *reinterpret_cast<const float4*>(&Ls[r0]);
+          const float4 l1 = *reinterpret_cast<const float4*>(&Ls[r0 + 4]);
+          const float4 d0 = *reinterpret_cast<const float4*>(&Dl[r0]);
+          const float4 d1 = *reinterpret_cast<const float4*>(&Dl[r0 + 4]);
+          lrow[8 * vh + 0] = l0.x; lrow[8 * vh + 1] = l0.y; lrow[8 * vh + 2] = l0.z; lrow[8 * vh + 3] = l0.w;
+          lrow[8 * vh + 4] = l1.x; lrow[8 * vh + 5] = l1.y; lrow[8 * vh + 6] = l1.z; lrow[8 * vh + 7] = l1.w;
+          drow[8 * vh + 0] = d0.x; drow[8 * vh + 1] = d0.y; drow[8 * vh + 2] = d0.z; drow[8 * vh + 3] = d0.w;
+          drow[8 * vh + 4] = d1.x; drow[8 * vh + 5] = d1.y; drow[8 * vh + 6] = d1.z; drow[8 * vh + 7] = d1.w;
+        }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int r = qb * 32 + acc_row_perm(v, hh);
-          float p = fast_exp2(sacc[qb][v] * a.scale_log2 - Ls[r]);
+          float p = fast_exp2(__builtin_fmaf(sacc[v], a.scale_log2, -lrow[v]));
           if (need_mask) {
-            const bool vis = key_valid && (!a.causal || my_kpos <= Ps[r]);
+            const bool vis = key_valid && (!a.causal || my_kpos <= Ps[qb * 32 + acc_row_perm(v, hh)]);
             p = vis ? p : 0.f;
           }
-          sacc[qb][v] = p;
-          pacc[qb][v] = p * (pacc[qb][v] - Dl[r]);
+          sacc[v] = p;
+          pacc[v] = p * (pacc[v] - drow[v]);
         }
 #pragma unroll
-      for (int t = 0; t < BM / 16; ++t) {
-        bf16x8 pb, sb;
+        for (int tt = 0; tt < 2; ++tt) {
+          bf16x8 pb, sb;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb[e] = (bf16)sacc[t >> 1][8 * (t & 1) + e];
-          sb[e] = (bf16)pacc[t >> 1][8 * (t & 1) + e];
+          for (int e = 0; e < 8; ++e) {
+            pb[e] = (bf16)sacc[8 * tt + e];
+            sb[e] = (bf16)pacc[8 * tt + e];
+          }
+          const int k0 = 32 * qb + 16 * tt + 8 * (grp >> 1);
+#pragma unroll
+          for (int db = 0; db < NDV; ++db)
+            dvacc[db] = mfma32(lds_tr8(dOs, OP, k0, ch * OCV + db * 32 + 16 * (grp & 1), gl), pb,
+                               dvacc[db]);
+#pragma unroll
+          for (int db = 0; db < NDK; ++db)
+            dkacc[db] = mfma32(lds_tr8(Qs, QP, k0, ch * OCK + db * 32 + 16 * (grp & 1), gl), sb,
+                               dkacc[db]);
+          *reinterpret_cast<bf16x8*>(&dSt[(wave * 32 + lq) * SP + qb * 32 + 16 * tt + 8 * hh]) = sb;
         }
-        const int k0 = 16 * t + 8 * (grp >> 1);
-#pragma unroll
-        for (int db = 0; db < NDV; ++db)
-          dvacc[db] = mfma32(lds_tr8(dOs, OP, k0, ch * OCV + db * 32 + 16 * (grp & 1), gl), pb,
-                             dvacc[db]);
-#pragma unroll
-        for (int db = 0; db < NDK; ++db)
-          dkacc[db] = mfma32(lds_tr8(Qs, QP, k0, ch * OCK + db * 32 + 16 * (grp & 1), gl), sb,
-                             dkacc[db]);
       }
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int hv = 0; hv < 2; ++hv) {
-          bf16x8 w;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) w[e] = (bf16)pacc[qb][8 * hv + e];
-          *reinterpret_cast<bf16x8*>(&dSt[(wave * 32 + lq) * SP + qb * 32 + 16 * hv + 8 * hh]) = w;
-        }
     } else {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
@@ -369,13 +371,18 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
       }
       float* p0 = accbase + (int64_t)(i0 + qb * 32 + 4 * hh) * a.acc_stride[1] + db * 32;
       const int64_t rs = a.acc_stride[1];
+      if (full_rows) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int dr = 8 * (v >> 2) + (v & 3);
-        if (full_rows || i0 + qb * 32 + 4 * hh + dr < s.qlen) atomicAdd(p0 + dr * rs, acc[v]);
+        for (int v = 0; v < 16; ++v) atomicAdd(p0 + (8 * (v >> 2) + (v & 3)) * rs, acc[v]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int dr = 8 * (v >> 2) + (v & 3);
+          if (i0 + qb * 32 + 4 * hh + dr < s.qlen) atomicAdd(p0 + dr * rs, acc[v]);
+        }
       }
     }
-    u = un;
+    k = kn;
   }
 
   if (!key_valid) return;

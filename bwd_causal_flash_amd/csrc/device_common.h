@@ -229,6 +229,15 @@ struct TileStage {
   __device__ __forceinline__ void load(const TIn* base, int64_t row_stride, int r0, int limit,
                                        int tid) {
     const int rg = tid >> 3, cp = (tid & 7) * 8;
+    if (r0 + ROWS <= limit) {   // whole tile in range: no per-row predicate
+#pragma unroll
+      for (int i = 0; i < RI; ++i) {
+        const TIn* p = base + (int64_t)(r0 + rg + 32 * i) * row_stride + cp;
+#pragma unroll
+        for (int j = 0; j < CJ; ++j) v[i][j] = Elem<TIn>::load8(p + 64 * j);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
       const int r = r0 + rg + 32 * i;

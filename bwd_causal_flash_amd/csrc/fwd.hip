@@ -122,8 +122,6 @@ __global__ __launch_bounds__(256) void fwd_kernel(const AttnArgs a) {
         sacc[kb] = mfma32(lds_row8(Ks, KP, kb * 32 + kr, ks * 16 + hh * 8), qreg[ks], sacc[kb]);
 
     const bool need_mask = (j0 + BN > s.klen) || (a.causal && kp0 + j0 + BN - 1 > wlo);
-    float x[2][16];
-    float mx = -kInf;
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -131,37 +129,41 @@ __global__ __launch_bounds__(256) void fwd_kernel(const AttnArgs a) {
         for (int v = 0; v < 16; ++v) {
           const int j = j0 + kb * 32 + acc_row_perm(v, hh);
           const bool vis = j < s.klen && (!a.causal || kp0 + j <= my_pos);
-          x[kb][v] = vis ? sacc[kb][v] * a.scale_log2 : -kInf;
-          mx = fmaxf(mx, x[kb][v]);
-        }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          x[kb][v] = sacc[kb][v] * a.scale_log2;
-          mx = fmaxf(mx, x[kb][v]);
+          sacc[kb][v] = vis ? sacc[kb][v] : -kInf;
         }
     }
-    mx = max_halves(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float base = (m_new == -kInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - base);
+    // Row max of the raw scores (the scale is positive), in log2 units.
+    float mx = -kInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
+    mx = max_halves(mx) * a.scale_log2;
+    // Lazy rescaling: the exponent base only moves when the row max grows by
+    // more than 2^8 (or on the first visible tile), so most tiles skip the
+    // rescale of O; P stays <= 2^8, exact in fp32 and safe in bf16.
+    const bool move = mx > m_run + 8.f;
+    if (__builtin_amdgcn_read_exec() & __ballot(move)) {
+      const float alpha = move ? fast_exp2(m_run - mx) : 1.f;   // m_run = -inf -> 0
+      if (move) m_run = mx;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+    }
+    const float base = m_run == -kInf ? 0.f : m_run;
+    float x[2][16];
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        x[kb][v] = fast_exp2(x[kb][v] - base);
+        x[kb][v] = fast_exp2(__builtin_fmaf(sacc[kb][v], a.scale_log2, -base));
         rs += x[kb][v];
       }
     rs = sum_halves(rs);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+    l_run += rs;
 
 #pragma unroll
     for (int st = 0; st < BN / 16; ++st) {

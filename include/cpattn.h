@@ -122,7 +122,7 @@ typedef struct cpa_problem {
   int64_t dq_stride[3], dk_stride[3], dv_stride[3];
   int64_t lse_stride[2];   /* [batch, head]; rows are contiguous */
 
-  float softmax_scale;     /* s; usually 1/sqrt(d_qk) */
+  float softmax_scale;     /* s > 0 (else declined); usually 1/sqrt(d_qk) */
   int32_t causal;          /* 0: every real key visible */
   int32_t thd_bottom_right;/* THD: pos_q(i) = i + seqused_k - seqused_q */
 

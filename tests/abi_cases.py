@@ -75,6 +75,8 @@ def main():
     case("too_many_segments", "CPA_ERR_SHAPE", fwd(p))
     p = good_problem(); p.softmax_scale = float("nan")
     case("nan_scale", "CPA_ERR_SHAPE", fwd(p))
+    p = good_problem(); p.softmax_scale = -0.1
+    case("negative_scale_declined", "CPA_ERR_UNSUPPORTED", fwd(p))
     p = good_problem(); p.layout = 1; p.num_seqs = 2
     case("thd_missing_metadata", "CPA_ERR_NULL", fwd(p))
     p = good_problem(); p.seqlen_q = 1 << 31
