@@ -427,6 +427,292 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
     }
 }
 
+// ------------------------------------------------------- paired waves
+//
+// Small head dims (D_qk + D_v <= 320): eight waves per workgroup, two per
+// SIMD, so one wave's exponentials overlap the other's matrix products.
+// Each 32-key group of the 128-key tile has a wave pair: role A computes
+// S = Q K^T, dP = dO V^T, P and dS and accumulates dK^T += Q^T dS; role B
+// recomputes S and P (the same arithmetic, so the same P) and accumulates
+// dV^T += dO^T P.  Both roles keep their accumulators in one register array,
+// so each wave holds only D_qk/2 of them.  The dQ tile is split over all
+// eight waves (blocks kg, kg+8 for B; kg+4 for A), which keeps the work per
+// SIMD even: A 72 and B 56 products per 64-row query tile at D 192/128.
+template <int DQK, int DV, typename TIn, typename TOut>
+__global__ __launch_bounds__(512, 1) void bwd_pair_kernel(const AttnArgs a) {
+  constexpr int BN = 128, BM = 64, NT = 512;
+  constexpr int QP = lds_pitch(DQK), OP = lds_pitch(DV), SP = lds_pitch(BM);
+  constexpr int KP = lds_pitch(DQK), VP = lds_pitch(DV);
+  constexpr int KSQ = DQK / 16, KSV = DV / 16;
+  constexpr int NDK = DQK / 32, NDV = DV / 32;
+  constexpr int NACC = NDK > NDV ? NDK : NDV;
+  constexpr int NBLK = (BM / 32) * NDK;
+  __shared__ __attribute__((aligned(16))) bf16 Qs[BM * QP];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[BM * OP];
+  __shared__ __attribute__((aligned(16))) bf16 dSt[BN * SP];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[BN * VP];
+  __shared__ __attribute__((aligned(16))) float Ls[BM];
+  __shared__ __attribute__((aligned(16))) float Dl[BM];
+  __shared__ __attribute__((aligned(16))) int Ps[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
+  const int kg = wave & 3;
+  const bool role_dv = wave >= 4;
+  const int kvh = blockIdx.x % a.heads_kv;
+  const int kt = blockIdx.y;
+  const int z = blockIdx.z;
+  const Seq s = load_seq(a, z);
+  const int j0 = kt * BN;
+  if (j0 >= s.klen) return;
+  const int kp0 = kpos0(a);
+
+  const int jw = j0 + kg * 32;
+  const int my_key = jw + lq;
+  const bool key_valid = my_key < s.klen;
+  const int my_kpos = kp0 + my_key;
+  const bool wave_has_keys = jw < s.klen;
+  const int wk_last = min(jw + 31, s.klen - 1);
+  const int wkpos_lo = kp0 + jw, wkpos_hi = kp0 + wk_last;
+  const int gkpos_lo = kp0 + j0;
+
+  const TIn* Q = static_cast<const TIn*>(a.q);
+  const TIn* K = static_cast<const TIn*>(a.k);
+  const TIn* V = static_cast<const TIn*>(a.v);
+  const TIn* dO = static_cast<const TIn*>(a.dout);
+  const int64_t kbase = (a.thd ? s.k_row0 * a.k_stride[1] : (int64_t)z * a.k_stride[0]) +
+                        (int64_t)kvh * a.k_stride[2];
+  const int64_t vbase = (a.thd ? s.k_row0 * a.v_stride[1] : (int64_t)z * a.v_stride[0]) +
+                        (int64_t)kvh * a.v_stride[2];
+  TileStage<BN, DQK, TIn, NT>::copy(K + kbase, a.k_stride[1], j0, s.klen, Ks, KP, tid);
+  TileStage<BN, DV, TIn, NT>::copy(V + vbase, a.v_stride[1], j0, s.klen, Vs, VP, tid);
+
+  f32x16 acc[NACC];
+#pragma unroll
+  for (int d = 0; d < NACC; ++d)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[d][v] = 0.f;
+
+  const int pr = perm32(lq);
+  const int nqt = (s.qlen + BM - 1) / BM;
+  const int total = a.group * nqt;
+  auto visible = [&](int u) -> bool {
+    if (!a.causal) return true;
+    const int i0 = (u % nqt) * BM;
+    int lo, hi;
+    qpos_range(a, s, i0, min(i0 + BM, s.qlen), lo, hi);
+    return hi >= gkpos_lo;
+  };
+  const int rot = (int)(((int64_t)kt * 37) % (total > 0 ? total : 1));
+  auto tile_of = [&](int k) -> int { return k + rot < total ? k + rot : k + rot - total; };
+  auto next_visible = [&](int k) -> int {
+    while (k < total && !visible(tile_of(k))) ++k;
+    return k;
+  };
+
+  TileStage<BM, DQK, TIn, NT> qst;
+  TileStage<BM, DV, TIn, NT> dost;
+  float pre_l = 0.f, pre_d = 0.f;
+  int pre_p = 0;
+  auto fetch = [&](int u) {
+    const int h = kvh * a.group + u / nqt;
+    const int i0 = (u % nqt) * BM;
+    const int64_t qb = (a.thd ? s.q_row0 * a.q_stride[1] : (int64_t)z * a.q_stride[0]) +
+                       (int64_t)h * a.q_stride[2];
+    const int64_t dob = (a.thd ? s.q_row0 * a.do_stride[1] : (int64_t)z * a.do_stride[0]) +
+                        (int64_t)h * a.do_stride[2];
+    qst.load(Q + qb, a.q_stride[1], i0, s.qlen, tid);
+    dost.load(dO + dob, a.do_stride[1], i0, s.qlen, tid);
+    if (tid < BM) {
+      const int i = i0 + tid;
+      const bool ok = i < s.qlen;
+      const int64_t lb = (a.thd ? s.q_row0 : (int64_t)z * a.lse_stride[0]) +
+                         (int64_t)h * a.lse_stride[1];
+      const int64_t db = (a.thd ? s.q_row0 : (int64_t)z * a.delta_stride[0]) +
+                         (int64_t)h * a.delta_stride[1];
+      const float l = ok ? a.lse[lb + i] : -kInf;
+      pre_l = (l == -kInf) ? kInf : l * kLog2e;   // P = 0 on empty/keyless rows
+      pre_d = ok ? a.delta[db + i] : 0.f;
+      pre_p = qpos(a, s, i);
+    }
+  };
+
+  int k = next_visible(0);
+  if (k < total) fetch(tile_of(k));
+  while (k < total) {
+    const int u = tile_of(k);
+    const int h = kvh * a.group + u / nqt;
+    const int i0 = (u % nqt) * BM;
+    const int i1 = min(i0 + BM, s.qlen);
+    int tlo, thi;
+    qpos_range(a, s, i0, i1, tlo, thi);
+    __syncthreads();
+    qst.store(Qs, QP, tid);
+    dost.store(dOs, OP, tid);
+    if (tid < BM) {
+      Ls[tid] = pre_l;
+      Dl[tid] = pre_d;
+      Ps[tid] = pre_p;
+    }
+    const int kn = next_visible(k + 1);
+    if (kn < total) fetch(tile_of(kn));
+    __syncthreads();
+
+    const bool wave_on = wave_has_keys && (!a.causal || thi >= wkpos_lo);
+    const bool need_mask = (jw + 32 > s.klen) || (a.causal && tlo < wkpos_hi);
+    if (wave_on) {
+#pragma unroll
+      for (int qb = 0; qb < BM / 32; ++qb) {
+        f32x16 sacc, pacc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
+#pragma unroll
+        for (int ks = 0; ks < KSQ; ++ks)
+          sacc = mfma32(lds_row8(Qs, QP, qb * 32 + pr, ks * 16 + hh * 8),
+                        lds_row8(Ks, KP, kg * 32 + lq, ks * 16 + hh * 8), sacc);
+        if (!role_dv) {
+#pragma unroll
+          for (int ks = 0; ks < KSV; ++ks)
+            pacc = mfma32(lds_row8(dOs, OP, qb * 32 + pr, ks * 16 + hh * 8),
+                          lds_row8(Vs, VP, kg * 32 + lq, ks * 16 + hh * 8), pacc);
+        }
+        // This lane's 16 rows are two runs of 8: qb*32 + 16*vh + 8*hh + e.
+#pragma unroll
+        for (int vh = 0; vh < 2; ++vh) {
+          const int r0 = qb * 32 + 16 * vh + 8 * hh;
+          const float4 l0 = *reinterpret_cast<const float4*>(&Ls[r0]);
+          const float4 l1 = *reinterpret_cast<const float4*>(&Ls[r0 + 4]);
+          const float lr[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int v = 8 * vh + e;
+            float p = fast_exp2(__builtin_fmaf(sacc[v], a.scale_log2, -lr[e]));
+            if (need_mask) {
+              const bool vis = key_valid && (!a.causal || my_kpos <= Ps[r0 + e]);
+              p = vis ? p : 0.f;
+            }
+            sacc[v] = p;
+          }
+          if (!role_dv) {
+            const float4 d0 = *reinterpret_cast<const float4*>(&Dl[r0]);
+            const float4 d1 = *reinterpret_cast<const float4*>(&Dl[r0 + 4]);
+            const float dr[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int v = 8 * vh + e;
+              pacc[v] = sacc[v] * (pacc[v] - dr[e]);
+            }
+          }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int k0 = 32 * qb + 16 * tt + 8 * (grp >> 1);
+          bf16x8 w;
+          if (!role_dv) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = (bf16)pacc[8 * tt + e];
+#pragma unroll
+            for (int db = 0; db < NDK; ++db)
+              acc[db] = mfma32(lds_tr8(Qs, QP, k0, db * 32 + 16 * (grp & 1), gl), w, acc[db]);
+            *reinterpret_cast<bf16x8*>(&dSt[(kg * 32 + lq) * SP + qb * 32 + 16 * tt + 8 * hh]) = w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = (bf16)sacc[8 * tt + e];
+#pragma unroll
+            for (int db = 0; db < NDV; ++db)
+              acc[db] = mfma32(lds_tr8(dOs, OP, k0, db * 32 + 16 * (grp & 1), gl), w, acc[db]);
+          }
+        }
+      }
+    } else if (!role_dv) {
+#pragma unroll
+      for (int qb = 0; qb < BM / 32; ++qb)
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv)
+          *reinterpret_cast<bf16x8*>(&dSt[(kg * 32 + lq) * SP + qb * 32 + 16 * hv + 8 * hh]) =
+              zero8();
+    }
+    __syncthreads();
+
+    // dQ tile (BM x DQK) = dS (BM x 128 keys) K (128 keys x DQK): 32x32
+    // blocks kg, kg+8 for role B and kg+4 for role A.
+    float* accbase = a.dq_acc +
+                     (a.thd ? s.q_row0 * a.acc_stride[1] : (int64_t)z * a.acc_stride[0]) +
+                     (int64_t)h * a.acc_stride[2] + lq;
+    const bool full_rows = i0 + BM <= s.qlen;
+    const int64_t rs = a.acc_stride[1];
+    for (int b = (role_dv ? kg : kg + 4); b < NBLK; b += 8) {
+      const int qb = b / NDK, db = b % NDK;
+      f32x16 dq;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) dq[v] = 0.f;
+#pragma unroll
+      for (int t = 0; t < BN / 16; ++t) {
+        const int k0 = 16 * t + 8 * (grp >> 1);
+        dq = mfma32(lds_tr8(dSt, SP, k0, qb * 32 + 16 * (grp & 1), gl),
+                    lds_tr8(Ks, KP, k0, db * 32 + 16 * (grp & 1), gl), dq);
+      }
+      float* p0 = accbase + (int64_t)(i0 + qb * 32 + 4 * hh) * rs + db * 32;
+      if (full_rows) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) atomicAdd(p0 + (8 * (v >> 2) + (v & 3)) * rs, dq[v]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int dr = 8 * (v >> 2) + (v & 3);
+          if (i0 + qb * 32 + 4 * hh + dr < s.qlen) atomicAdd(p0 + dr * rs, dq[v]);
+        }
+      }
+    }
+    k = kn;
+  }
+
+  if (!key_valid) return;
+  if (!role_dv) {
+    TOut* dK = static_cast<TOut*>(a.dk) +
+               (a.thd ? (s.k_row0 + my_key) * a.dk_stride[1]
+                      : (int64_t)z * a.dk_stride[0] + (int64_t)my_key * a.dk_stride[1]) +
+               (int64_t)kvh * a.dk_stride[2];
+#pragma unroll
+    for (int db = 0; db < NDK; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d = db * 32 + 8 * a4 + 4 * hh;
+        if constexpr (sizeof(TOut) == 2) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * a4 + e] * a.scale);
+          *reinterpret_cast<bf16x4*>(dK + d) = w;
+        } else {
+          *reinterpret_cast<float4*>(dK + d) =
+              make_float4(acc[db][4 * a4] * a.scale, acc[db][4 * a4 + 1] * a.scale,
+                          acc[db][4 * a4 + 2] * a.scale, acc[db][4 * a4 + 3] * a.scale);
+        }
+      }
+  } else {
+    TOut* dV = static_cast<TOut*>(a.dv) +
+               (a.thd ? (s.k_row0 + my_key) * a.dv_stride[1]
+                      : (int64_t)z * a.dv_stride[0] + (int64_t)my_key * a.dv_stride[1]) +
+               (int64_t)kvh * a.dv_stride[2];
+#pragma unroll
+    for (int db = 0; db < NDV; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d = db * 32 + 8 * a4 + 4 * hh;
+        if constexpr (sizeof(TOut) == 2) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (bf16)acc[db][4 * a4 + e];
+          *reinterpret_cast<bf16x4*>(dV + d) = w;
+        } else {
+          *reinterpret_cast<float4*>(dV + d) =
+              make_float4(acc[db][4 * a4], acc[db][4 * a4 + 1], acc[db][4 * a4 + 2], acc[db][4 * a4 + 3]);
+        }
+      }
+  }
+}
+
 // ---------------------------------------------------------------- launch
 
 template <int DQK, int DV>
@@ -452,8 +738,11 @@ static hipError_t bwd_variant(const AttnArgs& a, int step, hipStream_t st) {
   }
   if (step == 1 && krows > 0) {
     dim3 g(a.heads_kv * C::NCH, (krows + 127) / 128, a.nseq);
-    hipLaunchKernelGGL((bwd_main_kernel<DQK, DV, C::OCK, C::OCV, C::BM, TIn, TOut>), g,
-                       dim3(256), 0, st, a);
+    if constexpr (DQK + DV <= 320)
+      hipLaunchKernelGGL((bwd_pair_kernel<DQK, DV, TIn, TOut>), g, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_main_kernel<DQK, DV, C::OCK, C::OCV, C::BM, TIn, TOut>), g,
+                         dim3(256), 0, st, a);
   }
   if (step == 2 && qrows > 0) {
     constexpr int PB = 256 / pow2_at_least(DQK / 8);

@@ -221,10 +221,11 @@ __device__ __forceinline__ int kpos0(const AttnArgs& a) { return a.thd ? 0 : a.k
 // neighbouring threads read one row's 128 contiguous bytes and every offset
 // is a compile-time immediate.  load() fetches rows [r0, r0+ROWS) of the
 // source (zeros past `limit`), store() writes them to a padded LDS tile.
-template <int ROWS, int D, typename TIn>
+template <int ROWS, int D, typename TIn, int NT = 256>
 struct TileStage {
-  static constexpr int RI = ROWS / 32, CJ = D / 64;
-  static_assert(ROWS % 32 == 0 && D % 64 == 0, "tile shape");
+  static constexpr int RP = NT / 8;   // rows covered per pass
+  static constexpr int RI = ROWS / RP, CJ = D / 64;
+  static_assert(ROWS % RP == 0 && D % 64 == 0, "tile shape");
   bf16x8 v[RI][CJ];
   __device__ __forceinline__ void load(const TIn* base, int64_t row_stride, int r0, int limit,
                                        int tid) {
@@ -232,7 +233,7 @@ struct TileStage {
     if (r0 + ROWS <= limit) {   // whole tile in range: no per-row predicate
 #pragma unroll
       for (int i = 0; i < RI; ++i) {
-        const TIn* p = base + (int64_t)(r0 + rg + 32 * i) * row_stride + cp;
+        const TIn* p = base + (int64_t)(r0 + rg + RP * i) * row_stride + cp;
 #pragma unroll
         for (int j = 0; j < CJ; ++j) v[i][j] = Elem<TIn>::load8(p + 64 * j);
       }
@@ -240,7 +241,7 @@ struct TileStage {
     }
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
-      const int r = r0 + rg + 32 * i;
+      const int r = r0 + rg + RP * i;
       const TIn* p = base + (int64_t)r * row_stride + cp;
 #pragma unroll
       for (int j = 0; j < CJ; ++j) v[i][j] = r < limit ? Elem<TIn>::load8(p + 64 * j) : zero8();
@@ -252,9 +253,9 @@ struct TileStage {
     const int rg = tid >> 3, cp = (tid & 7) * 8;
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
-      const int r = r0 + rg + 32 * i;
+      const int r = r0 + rg + RP * i;
       const TIn* p = base + (int64_t)r * row_stride + cp;
-      bf16* t = tile + (rg + 32 * i) * pitch + cp;
+      bf16* t = tile + (rg + RP * i) * pitch + cp;
 #pragma unroll 2
       for (int j = 0; j < CJ; ++j)
         *reinterpret_cast<bf16x8*>(t + 64 * j) = r < limit ? Elem<TIn>::load8(p + 64 * j) : zero8();
@@ -266,7 +267,7 @@ struct TileStage {
     for (int i = 0; i < RI; ++i)
 #pragma unroll
       for (int j = 0; j < CJ; ++j)
-        *reinterpret_cast<bf16x8*>(tile + (rg + 32 * i) * pitch + cp + 64 * j) = v[i][j];
+        *reinterpret_cast<bf16x8*>(tile + (rg + RP * i) * pitch + cp + 64 * j) = v[i][j];
   }
 };
 

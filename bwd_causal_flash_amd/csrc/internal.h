@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/cpattn.h"
+#include "cpattn.h"
 
 namespace cpa {
 
