@@ -156,7 +156,7 @@ def main():
                    "heads": w.heads_q, "d_qk": w.d_qk, "d_v": w.d_v, "batch": w.batch,
                    "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
                    "wall_s_timed": round(wall, 3)},
-        "roofline": {"bound": "mfma", "kernel": "bwd_main_kernel<192,128>",
+        "roofline": {"bound": "mfma", "kernel": "bwd_pair_kernel<192,128>",
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "avg_launch_ms": round(main_ms, 4), "traffic": None},

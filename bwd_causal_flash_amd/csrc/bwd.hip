@@ -531,8 +531,8 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(const AttnArgs a) {
                          (int64_t)h * a.lse_stride[1];
       const int64_t db = (a.thd ? s.q_row0 : (int64_t)z * a.delta_stride[0]) +
                          (int64_t)h * a.delta_stride[1];
-      const float l = ok ? a.lse[lb + i] : -kInf;
-      pre_l = (l == -kInf) ? kInf : l * kLog2e;   // P = 0 on empty/keyless rows
+      // raw values only: converting here would wait for the loads at once
+      pre_l = ok ? a.lse[lb + i] : -kInf;
       pre_d = ok ? a.delta[db + i] : 0.f;
       pre_p = qpos(a, s, i);
     }
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(const AttnArgs a) {
     qst.store(Qs, QP, tid);
     dost.store(dOs, OP, tid);
     if (tid < BM) {
-      Ls[tid] = pre_l;
+      Ls[tid] = (pre_l == -kInf) ? kInf : pre_l * kLog2e;   // P = 0 on keyless rows
       Dl[tid] = pre_d;
       Ps[tid] = pre_p;
     }
@@ -567,12 +567,12 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(const AttnArgs a) {
         f32x16 sacc, pacc;
 #pragma unroll
         for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
-#pragma unroll
+#pragma unroll 4
         for (int ks = 0; ks < KSQ; ++ks)
           sacc = mfma32(lds_row8(Qs, QP, qb * 32 + pr, ks * 16 + hh * 8),
                         lds_row8(Ks, KP, kg * 32 + lq, ks * 16 + hh * 8), sacc);
         if (!role_dv) {
-#pragma unroll
+#pragma unroll 4
           for (int ks = 0; ks < KSV; ++ks)
             pacc = mfma32(lds_row8(dOs, OP, qb * 32 + pr, ks * 16 + hh * 8),
                           lds_row8(Vs, VP, kg * 32 + lq, ks * 16 + hh * 8), pacc);
@@ -642,7 +642,10 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(const AttnArgs a) {
                      (int64_t)h * a.acc_stride[2] + lq;
     const bool full_rows = i0 + BM <= s.qlen;
     const int64_t rs = a.acc_stride[1];
-    for (int b = (role_dv ? kg : kg + 4); b < NBLK; b += 8) {
+    // Block schedule with a compile-time count per role (NBLK is 4, 8 or
+    // 12), so the atomics issued here have a known count and the next
+    // iteration's wait for its prefetched tile need not wait for them.
+    auto dq_block = [&](int b) {
       const int qb = b / NDK, db = b % NDK;
       f32x16 dq;
 #pragma unroll
@@ -658,12 +661,23 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(const AttnArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) atomicAdd(p0 + (8 * (v >> 2) + (v & 3)) * rs, dq[v]);
       } else {
+        const int rlim = s.qlen - (i0 + qb * 32 + 4 * hh);
+        // Rows past the end add 0 to the tile's first row, which exists
+        // (i0 < qlen), instead of branching per lane.
+        float* safe = accbase + (int64_t)i0 * rs + db * 32;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int dr = 8 * (v >> 2) + (v & 3);
-          if (i0 + qb * 32 + 4 * hh + dr < s.qlen) atomicAdd(p0 + dr * rs, dq[v]);
+          atomicAdd(dr < rlim ? p0 + dr * rs : safe, dr < rlim ? dq[v] : 0.f);
         }
       }
+    };
+    static_assert(NBLK == 4 || NBLK == 8 || NBLK == 12, "dQ block schedule");
+    if (role_dv) {
+      dq_block(kg);
+      if constexpr (NBLK == 12) dq_block(kg + 8);
+    } else {
+      if constexpr (NBLK >= 8) dq_block(kg + 4);
     }
     k = kn;
   }
