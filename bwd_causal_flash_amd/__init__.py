@@ -161,9 +161,9 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, *, causal=True, scale=None, q_se
              stream=None, step: str = "attn_bwd") -> torch.Tensor:
     """Backward into preallocated dq, dk, dv.  Returns the workspace.
 
-    ``step`` selects the C entry point: "attn_bwd" (all three steps), or one
-    of "attn_bwd_pre", "attn_bwd_main", "attn_bwd_post"."""
-    if step not in ("attn_bwd", "attn_bwd_pre", "attn_bwd_main", "attn_bwd_post"):
+    ``step`` selects the C entry point: "attn_bwd" (all four steps), or one
+    of "attn_bwd_pre", "attn_bwd_main", "attn_bwd_dq", "attn_bwd_post"."""
+    if step not in ("attn_bwd", "attn_bwd_pre", "attn_bwd_main", "attn_bwd_dq", "attn_bwd_post"):
         raise ValueError(step)
     if o.dtype != q.dtype or dout.dtype != q.dtype:
         raise TypeError("o and dout must have q's dtype")
@@ -188,10 +188,13 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, *, causal=True, scale=None, q_se
     return workspace
 
 
-def bwd_workspace_bytes(q, k, v, *, varlen=None, **kw) -> int:
+def bwd_workspace_bytes(q, k, v, *, varlen=None, minimum=False, **kw) -> int:
+    """attn_bwd_workspace_size (or, with ``minimum``, attn_bwd_workspace_min)."""
     p = _fill_problem(q, k, v, causal=True, scale=None, out_dtype=0, q_segments=None,
                       k_pos_begin=0, varlen=varlen)
-    return int(_lib.load().attn_bwd_workspace_size(ctypes.byref(p)))
+    lib = _lib.load()
+    fn = lib.attn_bwd_workspace_min if minimum else lib.attn_bwd_workspace_size
+    return int(fn(ctypes.byref(p)))
 
 
 def _as4(o: torch.Tensor, lse: torch.Tensor):

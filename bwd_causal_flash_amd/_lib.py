@@ -81,6 +81,7 @@ EXPORTS = {
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_fwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Problem)]),
     "attn_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Problem)]),
+    "attn_bwd_workspace_min": (ctypes.c_size_t, [ctypes.POINTER(Problem)]),
     "attn_fwd": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 6 +
                  [ctypes.c_size_t, ctypes.c_void_p]),
     "attn_bwd": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 +
@@ -88,6 +89,8 @@ EXPORTS = {
     "attn_bwd_pre": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 +
                      [ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]),
     "attn_bwd_main": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 +
+                      [ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]),
+    "attn_bwd_dq": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 +
                       [ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]),
     "attn_bwd_post": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 +
                       [ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]),

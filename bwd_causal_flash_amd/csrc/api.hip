@@ -168,7 +168,33 @@ size_t bwd_delta_bytes(const cpa_problem* p) {
   return align_up((size_t)(d.nb * p->heads_q * d.rows_q) * 4);
 }
 
-void set_bwd_ws(AttnArgs& a, const cpa_problem* p, void* ws) {
+size_t bwd_acc_bytes(const cpa_problem* p) {
+  const Dims d = dims_of(p);
+  return align_up((size_t)(d.nb * d.rows_q * p->heads_q * p->d_qk) * 4);
+}
+
+// dS workspace of the small-head-dim backward: tiles of 64 query rows x 128
+// keys (16 KiB, bf16) for every query head, query tile row and key block of
+// a band.  Query tile rows per head: BSHD batch * ceil(S_q / 64); THD
+// ceil(T_q / 64) + num_seqs, which keeps every document's tiles apart
+// without reading its device lengths.
+constexpr size_t kDsTileBytes = 64 * 128 * 2;
+int64_t ds_tile_rows(const cpa_problem* p) {
+  if (p->layout == CPA_LAYOUT_THD) return (p->seqlen_q + 63) / 64 + p->num_seqs;
+  return (int64_t)p->batch * ((p->seqlen_q + 63) / 64);
+}
+int64_t ds_key_blocks(const cpa_problem* p) {
+  const int64_t kr = p->layout == CPA_LAYOUT_THD ? p->max_seqlen_k : p->seqlen_k;
+  return (kr + 127) / 128;
+}
+size_t ds_block_bytes(const cpa_problem* p) {
+  return (size_t)p->heads_q * (size_t)ds_tile_rows(p) * kDsTileBytes;
+}
+size_t bwd_base_bytes(const cpa_problem* p) {
+  return kAlign + bwd_delta_bytes(p) + bwd_acc_bytes(p);
+}
+
+void set_bwd_ws(AttnArgs& a, const cpa_problem* p, void* ws, size_t ws_bytes) {
   const Dims d = dims_of(p);
   char* base = static_cast<char*>(ws);
   a.err_flag = reinterpret_cast<int*>(base);
@@ -179,6 +205,17 @@ void set_bwd_ws(AttnArgs& a, const cpa_problem* p, void* ws) {
   a.acc_stride[0] = a.thd ? 0 : d.rows_q * p->heads_q * p->d_qk;
   a.acc_stride[1] = (int64_t)p->heads_q * p->d_qk;
   a.acc_stride[2] = p->d_qk;
+  a.ds = nullptr;
+  a.ds_nu = 0;
+  a.ds_nb = 0;
+  a.kt0 = 0;
+  if (cpa::bwd_uses_ds(p->d_qk, p->d_v)) {
+    const size_t room = (ws_bytes - bwd_base_bytes(p)) / ds_block_bytes(p);
+    const int64_t nkb = ds_key_blocks(p);
+    a.ds = base + bwd_base_bytes(p);
+    a.ds_nu = ds_tile_rows(p);
+    a.ds_nb = (int)((int64_t)room < nkb ? (int64_t)room : nkb);
+  }
 }
 
 }  // namespace
@@ -208,9 +245,15 @@ size_t attn_fwd_workspace_size(const cpa_problem* p) {
 
 size_t attn_bwd_workspace_size(const cpa_problem* p) {
   if (check_problem(p) != CPA_OK) return 0;
-  const Dims d = dims_of(p);
-  return kAlign + bwd_delta_bytes(p) +
-         align_up((size_t)(d.nb * d.rows_q * p->heads_q * p->d_qk) * 4);
+  if (!cpa::bwd_uses_ds(p->d_qk, p->d_v)) return bwd_base_bytes(p);
+  const int64_t nkb = ds_key_blocks(p);
+  return bwd_base_bytes(p) + ds_block_bytes(p) * (size_t)(nkb > 1 ? nkb : 1);
+}
+
+size_t attn_bwd_workspace_min(const cpa_problem* p) {
+  if (check_problem(p) != CPA_OK) return 0;
+  if (!cpa::bwd_uses_ds(p->d_qk, p->d_v)) return bwd_base_bytes(p);
+  return bwd_base_bytes(p) + ds_block_bytes(p);
 }
 
 cpa_status attn_fwd(const cpa_problem* p, const void* q, const void* k, const void* v, void* o,
@@ -258,7 +301,9 @@ cpa_status bwd_prepare(const cpa_problem* p, const void* q, const void* k, const
   if (st != CPA_OK) return st;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return CPA_ERR_NULL;
   if (flags & ~(uint32_t)CPA_FLAG_DETERMINISTIC) return CPA_ERR_UNSUPPORTED;
-  if (flags & CPA_FLAG_DETERMINISTIC) return CPA_ERR_UNSUPPORTED;
+  // Only the dS path is free of atomics.
+  if ((flags & CPA_FLAG_DETERMINISTIC) && !cpa::bwd_uses_ds(p->d_qk, p->d_v))
+    return CPA_ERR_UNSUPPORTED;
   if (!strides_ok(p->o_stride, 3) || !strides_ok(p->do_stride, 3) ||
       !strides_ok(p->dq_stride, 3) || !strides_ok(p->dk_stride, 3) ||
       !strides_ok(p->dv_stride, 3))
@@ -267,7 +312,7 @@ cpa_status bwd_prepare(const cpa_problem* p, const void* q, const void* k, const
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       (reinterpret_cast<uintptr_t>(lse) & 3))
     return CPA_ERR_ALIGN;
-  if (!ws || ws_bytes < attn_bwd_workspace_size(p) || !aligned16(ws)) return CPA_ERR_WORKSPACE;
+  if (!ws || ws_bytes < attn_bwd_workspace_min(p) || !aligned16(ws)) return CPA_ERR_WORKSPACE;
   const int ib = dtype_bytes(p->in_dtype), ob = dtype_bytes(p->out_dtype);
   const Span ins[] = {qspan(p, q, p->q_stride, p->d_qk, ib),
                       kspan(p, k, p->k_stride, p->d_qk, ib),
@@ -295,23 +340,41 @@ cpa_status bwd_prepare(const cpa_problem* p, const void* q, const void* k, const
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  set_bwd_ws(a, p, ws);
+  set_bwd_ws(a, p, ws, ws_bytes);
   return CPA_OK;
 }
 
-// steps: bit 0 = pre (with the metadata check), bit 1 = main, bit 2 = post.
+// steps: bit 0 = pre (with the metadata check), bit 1 = main, bit 2 = dq,
+// bit 3 = post.  The whole backward runs main and dq band by band when the
+// workspace holds fewer dS key blocks than the key range; the single steps
+// need room for the whole range.
 cpa_status bwd_run(const cpa_problem* p, const void* q, const void* k, const void* v,
                    const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
                    void* ws, size_t ws_bytes, uint32_t flags, cpa_stream_t stream, int steps) {
   AttnArgs a;
   const cpa_status st = bwd_prepare(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, flags, a);
   if (st != CPA_OK) return st;
+  const bool ds = cpa::bwd_uses_ds(p->d_qk, p->d_v);
+  const int64_t nkb = ds ? ds_key_blocks(p) : 0;
+  if (ds && steps != 15 && (steps & 6) && a.ds_nb < nkb) return CPA_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto run = [&](int step) {
+    return launch_bwd(a, p->d_qk, p->d_v, p->in_dtype, p->out_dtype, step, s) == hipSuccess;
+  };
   if ((steps & 1) && launch_meta_check(a, s) != hipSuccess) return CPA_ERR_LAUNCH;
-  for (int step = 0; step < 3; ++step)
-    if ((steps >> step) & 1)
-      if (launch_bwd(a, p->d_qk, p->d_v, p->in_dtype, p->out_dtype, step, s) != hipSuccess)
-        return CPA_ERR_LAUNCH;
+  if ((steps & 1) && !run(0)) return CPA_ERR_LAUNCH;
+  if (ds && a.ds_nb > 0) {
+    const int nb = a.ds_nb;
+    for (int64_t kt0 = 0; kt0 < nkb; kt0 += nb) {
+      a.kt0 = (int)kt0;
+      a.ds_nb = (int)(nkb - kt0 < nb ? nkb - kt0 : nb);
+      if ((steps & 2) && !run(1)) return CPA_ERR_LAUNCH;
+      if ((steps & 4) && !run(2)) return CPA_ERR_LAUNCH;
+    }
+  } else if (!ds && (steps & 2) && !run(1)) {
+    return CPA_ERR_LAUNCH;
+  }
+  if ((steps & 8) && !run(3)) return CPA_ERR_LAUNCH;
   return CPA_OK;
 }
 }  // namespace
@@ -321,7 +384,7 @@ extern "C" {
 cpa_status attn_bwd(const cpa_problem* p, const void* q, const void* k, const void* v,
                     const void* o, const void* dout, const float* lse, void* dq, void* dk,
                     void* dv, void* ws, size_t ws_bytes, uint32_t flags, cpa_stream_t stream) {
-  return bwd_run(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, flags, stream, 7);
+  return bwd_run(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, flags, stream, 15);
 }
 
 cpa_status attn_bwd_pre(const cpa_problem* p, const void* q, const void* k, const void* v,
@@ -336,10 +399,16 @@ cpa_status attn_bwd_main(const cpa_problem* p, const void* q, const void* k, con
   return bwd_run(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, flags, stream, 2);
 }
 
+cpa_status attn_bwd_dq(const cpa_problem* p, const void* q, const void* k, const void* v,
+                       const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                       void* dv, void* ws, size_t ws_bytes, uint32_t flags, cpa_stream_t stream) {
+  return bwd_run(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, flags, stream, 4);
+}
+
 cpa_status attn_bwd_post(const cpa_problem* p, const void* q, const void* k, const void* v,
                          const void* o, const void* dout, const float* lse, void* dq, void* dk,
                          void* dv, void* ws, size_t ws_bytes, uint32_t flags, cpa_stream_t stream) {
-  return bwd_run(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, flags, stream, 4);
+  return bwd_run(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, flags, stream, 8);
 }
 
 cpa_status attn_merge_lse(const cpa_merge_desc* d, const void* o_acc, const float* lse_acc,

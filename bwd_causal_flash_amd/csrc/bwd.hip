@@ -1,28 +1,29 @@
 // Causal attention backward on gfx950: recompute P from the saved LSE,
-// D = rowsum(dO * O), then dQ, dK, dV.
+// D = rowsum(dO * O), then dQ, dK, dV (FlashAttention-2's backward pass,
+// with the recompute-from-LSE step of the context-parallel pages).
 //
-// Three launches on the caller's stream:
+// Launches on the caller's stream:
 //   pre   D_i = <dO_i, O_i> in fp32 from the saved O, and zero the fp32 dQ
 //         accumulator (only real rows; padding is never touched);
-//   main  key-outer: one workgroup owns 128 keys of one kv head (32 keys
-//         per wave) and walks the query heads of its GQA group and the query
-//         tiles that can see those keys;
+//   main  key-outer: one workgroup owns 128 keys of one kv head and walks
+//         the query heads of its GQA group and the query tiles that can see
+//         those keys, accumulating dK and dV;
+//   dq    (head dims with D_qk + D_v <= 320) query-outer dQ_acc += dS K from
+//         the dS tiles main stored in the workspace;
 //   post  dQ = s * acc, rounded to the output type.
 //
-// In the main kernel each wave computes S = Q K_w^T and dP = dO V_w^T for
-// its 32 keys (lane = key column; K_w and V_w stay in registers), forms
-// P = exp(S - LSE) (zero where masked or where LSE = -inf) and dS = P (dP -
-// D), and accumulates dV^T += dO^T P and dK^T += Q^T dS.  The reduction
-// operands dO^T and Q^T are read from the row-major LDS tiles with the
-// transpose reads; P and dS feed the products directly from the
-// accumulators because the Q rows were loaded in perm32 order.  dS^T goes
-// to LDS once, and the four waves then split the dQ tile (dS K over all 128
-// keys of the workgroup) and add it to the fp32 accumulator with atomics.
-// All five products are bf16 x bf16 -> fp32 on the matrix cores.
+// Inside main a wave computes S = Q K_w^T and dP = dO V_w^T for its 32 keys
+// (lane = key column), forms P = exp(S - LSE) (zero where masked or where
+// LSE = -inf) and dS = P (dP - D), and accumulates dV^T += dO^T P and
+// dK^T += Q^T dS.  The reduction operands dO^T and Q^T are read from the
+// row-major LDS tiles with the transpose reads; P and dS feed the products
+// directly from the accumulators because the Q rows were loaded in perm32
+// order.  All products are bf16 x bf16 -> fp32 on the matrix cores.
 //
-// Head dim 512: dK, dV and dQ are produced in two column chunks of 256 by
-// separate workgroups (S and dP are recomputed per chunk), and K_w, V_w are
-// read from global memory instead of registers.
+// Head dims 256 and 512 run the older single kernel: dQ is added to the
+// fp32 accumulator with atomics, and for 512 dK, dV and dQ are produced in
+// two column chunks of 256 by separate workgroups (S and dP recomputed per
+// chunk) with K_w, V_w read from global memory.
 #include "device_common.h"
 
 namespace cpa {
@@ -427,41 +428,108 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
     }
 }
 
-// ------------------------------------------------------- paired waves
+// ------------------------------------------------ dS-materialising path
 //
-// Small head dims (D_qk + D_v <= 320): eight waves per workgroup, two per
-// SIMD, so one wave's exponentials overlap the other's matrix products.
-// Each 32-key group of the 128-key tile has a wave pair: role A computes
-// S = Q K^T, dP = dO V^T, P and dS and accumulates dK^T += Q^T dS; role B
-// recomputes S and P (the same arithmetic, so the same P) and accumulates
-// dV^T += dO^T P.  Both roles keep their accumulators in one register array,
-// so each wave holds only D_qk/2 of them.  The dQ tile is split over all
-// eight waves (blocks kg, kg+8 for B; kg+4 for A), which keeps the work per
-// SIMD even: A 72 and B 56 products per 64-row query tile at D 192/128.
+// For head dims with D_qk + D_v <= 320 the backward keeps dQ out of the
+// key-outer kernel: fp32 atomics on gfx950 retire at a fixed ~1.35 TB/s
+// however the addresses fall, which would bound the whole backward by the
+// dQ traffic (D_qk/128 fp32 adds per visible query-key pair).  Instead:
+//
+//   kv  one workgroup owns 128 keys of one kv head; wave (kg, qh) takes the
+//       32 keys kg and the 32 query rows qh of each 64-row query tile, so no
+//       product is computed twice.  It forms S, P, dP, dS, accumulates dK^T
+//       and dV^T in registers, and writes dS (bf16, the same value the
+//       products use) to a workspace tile.  The two query halves' partial
+//       dK, dV are summed through LDS at the end.
+//   dq  one workgroup owns four 64-row query tiles of one query head and
+//       walks the key blocks they see: dQ_acc += dS K, with K staged in LDS
+//       and dS read straight into the matrix-core operand registers.  Each
+//       accumulator row belongs to one workgroup, so the update is a plain
+//       read-add-write in a fixed order: the result is deterministic.
+//
+// dS tile = 64 query rows x 128 keys, 16 KiB, stored as 16 chunks of 1 KiB
+// (query half qb2 in 0..1, 16-key step t in 0..7); lane l of a chunk holds
+// dS[32*qb2 + l%32][16*t + 8*(l/32) + e], e = 0..7, i.e. exactly the A
+// operand of the 32x32x16 product.  Tile (h, u, kt) lives at index
+// (h * ds_nu + ubase(seq) + u) * ds_nb + (kt - kt0).
+
+constexpr int kDsTileElems = 64 * 128;
+
+// First dS tile row of sequence z (BSHD: z * tiles per batch entry; THD: a
+// bound that keeps documents apart without a prefix sum over lengths).
+__device__ __forceinline__ int64_t ds_ubase(const AttnArgs& a, const Seq& s, int z) {
+  return a.thd ? s.q_row0 / 64 + z : (int64_t)z * ((a.seqlen_q + 63) / 64);
+}
+
+// Row pitch for bf16 tiles read only along rows (16-byte reads): P/8 odd.
+constexpr int row_pitch(int d) { return (d / 8) % 2 ? d + 16 : d + 8; }
+
+template <int DQK, int DV>
+struct KvSmem {
+  static constexpr int BN = 128, BM = 64;
+  static constexpr int QP = lds_pitch(DQK), OP = lds_pitch(DV);
+  static constexpr int KP = row_pitch(DQK), VP = row_pitch(DV), TP = lds_pitch(32);
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = K_OFF + BN * KP * 2;
+  static constexpr int Q_OFF = V_OFF + BN * VP * 2;
+  static constexpr int O_OFF = Q_OFF + BM * QP * 2;
+  static constexpr int T_OFF = O_OFF + BM * OP * 2;
+  static constexpr int L_OFF = T_OFF + 8 * 32 * TP * 2;
+  static constexpr int D_OFF = L_OFF + BM * 4;
+  static constexpr int P_OFF = D_OFF + BM * 4;
+  static constexpr int BYTES = P_OFF + BM * 4;
+  // epilogue: one wave's partial accumulators per key group, fp32
+  static constexpr int RED_BYTES = 4 * DV / 32 * 16 * 64 * 4;
+  static_assert(BYTES <= 160 * 1024 && RED_BYTES <= T_OFF, "LDS budget");
+};
+
+// Write a key's accumulated row (dK^T or dV^T layout: lane = key column,
+// element v = dimension 8*(v/4) + 4*hh + v%4 of each 32-wide block) times mul.
+template <int ND, typename TOut>
+__device__ __forceinline__ void store_key_acc(const f32x16 (&acc)[ND], TOut* o, int hh, float mul) {
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int d = db * 32 + 8 * a4 + 4 * hh;
+      if constexpr (sizeof(TOut) == 2) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * a4 + e] * mul);
+        *reinterpret_cast<bf16x4*>(o + d) = w;
+      } else {
+        *reinterpret_cast<float4*>(o + d) =
+            make_float4(acc[db][4 * a4] * mul, acc[db][4 * a4 + 1] * mul,
+                        acc[db][4 * a4 + 2] * mul, acc[db][4 * a4 + 3] * mul);
+      }
+    }
+}
+
 template <int DQK, int DV, typename TIn, typename TOut>
-__global__ __launch_bounds__(512, 1) void bwd_pair_kernel(const AttnArgs a) {
-  constexpr int BN = 128, BM = 64, NT = 512;
-  constexpr int QP = lds_pitch(DQK), OP = lds_pitch(DV), SP = lds_pitch(BM);
-  constexpr int KP = lds_pitch(DQK), VP = lds_pitch(DV);
+__global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
+  using L = KvSmem<DQK, DV>;
+  constexpr int BN = L::BN, BM = L::BM, NT = 512;
+  constexpr int QP = L::QP, OP = L::OP, KP = L::KP, VP = L::VP, TP = L::TP;
   constexpr int KSQ = DQK / 16, KSV = DV / 16;
   constexpr int NDK = DQK / 32, NDV = DV / 32;
-  constexpr int NACC = NDK > NDV ? NDK : NDV;
-  constexpr int NBLK = (BM / 32) * NDK;
-  __shared__ __attribute__((aligned(16))) bf16 Qs[BM * QP];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[BM * OP];
-  __shared__ __attribute__((aligned(16))) bf16 dSt[BN * SP];
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[BN * VP];
-  __shared__ __attribute__((aligned(16))) float Ls[BM];
-  __shared__ __attribute__((aligned(16))) float Dl[BM];
-  __shared__ __attribute__((aligned(16))) int Ps[BM];
+  constexpr int NDKH = NDK / 2;   // dK^T column blocks per query-half wave
+  static_assert(NDK % 2 == 0, "dK column split");
+  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+  bf16* Ks = reinterpret_cast<bf16*>(smem + L::K_OFF);
+  bf16* Vs = reinterpret_cast<bf16*>(smem + L::V_OFF);
+  bf16* Qs = reinterpret_cast<bf16*>(smem + L::Q_OFF);
+  bf16* dOs = reinterpret_cast<bf16*>(smem + L::O_OFF);
+  float* Ls = reinterpret_cast<float*>(smem + L::L_OFF);
+  float* Dl = reinterpret_cast<float*>(smem + L::D_OFF);
+  int* Ps = reinterpret_cast<int*>(smem + L::P_OFF);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
-  const int kg = wave & 3;
-  const bool role_dv = wave >= 4;
-  const int kvh = blockIdx.x % a.heads_kv;
-  const int kt = blockIdx.y;
+  const int kg = wave & 3, qh = wave >> 2;
+  bf16* Ts = reinterpret_cast<bf16*>(smem + L::T_OFF);
+  bf16* Tw = Ts + wave * 32 * TP;
+  const int kvh = blockIdx.x;
+  const int kt = a.kt0 + (int)blockIdx.y;
   const int z = blockIdx.z;
   const Seq s = load_seq(a, z);
   const int j0 = kt * BN;
@@ -473,8 +541,7 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(const AttnArgs a) {
   const bool key_valid = my_key < s.klen;
   const int my_kpos = kp0 + my_key;
   const bool wave_has_keys = jw < s.klen;
-  const int wk_last = min(jw + 31, s.klen - 1);
-  const int wkpos_lo = kp0 + jw, wkpos_hi = kp0 + wk_last;
+  const int wkpos_lo = kp0 + jw, wkpos_hi = kp0 + min(jw + 31, s.klen - 1);
   const int gkpos_lo = kp0 + j0;
 
   const TIn* Q = static_cast<const TIn*>(a.q);
@@ -488,11 +555,15 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(const AttnArgs a) {
   TileStage<BN, DQK, TIn, NT>::copy(K + kbase, a.k_stride[1], j0, s.klen, Ks, KP, tid);
   TileStage<BN, DV, TIn, NT>::copy(V + vbase, a.v_stride[1], j0, s.klen, Vs, VP, tid);
 
-  f32x16 acc[NACC];
+  f32x16 acck[NDKH], accv[NDV];
 #pragma unroll
-  for (int d = 0; d < NACC; ++d)
+  for (int d = 0; d < NDKH; ++d)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[d][v] = 0.f;
+    for (int v = 0; v < 16; ++v) acck[d][v] = 0.f;
+#pragma unroll
+  for (int d = 0; d < NDV; ++d)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) accv[d][v] = 0.f;
 
   const int pr = perm32(lq);
   const int nqt = (s.qlen + BM - 1) / BM;
@@ -538,15 +609,19 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(const AttnArgs a) {
     }
   };
 
+  bf16* const ds = static_cast<bf16*>(a.ds);
+  const int64_t ubase = ds_ubase(a, s, z);
+  // this lane's 16 bytes of the wave's first chunk (qb2 = qh, t = 2*kg)
+  const int64_t chunk_off = ((int64_t)(qh * 8 + 2 * kg) * 64 + lane) * 8;
+
   int k = next_visible(0);
   if (k < total) fetch(tile_of(k));
   while (k < total) {
     const int u = tile_of(k);
     const int h = kvh * a.group + u / nqt;
-    const int i0 = (u % nqt) * BM;
+    const int ut = u % nqt;
+    const int i0 = ut * BM;
     const int i1 = min(i0 + BM, s.qlen);
-    int tlo, thi;
-    qpos_range(a, s, i0, i1, tlo, thi);
     __syncthreads();
     qst.store(Qs, QP, tid);
     dost.store(dOs, OP, tid);
@@ -556,181 +631,238 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(const AttnArgs a) {
       Ps[tid] = pre_p;
     }
     const int kn = next_visible(k + 1);
-    if (kn < total) fetch(tile_of(kn));
     __syncthreads();
 
-    const bool wave_on = wave_has_keys && (!a.causal || thi >= wkpos_lo);
-    const bool need_mask = (jw + 32 > s.klen) || (a.causal && tlo < wkpos_hi);
+    // Query halves: rows [i0 + 32*qq, +32) of the tile, handled by waves
+    // (kg, qq); a half with no visible (row, key) pair skips its products
+    // and contributes dS = 0.
+    bool on[2];
+    int wlo = 0;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const int r0 = i0 + qq * 32;
+      int lo = 0, hi = -1;
+      if (r0 < i1) qpos_range(a, s, r0, min(r0 + 32, i1), lo, hi);
+      on[qq] = wave_has_keys && r0 < i1 && (!a.causal || hi >= wkpos_lo);
+      if (qq == qh) wlo = lo;
+    }
+    const bool wave_on = on[qh];
+    const bool need_mask = (jw + 32 > s.klen) || (a.causal && wlo < wkpos_hi);
     if (wave_on) {
+      f32x16 sacc, pacc;
 #pragma unroll
-      for (int qb = 0; qb < BM / 32; ++qb) {
-        f32x16 sacc, pacc;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
+      for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
 #pragma unroll 4
-        for (int ks = 0; ks < KSQ; ++ks)
-          sacc = mfma32(lds_row8(Qs, QP, qb * 32 + pr, ks * 16 + hh * 8),
-                        lds_row8(Ks, KP, kg * 32 + lq, ks * 16 + hh * 8), sacc);
-        if (!role_dv) {
+      for (int ks = 0; ks < KSQ; ++ks)
+        sacc = mfma32(lds_row8(Qs, QP, qh * 32 + pr, ks * 16 + hh * 8),
+                      lds_row8(Ks, KP, kg * 32 + lq, ks * 16 + hh * 8), sacc);
 #pragma unroll 4
-          for (int ks = 0; ks < KSV; ++ks)
-            pacc = mfma32(lds_row8(dOs, OP, qb * 32 + pr, ks * 16 + hh * 8),
-                          lds_row8(Vs, VP, kg * 32 + lq, ks * 16 + hh * 8), pacc);
-        }
-        // This lane's 16 rows are two runs of 8: qb*32 + 16*vh + 8*hh + e.
+      for (int ks = 0; ks < KSV; ++ks)
+        pacc = mfma32(lds_row8(dOs, OP, qh * 32 + pr, ks * 16 + hh * 8),
+                      lds_row8(Vs, VP, kg * 32 + lq, ks * 16 + hh * 8), pacc);
+      // Prefetch the next tile only now: its staging registers are then not
+      // live during the S and dP products, where the pressure peaks.
+      if (kn < total) fetch(tile_of(kn));
+      // This lane's 16 rows are two runs of 8: qh*32 + 16*vh + 8*hh + e.
 #pragma unroll
-        for (int vh = 0; vh < 2; ++vh) {
-          const int r0 = qb * 32 + 16 * vh + 8 * hh;
-          const float4 l0 = *reinterpret_cast<const float4*>(&Ls[r0]);
-          const float4 l1 = *reinterpret_cast<const float4*>(&Ls[r0 + 4]);
-          const float lr[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+      for (int vh = 0; vh < 2; ++vh) {
+        const int rr = qh * 32 + 16 * vh + 8 * hh;
+        const float4 l0 = *reinterpret_cast<const float4*>(&Ls[rr]);
+        const float4 l1 = *reinterpret_cast<const float4*>(&Ls[rr + 4]);
+        const float4 d0 = *reinterpret_cast<const float4*>(&Dl[rr]);
+        const float4 d1 = *reinterpret_cast<const float4*>(&Dl[rr + 4]);
+        const float lr[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        const float dr[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int v = 8 * vh + e;
-            float p = fast_exp2(__builtin_fmaf(sacc[v], a.scale_log2, -lr[e]));
-            if (need_mask) {
-              const bool vis = key_valid && (!a.causal || my_kpos <= Ps[r0 + e]);
-              p = vis ? p : 0.f;
-            }
-            sacc[v] = p;
+        for (int e = 0; e < 8; ++e) {
+          const int v = 8 * vh + e;
+          float p = fast_exp2(__builtin_fmaf(sacc[v], a.scale_log2, -lr[e]));
+          if (need_mask) {
+            const bool vis = key_valid && (!a.causal || my_kpos <= Ps[rr + e]);
+            p = vis ? p : 0.f;
           }
-          if (!role_dv) {
-            const float4 d0 = *reinterpret_cast<const float4*>(&Dl[r0]);
-            const float4 d1 = *reinterpret_cast<const float4*>(&Dl[r0 + 4]);
-            const float dr[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int v = 8 * vh + e;
-              pacc[v] = sacc[v] * (pacc[v] - dr[e]);
-            }
-          }
-        }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int k0 = 32 * qb + 16 * tt + 8 * (grp >> 1);
-          bf16x8 w;
-          if (!role_dv) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] = (bf16)pacc[8 * tt + e];
-#pragma unroll
-            for (int db = 0; db < NDK; ++db)
-              acc[db] = mfma32(lds_tr8(Qs, QP, k0, db * 32 + 16 * (grp & 1), gl), w, acc[db]);
-            *reinterpret_cast<bf16x8*>(&dSt[(kg * 32 + lq) * SP + qb * 32 + 16 * tt + 8 * hh]) = w;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] = (bf16)sacc[8 * tt + e];
-#pragma unroll
-            for (int db = 0; db < NDV; ++db)
-              acc[db] = mfma32(lds_tr8(dOs, OP, k0, db * 32 + 16 * (grp & 1), gl), w, acc[db]);
-          }
+          sacc[v] = p;
+          pacc[v] = p * (pacc[v] - dr[e]);
         }
       }
-    } else if (!role_dv) {
 #pragma unroll
-      for (int qb = 0; qb < BM / 32; ++qb)
+      for (int tt = 0; tt < 2; ++tt) {
+        const int k0 = 32 * qh + 16 * tt + 8 * (grp >> 1);
+        bf16x8 wp, wd;
 #pragma unroll
-        for (int hv = 0; hv < 2; ++hv)
-          *reinterpret_cast<bf16x8*>(&dSt[(kg * 32 + lq) * SP + qb * 32 + 16 * hv + 8 * hh]) =
-              zero8();
-    }
-    __syncthreads();
-
-    // dQ tile (BM x DQK) = dS (BM x 128 keys) K (128 keys x DQK): 32x32
-    // blocks kg, kg+8 for role B and kg+4 for role A.
-    float* accbase = a.dq_acc +
-                     (a.thd ? s.q_row0 * a.acc_stride[1] : (int64_t)z * a.acc_stride[0]) +
-                     (int64_t)h * a.acc_stride[2] + lq;
-    const bool full_rows = i0 + BM <= s.qlen;
-    const int64_t rs = a.acc_stride[1];
-    // Block schedule with a compile-time count per role (NBLK is 4, 8 or
-    // 12), so the atomics issued here have a known count and the next
-    // iteration's wait for its prefetched tile need not wait for them.
-    auto dq_block = [&](int b) {
-      const int qb = b / NDK, db = b % NDK;
-      f32x16 dq;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) dq[v] = 0.f;
-#pragma unroll
-      for (int t = 0; t < BN / 16; ++t) {
-        const int k0 = 16 * t + 8 * (grp >> 1);
-        dq = mfma32(lds_tr8(dSt, SP, k0, qb * 32 + 16 * (grp & 1), gl),
-                    lds_tr8(Ks, KP, k0, db * 32 + 16 * (grp & 1), gl), dq);
-      }
-      float* p0 = accbase + (int64_t)(i0 + qb * 32 + 4 * hh) * rs + db * 32;
-      if (full_rows) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) atomicAdd(p0 + (8 * (v >> 2) + (v & 3)) * rs, dq[v]);
-      } else {
-        const int rlim = s.qlen - (i0 + qb * 32 + 4 * hh);
-        // Rows past the end add 0 to the tile's first row, which exists
-        // (i0 < qlen), instead of branching per lane.
-        float* safe = accbase + (int64_t)i0 * rs + db * 32;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int dr = 8 * (v >> 2) + (v & 3);
-          atomicAdd(dr < rlim ? p0 + dr * rs : safe, dr < rlim ? dq[v] : 0.f);
+        for (int e = 0; e < 8; ++e) {
+          wp[e] = (bf16)sacc[8 * tt + e];
+          wd[e] = (bf16)pacc[8 * tt + e];
         }
+#pragma unroll
+        for (int db = 0; db < NDV; ++db)
+          accv[db] = mfma32(lds_tr8(dOs, OP, k0, db * 32 + 16 * (grp & 1), gl), wp, accv[db]);
+        // dS^T block of this wave: row = key, column = query row (natural order)
+        *reinterpret_cast<bf16x8*>(&Tw[lq * TP + 16 * tt + 8 * hh]) = wd;
       }
-    };
-    static_assert(NBLK == 4 || NBLK == 8 || NBLK == 12, "dQ block schedule");
-    if (role_dv) {
-      dq_block(kg);
-      if constexpr (NBLK == 12) dq_block(kg + 8);
     } else {
-      if constexpr (NBLK >= 8) dq_block(kg + 4);
+      if (kn < total) fetch(tile_of(kn));
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        *reinterpret_cast<bf16x8*>(&Tw[lq * TP + 16 * tt + 8 * hh]) = zero8();
     }
+    __syncthreads();   // both query halves' dS blocks are in LDS
+
+    // dK^T column blocks [qh*NDKH, +NDKH) over both query halves; the dS
+    // operand (lane = key column, 8 consecutive query rows) is a row read of
+    // the half's dS^T block.
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      if (!on[qq]) continue;
+      const bf16* Tq = Ts + (kg + 4 * qq) * 32 * TP;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int k0 = 32 * qq + 16 * tt + 8 * (grp >> 1);
+        const bf16x8 wd = lds_row8(Tq, TP, lq, 16 * tt + 8 * hh);
+#pragma unroll
+        for (int j = 0; j < NDKH; ++j)
+          acck[j] = mfma32(lds_tr8(Qs, QP, k0, (qh * NDKH + j) * 32 + 16 * (grp & 1), gl), wd,
+                           acck[j]);
+      }
+    }
+    // This wave's two dS chunks for the dQ step (zeros when the half is off).
+    bf16* dst = ds + (((int64_t)h * a.ds_nu + ubase + ut) * a.ds_nb + (kt - a.kt0)) *
+                         kDsTileElems + chunk_off;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      *reinterpret_cast<bf16x8*>(dst + 512 * j) =
+          lds_tr8(Tw, TP, 16 * j + 8 * (grp >> 1), 16 * (grp & 1), gl);
     k = kn;
   }
 
-  if (!key_valid) return;
-  if (!role_dv) {
-    TOut* dK = static_cast<TOut*>(a.dk) +
-               (a.thd ? (s.k_row0 + my_key) * a.dk_stride[1]
-                      : (int64_t)z * a.dk_stride[0] + (int64_t)my_key * a.dk_stride[1]) +
-               (int64_t)kvh * a.dk_stride[2];
-#pragma unroll
-    for (int db = 0; db < NDK; ++db)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const int d = db * 32 + 8 * a4 + 4 * hh;
-        if constexpr (sizeof(TOut) == 2) {
-          bf16x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * a4 + e] * a.scale);
-          *reinterpret_cast<bf16x4*>(dK + d) = w;
-        } else {
-          *reinterpret_cast<float4*>(dK + d) =
-              make_float4(acc[db][4 * a4] * a.scale, acc[db][4 * a4 + 1] * a.scale,
-                          acc[db][4 * a4 + 2] * a.scale, acc[db][4 * a4 + 3] * a.scale);
-        }
-      }
-  } else {
-    TOut* dV = static_cast<TOut*>(a.dv) +
-               (a.thd ? (s.k_row0 + my_key) * a.dv_stride[1]
-                      : (int64_t)z * a.dv_stride[0] + (int64_t)my_key * a.dv_stride[1]) +
-               (int64_t)kvh * a.dv_stride[2];
+  // dK: each wave holds complete sums for its column blocks.  dV: the two
+  // query halves' partials are summed through LDS into the qh = 0 waves.
+  auto key_row = [&](void* outp, const int64_t* st) -> TOut* {
+    return static_cast<TOut*>(outp) +
+           (a.thd ? (s.k_row0 + my_key) * st[1] : (int64_t)z * st[0] + (int64_t)my_key * st[1]) +
+           (int64_t)kvh * st[2];
+  };
+  if (key_valid) store_key_acc(acck, key_row(a.dk, a.dk_stride) + qh * NDKH * 32, hh, a.scale);
+  float* red = reinterpret_cast<float*>(smem);
+  __syncthreads();
+  if (qh == 1) {
 #pragma unroll
     for (int db = 0; db < NDV; ++db)
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const int d = db * 32 + 8 * a4 + 4 * hh;
-        if constexpr (sizeof(TOut) == 2) {
-          bf16x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (bf16)acc[db][4 * a4 + e];
-          *reinterpret_cast<bf16x4*>(dV + d) = w;
-        } else {
-          *reinterpret_cast<float4*>(dV + d) =
-              make_float4(acc[db][4 * a4], acc[db][4 * a4 + 1], acc[db][4 * a4 + 2], acc[db][4 * a4 + 3]);
-        }
-      }
+      for (int v = 0; v < 16; ++v) red[((kg * NDV + db) * 16 + v) * 64 + lane] = accv[db][v];
   }
+  __syncthreads();
+  if (qh == 0) {
+#pragma unroll
+    for (int db = 0; db < NDV; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) accv[db][v] += red[((kg * NDV + db) * 16 + v) * 64 + lane];
+    if (key_valid) store_key_acc(accv, key_row(a.dv, a.dv_stride), hh, 1.f);
+  }
+}
+
+// Last key block (inclusive) that query tile ut of sequence s sees, or -1.
+__device__ __forceinline__ int dq_last_block(const AttnArgs& a, const Seq& s, int ut, int nkb,
+                                             int kp0) {
+  const int nqt = (s.qlen + 63) / 64;
+  if (ut >= nqt || nkb <= 0) return -1;
+  if (!a.causal) return nkb - 1;
+  int lo, hi;
+  qpos_range(a, s, ut * 64, min(ut * 64 + 64, s.qlen), lo, hi);
+  if (hi < kp0) return -1;
+  const int b = (hi - kp0) / 128;
+  return b < nkb - 1 ? b : nkb - 1;
+}
+
+template <int DQK, typename TIn>
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
+  constexpr int BN = 128, NT = 512, NDK = DQK / 32;
+  constexpr int KP = lds_pitch(DQK);
+  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
+  const int h = blockIdx.x;
+  const int kvh = h / a.group;
+  const int z = blockIdx.z;
+  const Seq s = load_seq(a, z);
+  const int ut0 = 4 * (int)blockIdx.y;
+  const int ut = ut0 + (wave >> 1);
+  const int qb2 = wave & 1;
+  const int nkb = (s.klen + BN - 1) / BN;
+  const int kp0 = kpos0(a);
+  const int my_last = dq_last_block(a, s, ut, nkb, kp0);
+  int wg_last = -1;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) wg_last = max(wg_last, dq_last_block(a, s, ut0 + t, nkb, kp0));
+  const int kt_begin = a.kt0;
+  const int kt_end = min(wg_last + 1, a.kt0 + a.ds_nb);
+  if (kt_begin >= kt_end) return;   // uniform over the workgroup
+
+  const TIn* K = static_cast<const TIn*>(a.k);
+  const int64_t kbase = (a.thd ? s.k_row0 * a.k_stride[1] : (int64_t)z * a.k_stride[0]) +
+                        (int64_t)kvh * a.k_stride[2];
+  const bf16* dsw = static_cast<const bf16*>(a.ds) +
+                    ((int64_t)h * a.ds_nu + ds_ubase(a, s, z) + ut) * a.ds_nb * kDsTileElems +
+                    ((int64_t)qb2 * 8 * 64 + lane) * 8;
+  auto load_frags = [&](int kt, bf16x8* f) {
+    const bf16* p = dsw + (int64_t)(kt - a.kt0) * kDsTileElems;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) f[t] = *reinterpret_cast<const bf16x8*>(p + 512 * t);
+  };
+
+  f32x16 acc[NDK];
+#pragma unroll
+  for (int d = 0; d < NDK; ++d)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[d][v] = 0.f;
+
+  TileStage<BN, DQK, TIn, NT> kst;
+  bf16x8 fr[8], nfr[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) nfr[t] = zero8();
+  kst.load(K + kbase, a.k_stride[1], kt_begin * BN, s.klen, tid);
+  if (kt_begin <= my_last) load_frags(kt_begin, fr);
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    __syncthreads();
+    kst.store(Ks, KP, tid);
+    if (kt + 1 < kt_end) {
+      kst.load(K + kbase, a.k_stride[1], (kt + 1) * BN, s.klen, tid);
+      if (kt + 1 <= my_last) load_frags(kt + 1, nfr);
+    }
+    __syncthreads();
+    if (kt <= my_last) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int db = 0; db < NDK; ++db)
+          acc[db] = mfma32(fr[t], lds_tr8(Ks, KP, 16 * t + 8 * (grp >> 1),
+                                          db * 32 + 16 * (grp & 1), gl), acc[db]);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) fr[t] = nfr[t];
+  }
+  if (my_last < kt_begin) return;
+  float* accbase = a.dq_acc + (a.thd ? s.q_row0 * a.acc_stride[1] : (int64_t)z * a.acc_stride[0]) +
+                   (int64_t)h * a.acc_stride[2] + lq;
+  const int64_t rs = a.acc_stride[1];
+  const int rbase = ut * 64 + qb2 * 32;
+#pragma unroll
+  for (int db = 0; db < NDK; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int i = rbase + acc_row(v, hh);
+      if (i < s.qlen) accbase[(int64_t)i * rs + db * 32] += acc[db][v];
+    }
 }
 
 // ---------------------------------------------------------------- launch
 
 template <int DQK, int DV>
 struct BwdCfg {
+  // dS-materialising path (kv + dq kernels) for the small head dims; the
+  // 256/512 dims keep the single key-outer kernel with dQ atomics.
+  static constexpr bool DS_PATH = DQK + DV <= 320;
   static constexpr bool BIG = DQK > 256 || DV > 256;
   static constexpr int OCK = BIG ? DQK / 2 : DQK;
   static constexpr int OCV = BIG ? DV / 2 : DV;
@@ -751,14 +883,23 @@ static hipError_t bwd_variant(const AttnArgs& a, int step, hipStream_t st) {
     hipLaunchKernelGGL((bwd_pre_kernel<DV, DQK, TIn>), g, dim3(256), 0, st, a);
   }
   if (step == 1 && krows > 0) {
-    dim3 g(a.heads_kv * C::NCH, (krows + 127) / 128, a.nseq);
-    if constexpr (DQK + DV <= 320)
-      hipLaunchKernelGGL((bwd_pair_kernel<DQK, DV, TIn, TOut>), g, dim3(512), 0, st, a);
-    else
+    if constexpr (C::DS_PATH) {
+      dim3 g(a.heads_kv, a.ds_nb, a.nseq);
+      hipLaunchKernelGGL((bwd_kv_kernel<DQK, DV, TIn, TOut>), g, dim3(512), 0, st, a);
+    } else {
+      dim3 g(a.heads_kv * C::NCH, (krows + 127) / 128, a.nseq);
       hipLaunchKernelGGL((bwd_main_kernel<DQK, DV, C::OCK, C::OCV, C::BM, TIn, TOut>), g,
                          dim3(256), 0, st, a);
+    }
   }
-  if (step == 2 && qrows > 0) {
+  if constexpr (C::DS_PATH) {
+    if (step == 2 && krows > 0 && qrows > 0) {
+      const int qtiles = (qrows + 63) / 64;
+      dim3 g(a.heads_q, (qtiles + 3) / 4, a.nseq);
+      hipLaunchKernelGGL((bwd_dq_kernel<DQK, TIn>), g, dim3(512), 0, st, a);
+    }
+  }
+  if (step == 3 && qrows > 0) {
     constexpr int PB = 256 / pow2_at_least(DQK / 8);
     const int64_t pairs = (int64_t)qrows * a.heads_q;
     dim3 g((unsigned)((pairs + PB - 1) / PB), 1, a.nseq);
@@ -775,7 +916,8 @@ static hipError_t bwd_dtypes(const AttnArgs& a, int in_dt, int out_dt, int step,
   return bwd_variant<DQK, DV, float, float>(a, step, st);
 }
 
-// step 0: D and dQ-accumulator zeroing; 1: main; 2: dQ cast.
+// step 0: D and dQ-accumulator zeroing; 1: key-outer kernel; 2: dQ
+// accumulation from the stored dS (no-op on the atomic path); 3: dQ cast.
 hipError_t launch_bwd(const AttnArgs& a, int d_qk, int d_v, int in_dt, int out_dt, int step,
                       hipStream_t st) {
   if (d_qk == 64 && d_v == 64) return bwd_dtypes<64, 64>(a, in_dt, out_dt, step, st);
@@ -785,5 +927,7 @@ hipError_t launch_bwd(const AttnArgs& a, int d_qk, int d_v, int in_dt, int out_d
   if (d_qk == 512 && d_v == 512) return bwd_dtypes<512, 512>(a, in_dt, out_dt, step, st);
   return hipErrorInvalidValue;
 }
+
+bool bwd_uses_ds(int d_qk, int d_v) { return d_qk + d_v <= 320; }
 
 }  // namespace cpa

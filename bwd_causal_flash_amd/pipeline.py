@@ -134,7 +134,8 @@ class RankStep:
 
     def backward(self, stream=None, main_events=None):
         """One backward over all query rows and keys.  ``main_events`` =
-        (start, end) HIP events recorded around the main kernel only."""
+        (start, end) HIP events recorded around the key-outer main kernel
+        only."""
         kw = dict(causal=True, scale=self.scale, q_segments=self.segments, k_pos_begin=0,
                   workspace=self.bwd_ws, stream=stream)
         args = (self.q, self.k, self.v, self.o, self.dout, self.lse, self.dq, self.dk, self.dv)
@@ -144,6 +145,7 @@ class RankStep:
         attn_bwd(*args, step="attn_bwd_main", **kw)
         if main_events:
             main_events[1].record(stream)
+        attn_bwd(*args, step="attn_bwd_dq", **kw)
         attn_bwd(*args, step="attn_bwd_post", **kw)
         return self.dq, self.dk, self.dv
 

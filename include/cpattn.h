@@ -157,19 +157,36 @@ cpa_status attn_fwd(const cpa_problem* p, const void* q, const void* k,
                     const void* v, void* o, float* lse, void* ws,
                     size_t ws_bytes, cpa_stream_t stream);
 
-/* Bytes of workspace attn_bwd needs (host, pure): the error flag, D =
- * rowsum(dO*O) and an fp32 dQ accumulator. */
+/* Bytes of workspace attn_bwd needs (host, pure) for its fastest schedule:
+ * the error flag, D = rowsum(dO*O), an fp32 dQ accumulator and, for head
+ * dims with d_qk + d_v <= 320, the bf16 dS tiles of the whole key range
+ * (16 KiB per query head, 64-row query tile and 128-key block: about
+ * 2 * heads_q * S_q * S_k bytes).  Same problem -> same size. */
 size_t attn_bwd_workspace_size(const cpa_problem* p);
+
+/* Smallest workspace attn_bwd accepts (host, pure): as above with the dS
+ * tiles of one 128-key block.  Between this and attn_bwd_workspace_size,
+ * attn_bwd processes the keys in bands of as many blocks as fit. */
+size_t attn_bwd_workspace_min(const cpa_problem* p);
 
 /*
  * Backward.  Given the saved q, k, v, o (in_dtype), lse (fp32) and dout,
  * writes dq, dk, dv (out_dtype) for every real row, with exact zeros where a
- * row or key has no visible partner; THD padding rows are untouched.  dQ is
- * accumulated in fp32 with atomics, so its low bits may vary from run to run
- * (the pages' backward kernels are nondeterministic too, PR 3699).  flags:
- * CPA_FLAG_DETERMINISTIC is declined with CPA_ERR_UNSUPPORTED.  Outputs must
- * not overlap each other or the inputs; ws holds attn_bwd_workspace_size(p)
- * bytes (first int32 = THD metadata error flag, as for attn_fwd).
+ * row or key has no visible partner; THD padding rows are untouched.
+ *
+ * Head dims with d_qk + d_v <= 320 (64/64, 128/128, 192/128): a key-outer
+ * kernel writes dK, dV and the bf16 dS tiles; a query-outer kernel then
+ * adds dS K into the dQ accumulator with a fixed order and no atomics, so
+ * the result is bitwise deterministic and CPA_FLAG_DETERMINISTIC is
+ * honoured.  (FlashAttention-2's backward adds dS K to dQ with atomics; on
+ * this GPU fp32 atomics retire at about 1.35 TB/s, which would bound the
+ * whole backward, so dS is stored and reduced per query tile instead.)
+ * Head dims 256 and 512 add dQ with fp32 atomics, so its low bits may vary
+ * from run to run (the pages' backward kernels are nondeterministic too,
+ * PR 3699), and CPA_FLAG_DETERMINISTIC is declined with
+ * CPA_ERR_UNSUPPORTED.  Outputs must not overlap each other or the inputs;
+ * ws holds at least attn_bwd_workspace_min(p) bytes (first int32 = THD
+ * metadata error flag, as for attn_fwd).
  */
 cpa_status attn_bwd(const cpa_problem* p, const void* q, const void* k,
                     const void* v, const void* o, const void* dout,
@@ -177,19 +194,24 @@ cpa_status attn_bwd(const cpa_problem* p, const void* q, const void* k,
                     size_t ws_bytes, uint32_t flags, cpa_stream_t stream);
 
 /*
- * The three steps attn_bwd enqueues, callable one by one with the same
+ * The four steps attn_bwd enqueues, callable one by one with the same
  * arguments (the backward helper chain of PR 3699, "Add cuDNN OSS backward
  * dispatch for context parallel attention", Implementation and supported
  * scope).  They must run in this order on one stream, with the same problem,
  * tensors and workspace:
  *   attn_bwd_pre   writes the metadata flag, D = rowsum(dO*O) (fp32, from
  *                  the given O) and zeroes the fp32 dQ accumulator;
- *   attn_bwd_main  recomputes P from the LSE and accumulates dK, dV (written
- *                  to dk, dv) and dQ (into the workspace accumulator);
+ *   attn_bwd_main  recomputes P from the LSE, writes dK, dV (to dk, dv) and
+ *                  either stores dS in the workspace (d_qk + d_v <= 320) or
+ *                  adds dS K to the dQ accumulator with atomics;
+ *   attn_bwd_dq    adds dS K for the same key range to the accumulator
+ *                  (no-op for head dims 256 and 512);
  *   attn_bwd_post  writes dq = softmax_scale * accumulator.
- * attn_bwd_main may be called several times between one pre and one post,
- * with K/V (and k_pos_begin) of different key blocks, to accumulate dQ over
- * the blocks of a ring while each call writes its own block's dK, dV.
+ * attn_bwd_main followed by attn_bwd_dq may be repeated between one pre and
+ * one post, with K/V (and k_pos_begin) of different key blocks, to
+ * accumulate dQ over the blocks of a ring while each main writes its own
+ * block's dK, dV.  Called one by one, main and dq need the full
+ * attn_bwd_workspace_size(p) (else CPA_ERR_WORKSPACE).
  */
 cpa_status attn_bwd_pre(const cpa_problem* p, const void* q, const void* k,
                         const void* v, const void* o, const void* dout,
@@ -201,6 +223,11 @@ cpa_status attn_bwd_main(const cpa_problem* p, const void* q, const void* k,
                          const float* lse, void* dq, void* dk, void* dv,
                          void* ws, size_t ws_bytes, uint32_t flags,
                          cpa_stream_t stream);
+cpa_status attn_bwd_dq(const cpa_problem* p, const void* q, const void* k,
+                       const void* v, const void* o, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv,
+                       void* ws, size_t ws_bytes, uint32_t flags,
+                       cpa_stream_t stream);
 cpa_status attn_bwd_post(const cpa_problem* p, const void* q, const void* k,
                          const void* v, const void* o, const void* dout,
                          const float* lse, void* dq, void* dk, void* dv,

@@ -86,14 +86,28 @@ def main():
         return lib.attn_bwd(ctypes.byref(p), ptr(1), ptr(2), ptr(3), ptr(40), ptr(50), ptr(60),
                             ptr(dq), ptr(dk), ptr(dv), ptr(200), wsb, flags, None)
 
+    p = good_problem(d_qk=256, d_v=256)
+    case("bwd_deterministic_declined_atomic_dims", "CPA_ERR_UNSUPPORTED", bwd(p, flags=1))
     p = good_problem()
-    case("bwd_deterministic_declined", "CPA_ERR_UNSUPPORTED", bwd(p, flags=1))
+    # The dS path honours the flag: validation passes and only the launch,
+    # with no GPU visible, fails.
+    case("bwd_deterministic_accepted_ds_dims", "CPA_ERR_LAUNCH", bwd(p, flags=1))
     case("bwd_unknown_flag", "CPA_ERR_UNSUPPORTED", bwd(p, flags=2))
     need = lib.attn_bwd_workspace_size(ctypes.byref(p))
-    case("bwd_workspace_small", "CPA_ERR_WORKSPACE", bwd(p, wsb=need - 1))
+    least = lib.attn_bwd_workspace_min(ctypes.byref(p))
+    case("bwd_workspace_small", "CPA_ERR_WORKSPACE", bwd(p, wsb=least - 1))
+    case("bwd_workspace_min_accepted", "CPA_ERR_LAUNCH", bwd(p, wsb=least))
+    step = lambda fn, wsb: fn(ctypes.byref(p), ptr(1), ptr(2), ptr(3), ptr(40), ptr(50), ptr(60),
+                             ptr(100), ptr(120), ptr(140), ptr(200), wsb, 0, None)
+    case("bwd_main_step_needs_full_workspace", "CPA_ERR_WORKSPACE", step(lib.attn_bwd_main, least))
+    case("bwd_dq_step_needs_full_workspace", "CPA_ERR_WORKSPACE", step(lib.attn_bwd_dq, need - 1))
     case("bwd_outputs_overlap", "CPA_ERR_OVERLAP", bwd(p, dk=100))
     case("bwd_output_overlaps_input", "CPA_ERR_OVERLAP", bwd(p, dq=2))
     out["bwd_workspace_bytes"] = ["int", int(need)]
+    out["bwd_workspace_min_bytes"] = ["int", int(least)]
+    p = good_problem(d_qk=256, d_v=256)
+    out["bwd_workspace_atomic_dims"] = ["int", int(lib.attn_bwd_workspace_size(ctypes.byref(p))),
+                                        int(lib.attn_bwd_workspace_min(ctypes.byref(p)))]
 
     md = _lib.MergeDesc()
     md.batch, md.heads, md.d_v, md.seqlen = 1, 4, 128, 64

@@ -1,0 +1,139 @@
+"""Backward paths beyond one full call, on the dS path (d_qk + d_v <= 320):
+
+* CPA_FLAG_DETERMINISTIC: repeated calls, also on a side stream, give
+  bitwise identical dQ, dK, dV;
+* a workspace below attn_bwd_workspace_size: the keys are processed in
+  bands; dK and dV do not depend on the band split (bitwise), dQ meets the
+  accuracy criterion for every split;
+* the ring-step use of the step entry points (the per-block backward of the
+  pages' P2P ring): pre once, then main + dq per key block with that
+  block's K, V, dK, dV and k_pos_begin, then post once.
+
+Every result is checked against the fp64 oracle with the accuracy
+criterion (tests/criteria.py).
+"""
+import math
+
+import pytest
+import torch
+
+import oracle
+from tests import criteria
+from tests.gpu_util import dev, naive64, say, true64
+
+pytestmark = pytest.mark.gpu
+
+import bwd_causal_flash_amd as cpa  # noqa: E402
+
+# Dual-chunk query rows (positions 0..127 and 896..1023), 1024 keys, GQA 4/2,
+# head dims 192/128: 8 key blocks, two of them ragged in the ring split.
+B, SQ, SK, HQ, HKV, DQK, DV = 1, 256, 1024, 4, 2, 192, 128
+SEGS = [(0, 0), (128, 896)]
+SCALE = 1.0 / math.sqrt(DQK)
+DETERMINISTIC = 1
+
+
+@pytest.fixture(scope="module")
+def problem():
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn(B, SQ, HQ, DQK, generator=g)
+    k = torch.randn(B, SK, HKV, DQK, generator=g)
+    v = torch.randn(B, SK, HKV, DV, generator=g)
+    do = torch.randn(B, SQ, HQ, DV, generator=g)
+    ref = {}
+    for kind, f in (("true", true64), ("naive", naive64)):
+        dq, dk, dv = oracle.bshd_backward(f(q), f(k), f(v), f(do), SCALE, SEGS, 0, True)
+        ref[kind] = dict(dq=dq, dk=dk, dv=dv)
+    d = dev()
+    qi, ki, vi, doi = (x.to(torch.bfloat16).to(d) for x in (q, k, v, do))
+    say("fwd for backward-path tests")
+    o, lse = cpa.forward(qi, ki, vi, scale=SCALE, q_segments=SEGS)
+    torch.cuda.synchronize()
+    return dict(q=qi, k=ki, v=vi, do=doi, o=o, lse=lse, ref=ref)
+
+
+def _outputs(p):
+    return (torch.empty_like(p["q"]), torch.empty_like(p["k"]),
+            torch.empty(p["v"].shape, dtype=torch.bfloat16, device=p["q"].device))
+
+
+def _run(p, ws=None, flags=0, stream=None):
+    dq, dk, dv = _outputs(p)
+    cpa.attn_bwd(p["q"], p["k"], p["v"], p["o"], p["do"], p["lse"], dq, dk, dv, scale=SCALE,
+                 q_segments=SEGS, workspace=ws, flags=flags, stream=stream)
+    return dq, dk, dv
+
+
+def _check(p, dq, dk, dv, tag):
+    torch.cuda.synchronize()
+    log = {}
+    for name, val in (("dq", dq), ("dk", dk), ("dv", dv)):
+        criteria.check(f"{tag}:{name}", val, p["ref"]["true"][name], p["ref"]["naive"][name],
+                       grad=True, out_bf16=True, log=log)
+    print(tag, {k_: round(v_["ratio"], 3) for k_, v_ in log.items()})
+
+
+def _bits(x):
+    return x.view(torch.int16)
+
+
+def test_deterministic_flag_is_bitwise_reproducible(problem):
+    p = problem
+    say("bwd deterministic x20")
+    first = _run(p, flags=DETERMINISTIC)
+    _check(p, *first, "deterministic")
+    for _ in range(19):
+        again = _run(p, flags=DETERMINISTIC)
+        for a, b in zip(first, again):
+            assert torch.equal(_bits(a), _bits(b))
+    side = torch.cuda.Stream()
+    say("bwd deterministic on a side stream")
+    with torch.cuda.stream(side):
+        other = _run(p, flags=DETERMINISTIC, stream=side)
+    side.synchronize()
+    for a, b in zip(first, other):
+        assert torch.equal(_bits(a), _bits(b))
+
+
+def test_banded_workspace(problem):
+    p = problem
+    full = cpa.bwd_workspace_bytes(p["q"], p["k"], p["v"])
+    least = cpa.bwd_workspace_bytes(p["q"], p["k"], p["v"], minimum=True)
+    block = (full - least) // 7                 # 8 key blocks of 128
+    assert full - least == 7 * block and block == HQ * (SQ // 64) * 64 * 128 * 2
+    dev_ = p["q"].device
+    results = {}
+    for nblocks in (8, 3, 1):
+        size = least + (nblocks - 1) * block
+        ws = torch.empty(size, dtype=torch.uint8, device=dev_)
+        say(f"bwd with room for {nblocks} dS key blocks")
+        results[nblocks] = _run(p, ws=ws)
+        _check(p, *results[nblocks], f"bands_of_{nblocks}")
+    for nb in (3, 1):
+        assert torch.equal(_bits(results[8][1]), _bits(results[nb][1]))   # dK
+        assert torch.equal(_bits(results[8][2]), _bits(results[nb][2]))   # dV
+
+
+def test_ring_step_backward(problem):
+    """pre once, main + dq per key block (384, 384, 256 keys), post once."""
+    p = problem
+    blocks = [(0, 384), (384, 768), (768, 1024)]
+    dq, dk, dv = _outputs(p)
+    ws_bytes = max(cpa.bwd_workspace_bytes(p["q"], p["k"][:, a:b], p["v"][:, a:b])
+                   for a, b in blocks)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=p["q"].device)
+    common = dict(scale=SCALE, q_segments=SEGS, workspace=ws)
+
+    def call(step, a, b):
+        cpa.attn_bwd(p["q"], p["k"][:, a:b], p["v"][:, a:b], p["o"], p["do"], p["lse"], dq,
+                     dk[:, a:b], dv[:, a:b], k_pos_begin=a, step=step, **common)
+
+    say("ring-step bwd: pre")
+    call("attn_bwd_pre", *blocks[0])
+    for a, b in blocks:
+        say(f"ring-step bwd: main + dq keys [{a}, {b})")
+        call("attn_bwd_main", a, b)
+        call("attn_bwd_dq", a, b)
+    say("ring-step bwd: post")
+    call("attn_bwd_post", *blocks[-1])
+    _check(p, dq, dk, dv, "ring_step")
