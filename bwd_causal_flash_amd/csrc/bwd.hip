@@ -469,22 +469,40 @@ struct KvSmem {
   static constexpr int BN = 128, BM = 64;
   static constexpr int QP = lds_pitch(DQK), OP = lds_pitch(DV);
   static constexpr int KP = row_pitch(DQK), VP = row_pitch(DV), TP = lds_pitch(32);
-  static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = K_OFF + BN * KP * 2;
-  static constexpr int Q_OFF = V_OFF + BN * VP * 2;
+  // The per-tile arrays come first, so that their offsets fit the 16-bit
+  // immediate of the LDS instructions; K and V are read through per-lane
+  // bases that stay fixed for the whole kernel.
+  static constexpr int Q_OFF = 0;
   static constexpr int O_OFF = Q_OFF + BM * QP * 2;
-  static constexpr int T_OFF = O_OFF + BM * OP * 2;
-  static constexpr int L_OFF = T_OFF + 8 * 32 * TP * 2;
+  static constexpr int L_OFF = O_OFF + BM * OP * 2;
   static constexpr int D_OFF = L_OFF + BM * 4;
   static constexpr int P_OFF = D_OFF + BM * 4;
-  static constexpr int BYTES = P_OFF + BM * 4;
+  static constexpr int T_OFF = P_OFF + BM * 4;
+  static constexpr int K_OFF = T_OFF + 8 * 32 * TP * 2;
+  static constexpr int V_OFF = K_OFF + BN * KP * 2;
+  static constexpr int BYTES = V_OFF + BN * VP * 2;
   // epilogue: one wave's partial accumulators per key group, fp32
   static constexpr int RED_BYTES = 4 * DV / 32 * 16 * 64 * 4;
-  static_assert(BYTES <= 160 * 1024 && RED_BYTES <= T_OFF, "LDS budget");
+  static_assert(BYTES <= 160 * 1024 && RED_BYTES <= BYTES, "LDS budget");
+  static_assert(T_OFF <= 65536, "per-tile arrays within the immediate range");
 };
 
 // Write a key's accumulated row (dK^T or dV^T layout: lane = key column,
 // element v = dimension 8*(v/4) + 4*hh + v%4 of each 32-wide block) times mul.
+// Workgroups go to the 8 XCDs round-robin in launch order, and each XCD
+// has its own L2.  Re-deal a (x, y) grid slice so that XCD c runs the
+// contiguous range [c*N/8, (c+1)*N/8) of x-major indices: the workgroups
+// that run together on one XCD then share x (the head) and take
+// neighbouring y.  (Slices whose size is not a multiple of 8 are dealt in
+// plain x-major order.)
+__device__ __forceinline__ void xcd_remap(int& x, int& y) {
+  const int gx = gridDim.x, gy = gridDim.y, n = gx * gy;
+  const int l = blockIdx.x + gx * blockIdx.y;
+  const int t = (n % 8 == 0) ? (l % 8) * (n / 8) + l / 8 : l;
+  x = t / gy;
+  y = t % gy;
+}
+
 template <int ND, typename TOut>
 __device__ __forceinline__ void store_key_acc(const f32x16 (&acc)[ND], TOut* o, int hh, float mul) {
 #pragma unroll
@@ -528,8 +546,9 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   const int kg = wave & 3, qh = wave >> 2;
   bf16* Ts = reinterpret_cast<bf16*>(smem + L::T_OFF);
   bf16* Tw = Ts + wave * 32 * TP;
-  const int kvh = blockIdx.x;
-  const int kt = a.kt0 + (int)blockIdx.y;
+  int kvh, kt;
+  xcd_remap(kvh, kt);
+  kt += a.kt0;
   const int z = blockIdx.z;
   const Seq s = load_seq(a, z);
   const int j0 = kt * BN;
@@ -575,8 +594,9 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
     qpos_range(a, s, i0, min(i0 + BM, s.qlen), lo, hi);
     return hi >= gkpos_lo;
   };
-  const int rot = (int)(((int64_t)kt * 37) % (total > 0 ? total : 1));
-  auto tile_of = [&](int k) -> int { return k + rot < total ? k + rot : k + rot - total; };
+  // Every workgroup walks the query tiles in the same order, so the ones
+  // that run together on an XCD read each Q / dO tile while it is in L2.
+  auto tile_of = [&](int k) -> int { return k; };
   auto next_visible = [&](int k) -> int {
     while (k < total && !visible(tile_of(k))) ++k;
     return k;
@@ -652,14 +672,31 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
       f32x16 sacc, pacc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
-#pragma unroll 4
-      for (int ks = 0; ks < KSQ; ++ks)
-        sacc = mfma32(lds_row8(Qs, QP, qh * 32 + pr, ks * 16 + hh * 8),
-                      lds_row8(Ks, KP, kg * 32 + lq, ks * 16 + hh * 8), sacc);
-#pragma unroll 4
-      for (int ks = 0; ks < KSV; ++ks)
-        pacc = mfma32(lds_row8(dOs, OP, qh * 32 + pr, ks * 16 + hh * 8),
-                      lds_row8(Vs, VP, kg * 32 + lq, ks * 16 + hh * 8), pacc);
+      // S and dP as two interleaved chains; the operands of step i + AHEAD
+      // are read before the products of step i.
+      {
+        constexpr int NS = KSQ > KSV ? KSQ : KSV, AHEAD = 2;
+        bf16x8 qa[NS], kb[NS], oa[NS], vb[NS];
+        auto rd = [&](int i) {
+          if (i < KSQ) {
+            qa[i] = lds_row8(Qs, QP, qh * 32 + pr, i * 16 + hh * 8);
+            kb[i] = lds_row8(Ks, KP, kg * 32 + lq, i * 16 + hh * 8);
+          }
+          if (i < KSV) {
+            oa[i] = lds_row8(dOs, OP, qh * 32 + pr, i * 16 + hh * 8);
+            vb[i] = lds_row8(Vs, VP, kg * 32 + lq, i * 16 + hh * 8);
+          }
+        };
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i) rd(i);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          if (i + AHEAD < NS) rd(i + AHEAD);
+          if (i < KSQ) sacc = mfma32(qa[i], kb[i], sacc);
+          if (i < KSV) pacc = mfma32(oa[i], vb[i], pacc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       // Prefetch the next tile only now: its staging registers are then not
       // live during the S and dP products, where the pressure peaks.
       if (kn < total) fetch(tile_of(kn));
@@ -685,20 +722,34 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
           pacc[v] = p * (pacc[v] - dr[e]);
         }
       }
+      bf16x8 wp[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const int k0 = 32 * qh + 16 * tt + 8 * (grp >> 1);
-        bf16x8 wp, wd;
+        bf16x8 wd;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          wp[e] = (bf16)sacc[8 * tt + e];
+          wp[tt][e] = (bf16)sacc[8 * tt + e];
           wd[e] = (bf16)pacc[8 * tt + e];
         }
-#pragma unroll
-        for (int db = 0; db < NDV; ++db)
-          accv[db] = mfma32(lds_tr8(dOs, OP, k0, db * 32 + 16 * (grp & 1), gl), wp, accv[db]);
         // dS^T block of this wave: row = key, column = query row (natural order)
         *reinterpret_cast<bf16x8*>(&Tw[lq * TP + 16 * tt + 8 * hh]) = wd;
+      }
+      // dV^T += dO^T P over the wave's 32 query rows, operands 2 steps ahead.
+      {
+        constexpr int N = 2 * NDV, AHEAD = 2;
+        bf16x8 oa[N];
+        auto rd = [&](int i) {
+          const int tt = i / NDV, db = i % NDV;
+          oa[i] = lds_tr8(dOs, OP, 32 * qh + 16 * tt + 8 * (grp >> 1), db * 32 + 16 * (grp & 1), gl);
+        };
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i) rd(i);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          if (i + AHEAD < N) rd(i + AHEAD);
+          accv[i % NDV] = mfma32(oa[i], wp[i / NDV], accv[i % NDV]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     } else {
       if (kn < total) fetch(tile_of(kn));
@@ -715,14 +766,21 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
     for (int qq = 0; qq < 2; ++qq) {
       if (!on[qq]) continue;
       const bf16* Tq = Ts + (kg + 4 * qq) * 32 * TP;
+      const bf16x8 wd[2] = {lds_row8(Tq, TP, lq, 8 * hh), lds_row8(Tq, TP, lq, 16 + 8 * hh)};
+      constexpr int N = 2 * NDKH, AHEAD = 2;
+      bf16x8 qa[N];
+      auto rd = [&](int i) {
+        const int tt = i / NDKH, j = i % NDKH;
+        qa[i] = lds_tr8(Qs, QP, 32 * qq + 16 * tt + 8 * (grp >> 1),
+                        (qh * NDKH + j) * 32 + 16 * (grp & 1), gl);
+      };
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int k0 = 32 * qq + 16 * tt + 8 * (grp >> 1);
-        const bf16x8 wd = lds_row8(Tq, TP, lq, 16 * tt + 8 * hh);
+      for (int i = 0; i < AHEAD; ++i) rd(i);
 #pragma unroll
-        for (int j = 0; j < NDKH; ++j)
-          acck[j] = mfma32(lds_tr8(Qs, QP, k0, (qh * NDKH + j) * 32 + 16 * (grp & 1), gl), wd,
-                           acck[j]);
+      for (int i = 0; i < N; ++i) {
+        if (i + AHEAD < N) rd(i + AHEAD);
+        acck[i % NDKH] = mfma32(qa[i], wd[i / NDKH], acck[i % NDKH]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // This wave's two dS chunks for the dQ step (zeros when the half is off).
