@@ -190,8 +190,12 @@ int64_t ds_key_blocks(const cpa_problem* p) {
 size_t ds_block_bytes(const cpa_problem* p) {
   return (size_t)p->heads_q * (size_t)ds_tile_rows(p) * kDsTileBytes;
 }
+size_t tile_pos_bytes(const cpa_problem* p) {
+  if (!cpa::bwd_uses_ds(p->d_qk, p->d_v)) return 0;
+  return align_up((size_t)ds_tile_rows(p) * 16);
+}
 size_t bwd_base_bytes(const cpa_problem* p) {
-  return kAlign + bwd_delta_bytes(p) + bwd_acc_bytes(p);
+  return kAlign + bwd_delta_bytes(p) + bwd_acc_bytes(p) + tile_pos_bytes(p);
 }
 
 void set_bwd_ws(AttnArgs& a, const cpa_problem* p, void* ws, size_t ws_bytes) {
@@ -205,6 +209,7 @@ void set_bwd_ws(AttnArgs& a, const cpa_problem* p, void* ws, size_t ws_bytes) {
   a.acc_stride[0] = a.thd ? 0 : d.rows_q * p->heads_q * p->d_qk;
   a.acc_stride[1] = (int64_t)p->heads_q * p->d_qk;
   a.acc_stride[2] = p->d_qk;
+  a.tile_pos = base + kAlign + bwd_delta_bytes(p) + bwd_acc_bytes(p);
   a.ds = nullptr;
   a.ds_nu = 0;
   a.ds_nb = 0;

@@ -461,6 +461,31 @@ __device__ __forceinline__ int64_t ds_ubase(const AttnArgs& a, const Seq& s, int
   return a.thd ? s.q_row0 / 64 + z : (int64_t)z * ((a.seqlen_q + 63) / 64);
 }
 
+// Query positions of each 64-row tile of a sequence, per 32-row half (min,
+// max; an empty half has lo = INT32_MAX, hi = INT32_MIN), at the tile's dS
+// row index.  Written once by the pre step for the key-outer kernel.
+struct TilePos {
+  int lo0, hi0, lo1, hi1;
+};
+
+__global__ __launch_bounds__(64) void bwd_tiles_kernel(const AttnArgs a) {
+  const int z = blockIdx.z;
+  const Seq s = load_seq(a, z);
+  const int ut = blockIdx.x * 64 + threadIdx.x;
+  if (ut * 64 >= s.qlen) return;
+  TilePos e;
+  int* f = &e.lo0;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int r0 = ut * 64 + 32 * hf, r1 = min(r0 + 32, s.qlen);
+    int lo = INT32_MAX, hi = INT32_MIN;
+    if (r0 < r1) qpos_range(a, s, r0, r1, lo, hi);
+    f[2 * hf] = lo;
+    f[2 * hf + 1] = hi;
+  }
+  reinterpret_cast<TilePos*>(a.tile_pos)[ds_ubase(a, s, z) + ut] = e;
+}
+
 // Row pitch for bf16 tiles read only along rows (16-byte reads): P/8 odd.
 constexpr int row_pitch(int d) { return (d / 8) % 2 ? d + 16 : d + 8; }
 
@@ -586,62 +611,65 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
 
   const int pr = perm32(lq);
   const int nqt = (s.qlen + BM - 1) / BM;
-  const int total = a.group * nqt;
-  auto visible = [&](int u) -> bool {
-    if (!a.causal) return true;
-    const int i0 = (u % nqt) * BM;
-    int lo, hi;
-    qpos_range(a, s, i0, min(i0 + BM, s.qlen), lo, hi);
-    return hi >= gkpos_lo;
+  bf16* const ds = static_cast<bf16*>(a.ds);
+  const int64_t ubase = ds_ubase(a, s, z);
+  // Query positions of the sequence's 64-row tiles (min and max of each
+  // 32-row half), written by the pre step; uniform scalar loads.
+  // (constant address space: the table is not written during this kernel,
+  // so the uniform reads become scalar loads)
+  typedef const __attribute__((address_space(4))) int* ConstInt;
+  const ConstInt tpos = (ConstInt)(uintptr_t)a.tile_pos + 4 * ubase;
+  auto tile_hi = [&](int ut) -> int {
+    const int h0 = tpos[4 * ut + 1], h1 = tpos[4 * ut + 3];
+    return h0 > h1 ? h0 : h1;
   };
-  // Every workgroup walks the query tiles in the same order, so the ones
-  // that run together on an XCD read each Q / dO tile while it is in L2.
-  auto tile_of = [&](int k) -> int { return k; };
-  auto next_visible = [&](int k) -> int {
-    while (k < total && !visible(tile_of(k))) ++k;
-    return k;
+  // Next (query head, tile) at or after (hg, ut) whose tile sees a key of
+  // the block.  Every workgroup walks the tiles in the same order, so the
+  // ones that run together on an XCD read each Q / dO tile while it is in L2.
+  auto seek = [&](int& hg, int& ut) {
+    while (hg < a.group) {
+      if (a.causal)
+        while (ut < nqt && tile_hi(ut) < gkpos_lo) ++ut;
+      if (ut < nqt) return;
+      ++hg;
+      ut = 0;
+    }
   };
 
   TileStage<BM, DQK, TIn, NT> qst;
   TileStage<BM, DV, TIn, NT> dost;
   float pre_l = 0.f, pre_d = 0.f;
   int pre_p = 0;
-  auto fetch = [&](int u) {
-    const int h = kvh * a.group + u / nqt;
-    const int i0 = (u % nqt) * BM;
-    const int64_t qb = (a.thd ? s.q_row0 * a.q_stride[1] : (int64_t)z * a.q_stride[0]) +
-                       (int64_t)h * a.q_stride[2];
-    const int64_t dob = (a.thd ? s.q_row0 * a.do_stride[1] : (int64_t)z * a.do_stride[0]) +
-                        (int64_t)h * a.do_stride[2];
-    qst.load(Q + qb, a.q_stride[1], i0, s.qlen, tid);
-    dost.load(dO + dob, a.do_stride[1], i0, s.qlen, tid);
+  const int64_t qseq = a.thd ? s.q_row0 * a.q_stride[1] : (int64_t)z * a.q_stride[0];
+  const int64_t oseq = a.thd ? s.q_row0 * a.do_stride[1] : (int64_t)z * a.do_stride[0];
+  const int64_t lseq = a.thd ? s.q_row0 : (int64_t)z * a.lse_stride[0];
+  const int64_t dseq = a.thd ? s.q_row0 : (int64_t)z * a.delta_stride[0];
+  auto fetch = [&](int hg, int ut) {
+    const int h = kvh * a.group + hg;
+    const int i0 = ut * BM;
+    qst.load(Q + qseq + (int64_t)h * a.q_stride[2], a.q_stride[1], i0, s.qlen, tid);
+    dost.load(dO + oseq + (int64_t)h * a.do_stride[2], a.do_stride[1], i0, s.qlen, tid);
     if (tid < BM) {
       const int i = i0 + tid;
       const bool ok = i < s.qlen;
-      const int64_t lb = (a.thd ? s.q_row0 : (int64_t)z * a.lse_stride[0]) +
-                         (int64_t)h * a.lse_stride[1];
-      const int64_t db = (a.thd ? s.q_row0 : (int64_t)z * a.delta_stride[0]) +
-                         (int64_t)h * a.delta_stride[1];
       // raw values only: converting here would wait for the loads at once
-      pre_l = ok ? a.lse[lb + i] : -kInf;
-      pre_d = ok ? a.delta[db + i] : 0.f;
+      pre_l = ok ? a.lse[lseq + (int64_t)h * a.lse_stride[1] + i] : -kInf;
+      pre_d = ok ? a.delta[dseq + (int64_t)h * a.delta_stride[1] + i] : 0.f;
       pre_p = qpos(a, s, i);
     }
   };
 
-  bf16* const ds = static_cast<bf16*>(a.ds);
-  const int64_t ubase = ds_ubase(a, s, z);
   // this lane's 16 bytes of the wave's first chunk (qb2 = qh, t = 2*kg)
   const int64_t chunk_off = ((int64_t)(qh * 8 + 2 * kg) * 64 + lane) * 8;
 
-  int k = next_visible(0);
-  if (k < total) fetch(tile_of(k));
-  while (k < total) {
-    const int u = tile_of(k);
-    const int h = kvh * a.group + u / nqt;
-    const int ut = u % nqt;
+  int hg = 0, ut = 0;
+  seek(hg, ut);
+  if (hg < a.group) fetch(hg, ut);
+  while (hg < a.group) {
+    const int h = kvh * a.group + hg;
     const int i0 = ut * BM;
     const int i1 = min(i0 + BM, s.qlen);
+    const TilePos tp = {tpos[4 * ut], tpos[4 * ut + 1], tpos[4 * ut + 2], tpos[4 * ut + 3]};
     __syncthreads();
     qst.store(Qs, QP, tid);
     dost.store(dOs, OP, tid);
@@ -650,22 +678,16 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
       Dl[tid] = pre_d;
       Ps[tid] = pre_p;
     }
-    const int kn = next_visible(k + 1);
+    int nhg = hg, nut = ut + 1;
+    seek(nhg, nut);
     __syncthreads();
 
     // Query halves: rows [i0 + 32*qq, +32) of the tile, handled by waves
     // (kg, qq); a half with no visible (row, key) pair skips its products
     // and contributes dS = 0.
-    bool on[2];
-    int wlo = 0;
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      const int r0 = i0 + qq * 32;
-      int lo = 0, hi = -1;
-      if (r0 < i1) qpos_range(a, s, r0, min(r0 + 32, i1), lo, hi);
-      on[qq] = wave_has_keys && r0 < i1 && (!a.causal || hi >= wkpos_lo);
-      if (qq == qh) wlo = lo;
-    }
+    const bool on[2] = {wave_has_keys && i0 < i1 && (!a.causal || tp.hi0 >= wkpos_lo),
+                        wave_has_keys && i0 + 32 < i1 && (!a.causal || tp.hi1 >= wkpos_lo)};
+    const int wlo = qh ? tp.lo1 : tp.lo0;
     const bool wave_on = on[qh];
     const bool need_mask = (jw + 32 > s.klen) || (a.causal && wlo < wkpos_hi);
     if (wave_on) {
@@ -699,7 +721,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
       }
       // Prefetch the next tile only now: its staging registers are then not
       // live during the S and dP products, where the pressure peaks.
-      if (kn < total) fetch(tile_of(kn));
+      if (nhg < a.group) fetch(nhg, nut);
       // This lane's 16 rows are two runs of 8: qh*32 + 16*vh + 8*hh + e.
 #pragma unroll
       for (int vh = 0; vh < 2; ++vh) {
@@ -752,7 +774,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
         }
       }
     } else {
-      if (kn < total) fetch(tile_of(kn));
+      if (nhg < a.group) fetch(nhg, nut);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
         *reinterpret_cast<bf16x8*>(&Tw[lq * TP + 16 * tt + 8 * hh]) = zero8();
@@ -790,7 +812,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
     for (int j = 0; j < 2; ++j)
       *reinterpret_cast<bf16x8*>(dst + 512 * j) =
           lds_tr8(Tw, TP, 16 * j + 8 * (grp >> 1), 16 * (grp & 1), gl);
-    k = kn;
+    hg = nhg;
+    ut = nut;
   }
 
   // dK: each wave holds complete sums for its column blocks.  dV: the two
@@ -939,6 +962,10 @@ static hipError_t bwd_variant(const AttnArgs& a, int step, hipStream_t st) {
     const int64_t pairs = (int64_t)qrows * a.heads_q;
     dim3 g((unsigned)((pairs + PB - 1) / PB), 1, a.nseq);
     hipLaunchKernelGGL((bwd_pre_kernel<DV, DQK, TIn>), g, dim3(256), 0, st, a);
+    if constexpr (C::DS_PATH) {
+      const int qtiles = (qrows + 63) / 64;
+      hipLaunchKernelGGL(bwd_tiles_kernel, dim3((qtiles + 63) / 64, 1, a.nseq), dim3(64), 0, st, a);
+    }
   }
   if (step == 1 && krows > 0) {
     if constexpr (C::DS_PATH) {

@@ -23,6 +23,7 @@ struct AttnArgs {
   void* dv;
   float* dq_acc;      // bwd workspace: fp32 [rows][heads_q][d_qk]
   void* ds;           // bwd workspace: bf16 dS tiles (small head dims)
+  void* tile_pos;     // bwd workspace: query positions per dS tile row
   int64_t ds_nu;      // dS tile rows per query head
   int ds_nb;          // key blocks per dS band
   int kt0;            // first key block of the band

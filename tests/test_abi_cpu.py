@@ -93,9 +93,10 @@ def test_argument_errors_are_rejected_before_launch():
     assert not bad, bad
     assert res["pack_size_invalid_is_zero"][1] == 0
     assert res["pack_size_valid"][1] % 256 == 0 and res["pack_size_valid"][1] > 0
-    # flag + D + fp32 dQ accumulator, then dS tiles: 4 heads x 4 query tiles
-    # x 16 KiB per 128-key block; the problem has 256 keys = 2 blocks.
-    base = 256 + 4 * 256 * 4 + 256 * 4 * 128 * 4
+    # flag + D + fp32 dQ accumulator + query-tile position table (4 tiles x
+    # 16 B, padded to 256), then dS tiles: 4 heads x 4 query tiles x 16 KiB
+    # per 128-key block; the problem has 256 keys = 2 blocks.
+    base = 256 + 4 * 256 * 4 + 256 * 4 * 128 * 4 + 256
     block = 4 * 4 * 64 * 128 * 2
     assert res["bwd_workspace_min_bytes"][1] == base + block
     assert res["bwd_workspace_bytes"][1] == base + 2 * block
