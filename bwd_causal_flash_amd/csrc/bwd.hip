@@ -883,8 +883,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   const TIn* K = static_cast<const TIn*>(a.k);
   const int64_t kbase = (a.thd ? s.k_row0 * a.k_stride[1] : (int64_t)z * a.k_stride[0]) +
                         (int64_t)kvh * a.k_stride[2];
+  // (waves past the sequence's last tile read that tile and discard it)
+  const int nqt = (s.qlen + 63) / 64;
+  const int utc = ut < nqt ? ut : nqt - 1;
   const bf16* dsw = static_cast<const bf16*>(a.ds) +
-                    ((int64_t)h * a.ds_nu + ds_ubase(a, s, z) + ut) * a.ds_nb * kDsTileElems +
+                    ((int64_t)h * a.ds_nu + ds_ubase(a, s, z) + utc) * a.ds_nb * kDsTileElems +
                     ((int64_t)qb2 * 8 * 64 + lane) * 8;
   auto load_frags = [&](int kt, bf16x8* f) {
     const bf16* p = dsw + (int64_t)(kt - a.kt0) * kDsTileElems;
@@ -898,18 +901,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[d][v] = 0.f;
 
-  TileStage<BN, DQK, TIn, NT> kst;
-  bf16x8 fr[8], nfr[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) nfr[t] = zero8();
+  // Two fragment buffers used in turn (no register copy between
+  // iterations, which would force a wait for the prefetched loads).
+  TileStage<BN, DQK, TIn, NT, true> kst;
+  bf16x8 fa[8], fb[8];
+  // The next block's fragments are loaded even when this wave will not use
+  // them (same tile buffer, in range), so every wave has the same loads in
+  // flight and the wait before staging K covers only K.
   kst.load(K + kbase, a.k_stride[1], kt_begin * BN, s.klen, tid);
-  if (kt_begin <= my_last) load_frags(kt_begin, fr);
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
+  load_frags(kt_begin, fa);
+  auto body = [&](int kt, const bf16x8 (&cur)[8], bf16x8 (&nxt)[8]) {
     __syncthreads();
     kst.store(Ks, KP, tid);
     if (kt + 1 < kt_end) {
       kst.load(K + kbase, a.k_stride[1], (kt + 1) * BN, s.klen, tid);
-      if (kt + 1 <= my_last) load_frags(kt + 1, nfr);
+      load_frags(kt + 1, nxt);
     }
     __syncthreads();
     if (kt <= my_last) {
@@ -917,24 +923,36 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
       for (int t = 0; t < 8; ++t)
 #pragma unroll
         for (int db = 0; db < NDK; ++db)
-          acc[db] = mfma32(fr[t], lds_tr8(Ks, KP, 16 * t + 8 * (grp >> 1),
-                                          db * 32 + 16 * (grp & 1), gl), acc[db]);
+          acc[db] = mfma32(cur[t], lds_tr8(Ks, KP, 16 * t + 8 * (grp >> 1),
+                                           db * 32 + 16 * (grp & 1), gl), acc[db]);
     }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) fr[t] = nfr[t];
+  };
+  for (int kt = kt_begin; kt < kt_end; kt += 2) {
+    body(kt, fa, fb);
+    if (kt + 1 < kt_end) body(kt + 1, fb, fa);
   }
   if (my_last < kt_begin) return;
+  // Accumulator update: all loads, then all stores (the rows are distinct).
   float* accbase = a.dq_acc + (a.thd ? s.q_row0 * a.acc_stride[1] : (int64_t)z * a.acc_stride[0]) +
                    (int64_t)h * a.acc_stride[2] + lq;
   const int64_t rs = a.acc_stride[1];
   const int rbase = ut * 64 + qb2 * 32;
+  float* p0 = accbase + (int64_t)(rbase + 4 * hh) * rs;
+  const bool full = rbase + 32 <= s.qlen;
 #pragma unroll
-  for (int db = 0; db < NDK; ++db)
+  for (int db = 0; db < NDK; ++db) {   // per 32-column block: 16 loads, then 16 stores
+    float old[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int i = rbase + acc_row(v, hh);
-      if (i < s.qlen) accbase[(int64_t)i * rs + db * 32] += acc[db][v];
+      const bool ok = full || rbase + acc_row(v, hh) < s.qlen;
+      old[v] = ok ? p0[(8 * (v >> 2) + (v & 3)) * rs + db * 32] : 0.f;
     }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const bool ok = full || rbase + acc_row(v, hh) < s.qlen;
+      if (ok) p0[(8 * (v >> 2) + (v & 3)) * rs + db * 32] = old[v] + acc[db][v];
+    }
+  }
 }
 
 // ---------------------------------------------------------------- launch

@@ -221,7 +221,12 @@ __device__ __forceinline__ int kpos0(const AttnArgs& a) { return a.thd ? 0 : a.k
 // neighbouring threads read one row's 128 contiguous bytes and every offset
 // is a compile-time immediate.  load() fetches rows [r0, r0+ROWS) of the
 // source (zeros past `limit`), store() writes them to a padded LDS tile.
-template <int ROWS, int D, typename TIn, int NT = 256>
+// CLAMP selects how a tail tile (rows past `limit`) is loaded: with CLAMP,
+// every thread still issues all its loads (rows past the end read the last
+// row and are zeroed afterwards), so the number of loads in flight does not
+// depend on the lane and later waits can stay exact; without it, those rows
+// are skipped.  CLAMP requires limit >= 1.
+template <int ROWS, int D, typename TIn, int NT = 256, bool CLAMP = false>
 struct TileStage {
   static constexpr int RP = NT / 8;   // rows covered per pass
   static constexpr int RI = ROWS / RP, CJ = D / 64;
@@ -242,9 +247,19 @@ struct TileStage {
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
       const int r = r0 + rg + RP * i;
-      const TIn* p = base + (int64_t)r * row_stride + cp;
+      if constexpr (CLAMP) {
+        const int rc = r < limit ? r : limit - 1;
+        const TIn* p = base + (int64_t)rc * row_stride + cp;
 #pragma unroll
-      for (int j = 0; j < CJ; ++j) v[i][j] = r < limit ? Elem<TIn>::load8(p + 64 * j) : zero8();
+        for (int j = 0; j < CJ; ++j) {
+          const bf16x8 x = Elem<TIn>::load8(p + 64 * j);
+          v[i][j] = r < limit ? x : zero8();
+        }
+      } else {
+        const TIn* p = base + (int64_t)r * row_stride + cp;
+#pragma unroll
+        for (int j = 0; j < CJ; ++j) v[i][j] = r < limit ? Elem<TIn>::load8(p + 64 * j) : zero8();
+      }
     }
   }
   // Direct copy with few registers live (at most two chunks in flight).

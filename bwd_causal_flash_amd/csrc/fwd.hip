@@ -91,8 +91,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(const AttnArgs a) {
 
   // K/V tiles go global -> registers -> LDS; tile t+1 is fetched while
   // tile t is being computed.
-  TileStage<BN, DQK, TIn> kst;
-  TileStage<BN, DVC, TIn> vst;
+  TileStage<BN, DQK, TIn, 256, true> kst;   // limit = klen >= 1 when ntiles > 0
+  TileStage<BN, DVC, TIn, 256, true> vst;
   if (ntiles > 0) {
     kst.load(Kb, a.k_stride[1], 0, s.klen, tid);
     vst.load(Vb, a.v_stride[1], 0, s.klen, tid);
