@@ -36,6 +36,10 @@ if ROOT not in sys.path:
 
 METRIC = "causal attn fwd+bwd ms & TFLOP/s (BF16, % MFMA peak), 32K-seq CP4 rank shape"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_kv_kernel_cp4_rank_traffic.md")
+KERNEL_SOURCES = ("bwd_causal_flash_amd/csrc/bwd.hip", "bwd_causal_flash_amd/csrc/device_common.h",
+                  "bwd_causal_flash_amd/csrc/internal.h")
+COPY_BYTES = 512 << 20        # calibration copy: reads and writes this many bytes
 
 
 def visible_pairs(q_positions, n_keys):
@@ -52,6 +56,33 @@ def flops(nvis, heads, dqk, dv):
 def kv_kernel_flops(nvis, heads, dqk, dv):
     """S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q."""
     return 2.0 * nvis * (2 * dqk + 2 * dv) * heads
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the key-outer backward kernel, from the
+    committed rocprofv3 counter summary, or None when that summary is
+    missing or was taken on different kernel sources."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if ":" in line and line.strip().startswith(("source_sha256", "traffic_bytes_per_launch")):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip().strip("`")
+        if fields.get("source_sha256") != kernel_source_hash():
+            return None
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, x, qpos):
@@ -85,6 +116,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true",
                     help="also print per-phase times (stderr)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run a plain elementwise copy of a known size "
+                         "(for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this library "
@@ -145,6 +179,13 @@ def main():
                           "fwd_tflops": round(f_fwd / 1e12, 4),
                           "bwd_tflops": round(f_bwd / 1e12, 4)}), file=sys.stderr)
 
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)    # one elementwise kernel: reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, x, qpos)
     out = {
         "metric": METRIC,
@@ -167,7 +208,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "bwd_kv_kernel<192,128>",
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "avg_launch_ms": round(main_ms, 4), "traffic": None},
+                     "avg_launch_ms": round(main_ms, 4), "traffic": measured_traffic()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
