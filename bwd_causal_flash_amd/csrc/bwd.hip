@@ -805,13 +805,16 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // This wave's two dS chunks for the dQ step (zeros when the half is off).
+    // This wave's two dS chunks for the dQ step (zeros when the half is off),
+    // stored non-temporally: they are read once, by another kernel, and
+    // would otherwise push the query tiles that other workgroups reuse out
+    // of L2.
     bf16* dst = ds + (((int64_t)h * a.ds_nu + ubase + ut) * a.ds_nb + (kt - a.kt0)) *
                          kDsTileElems + chunk_off;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      *reinterpret_cast<bf16x8*>(dst + 512 * j) =
-          lds_tr8(Tw, TP, 16 * j + 8 * (grp >> 1), 16 * (grp & 1), gl);
+      __builtin_nontemporal_store(lds_tr8(Tw, TP, 16 * j + 8 * (grp >> 1), 16 * (grp & 1), gl),
+                                  reinterpret_cast<bf16x8*>(dst + 512 * j));
     hg = nhg;
     ut = nut;
   }
@@ -892,7 +895,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   auto load_frags = [&](int kt, bf16x8* f) {
     const bf16* p = dsw + (int64_t)(kt - a.kt0) * kDsTileElems;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) f[t] = *reinterpret_cast<const bf16x8*>(p + 512 * t);
+    for (int t = 0; t < 8; ++t)   // streamed once: non-temporal, K keeps L2
+      f[t] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p + 512 * t));
   };
 
   f32x16 acc[NDK];
