@@ -24,8 +24,15 @@
 
 namespace cpa {
 
+// Two workgroups per CU where the registers allow it (<= 256 per lane): the
+// second workgroup's waves fill the gaps of the first (their barriers are
+// independent), which the measured kernel time shows to be worth more than
+// the accumulator registers a single workgroup could use.
+template <int DSUM>
+constexpr int fwd_blocks_per_cu() { return DSUM <= 320 ? 2 : 1; }
+
 template <int DQK, int DVC, int NCH, typename TIn, typename TOut>
-__global__ __launch_bounds__(256) void fwd_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kernel(const AttnArgs a) {
   constexpr int BM = 128, BN = 64;
   constexpr int KP = lds_pitch(DQK), VP = lds_pitch(DVC);
   constexpr int KS = DQK / 16;
