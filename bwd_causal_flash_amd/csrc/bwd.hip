@@ -908,19 +908,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   // Two fragment buffers used in turn (no register copy between
   // iterations, which would force a wait for the prefetched loads).
   TileStage<BN, DQK, TIn, NT, true> kst;
-  bf16x8 fa[8], fb[8];
-  // The next block's fragments are loaded even when this wave will not use
-  // them (same tile buffer, in range), so every wave has the same loads in
-  // flight and the wait before staging K covers only K.
+  bf16x8 fa[8], fb[8], fc[8];
   kst.load(K + kbase, a.k_stride[1], kt_begin * BN, s.klen, tid);
   load_frags(kt_begin, fa);
-  auto body = [&](int kt, const bf16x8 (&cur)[8], bf16x8 (&nxt)[8]) {
+  if (kt_begin + 1 < kt_end) load_frags(kt_begin + 1, fb);
+  // dS fragments two blocks ahead (three register sets in turn).
+  auto body = [&](int kt, const bf16x8 (&cur)[8], bf16x8 (&nn)[8]) {
     __syncthreads();
     kst.store(Ks, KP, tid);
-    if (kt + 1 < kt_end) {
-      kst.load(K + kbase, a.k_stride[1], (kt + 1) * BN, s.klen, tid);
-      load_frags(kt + 1, nxt);
-    }
+    if (kt + 1 < kt_end) kst.load(K + kbase, a.k_stride[1], (kt + 1) * BN, s.klen, tid);
+    if (kt + 2 < kt_end) load_frags(kt + 2, nn);
     __syncthreads();
     if (kt <= my_last) {
 #pragma unroll
@@ -931,9 +928,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
                                            db * 32 + 16 * (grp & 1), gl), acc[db]);
     }
   };
-  for (int kt = kt_begin; kt < kt_end; kt += 2) {
-    body(kt, fa, fb);
+  for (int kt = kt_begin; kt < kt_end; kt += 3) {
+    body(kt, fa, fc);
     if (kt + 1 < kt_end) body(kt + 1, fb, fa);
+    if (kt + 2 < kt_end) body(kt + 2, fc, fb);
   }
   if (my_last < kt_begin) return;
   // Accumulator update: all loads, then all stores (the rows are distinct).
