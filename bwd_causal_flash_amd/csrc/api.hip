@@ -173,7 +173,7 @@ size_t bwd_acc_bytes(const cpa_problem* p) {
   return align_up((size_t)(d.nb * d.rows_q * p->heads_q * p->d_qk) * 4);
 }
 
-// dS workspace of the small-head-dim backward: tiles of 64 query rows x 128
+// dS workspace of the backward: tiles of 64 query rows x 128
 // keys (16 KiB, bf16) for every query head, query tile row and key block of
 // a band.  Query tile rows per head: BSHD batch * ceil(S_q / 64); THD
 // ceil(T_q / 64) + num_seqs, which keeps every document's tiles apart
@@ -191,7 +191,6 @@ size_t ds_block_bytes(const cpa_problem* p) {
   return (size_t)p->heads_q * (size_t)ds_tile_rows(p) * kDsTileBytes;
 }
 size_t tile_pos_bytes(const cpa_problem* p) {
-  if (!cpa::bwd_uses_ds(p->d_qk, p->d_v)) return 0;
   return align_up((size_t)ds_tile_rows(p) * 16);
 }
 size_t bwd_base_bytes(const cpa_problem* p) {
@@ -214,13 +213,11 @@ void set_bwd_ws(AttnArgs& a, const cpa_problem* p, void* ws, size_t ws_bytes) {
   a.ds_nu = 0;
   a.ds_nb = 0;
   a.kt0 = 0;
-  if (cpa::bwd_uses_ds(p->d_qk, p->d_v)) {
-    const size_t room = (ws_bytes - bwd_base_bytes(p)) / ds_block_bytes(p);
-    const int64_t nkb = ds_key_blocks(p);
-    a.ds = base + bwd_base_bytes(p);
-    a.ds_nu = ds_tile_rows(p);
-    a.ds_nb = (int)((int64_t)room < nkb ? (int64_t)room : nkb);
-  }
+  const size_t room = (ws_bytes - bwd_base_bytes(p)) / ds_block_bytes(p);
+  const int64_t nkb = ds_key_blocks(p);
+  a.ds = base + bwd_base_bytes(p);
+  a.ds_nu = ds_tile_rows(p);
+  a.ds_nb = (int)((int64_t)room < nkb ? (int64_t)room : nkb);
 }
 
 }  // namespace
@@ -250,14 +247,12 @@ size_t attn_fwd_workspace_size(const cpa_problem* p) {
 
 size_t attn_bwd_workspace_size(const cpa_problem* p) {
   if (check_problem(p) != CPA_OK) return 0;
-  if (!cpa::bwd_uses_ds(p->d_qk, p->d_v)) return bwd_base_bytes(p);
   const int64_t nkb = ds_key_blocks(p);
   return bwd_base_bytes(p) + ds_block_bytes(p) * (size_t)(nkb > 1 ? nkb : 1);
 }
 
 size_t attn_bwd_workspace_min(const cpa_problem* p) {
   if (check_problem(p) != CPA_OK) return 0;
-  if (!cpa::bwd_uses_ds(p->d_qk, p->d_v)) return bwd_base_bytes(p);
   return bwd_base_bytes(p) + ds_block_bytes(p);
 }
 
@@ -305,10 +300,9 @@ cpa_status bwd_prepare(const cpa_problem* p, const void* q, const void* k, const
   cpa_status st = check_problem(p);
   if (st != CPA_OK) return st;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return CPA_ERR_NULL;
+  // The backward has no atomics, so the result is always deterministic and
+  // CPA_FLAG_DETERMINISTIC asks for nothing more.
   if (flags & ~(uint32_t)CPA_FLAG_DETERMINISTIC) return CPA_ERR_UNSUPPORTED;
-  // Only the dS path is free of atomics.
-  if ((flags & CPA_FLAG_DETERMINISTIC) && !cpa::bwd_uses_ds(p->d_qk, p->d_v))
-    return CPA_ERR_UNSUPPORTED;
   if (!strides_ok(p->o_stride, 3) || !strides_ok(p->do_stride, 3) ||
       !strides_ok(p->dq_stride, 3) || !strides_ok(p->dk_stride, 3) ||
       !strides_ok(p->dv_stride, 3))
@@ -359,16 +353,15 @@ cpa_status bwd_run(const cpa_problem* p, const void* q, const void* k, const voi
   AttnArgs a;
   const cpa_status st = bwd_prepare(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, flags, a);
   if (st != CPA_OK) return st;
-  const bool ds = cpa::bwd_uses_ds(p->d_qk, p->d_v);
-  const int64_t nkb = ds ? ds_key_blocks(p) : 0;
-  if (ds && steps != 15 && (steps & 6) && a.ds_nb < nkb) return CPA_ERR_WORKSPACE;
+  const int64_t nkb = ds_key_blocks(p);
+  if (steps != 15 && (steps & 6) && a.ds_nb < nkb) return CPA_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   auto run = [&](int step) {
     return launch_bwd(a, p->d_qk, p->d_v, p->in_dtype, p->out_dtype, step, s) == hipSuccess;
   };
   if ((steps & 1) && launch_meta_check(a, s) != hipSuccess) return CPA_ERR_LAUNCH;
   if ((steps & 1) && !run(0)) return CPA_ERR_LAUNCH;
-  if (ds && a.ds_nb > 0) {
+  if (a.ds_nb > 0) {
     const int nb = a.ds_nb;
     for (int64_t kt0 = 0; kt0 < nkb; kt0 += nb) {
       a.kt0 = (int)kt0;
@@ -376,8 +369,6 @@ cpa_status bwd_run(const cpa_problem* p, const void* q, const void* k, const voi
       if ((steps & 2) && !run(1)) return CPA_ERR_LAUNCH;
       if ((steps & 4) && !run(2)) return CPA_ERR_LAUNCH;
     }
-  } else if (!ds && (steps & 2) && !run(1)) {
-    return CPA_ERR_LAUNCH;
   }
   if ((steps & 8) && !run(3)) return CPA_ERR_LAUNCH;
   return CPA_OK;

@@ -8,8 +8,8 @@
 //   main  key-outer: one workgroup owns 128 keys of one kv head and walks
 //         the query heads of its GQA group and the query tiles that can see
 //         those keys, accumulating dK and dV;
-//   dq    (head dims with D_qk + D_v <= 320) query-outer dQ_acc += dS K from
-//         the dS tiles main stored in the workspace;
+//   dq    query-outer dQ_acc += dS K from the dS tiles main stored in the
+//         workspace (plain read-add-write, no atomics: deterministic);
 //   post  dQ = s * acc, rounded to the output type.
 //
 // Inside main a wave computes S = Q K_w^T and dP = dO V_w^T for its 32 keys
@@ -20,10 +20,10 @@
 // directly from the accumulators because the Q rows were loaded in perm32
 // order.  All products are bf16 x bf16 -> fp32 on the matrix cores.
 //
-// Head dims 256 and 512 run the older single kernel: dQ is added to the
-// fp32 accumulator with atomics, and for 512 dK, dV and dQ are produced in
-// two column chunks of 256 by separate workgroups (S and dP recomputed per
-// chunk) with K_w, V_w read from global memory.
+// Head dims up to D_qk + D_v = 320 run the 8-wave kv kernel below; 256 and
+// 512 run a 4-wave kernel over 32-row query blocks, and for 512 dK and dV
+// are produced in two column chunks of 256 by separate workgroups (S and dP
+// recomputed per chunk) with K_w, V_w read from global memory.
 #include "device_common.h"
 
 namespace cpa {
@@ -110,6 +110,8 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(const AttnArgs a) {
 
 // ---------------------------------------------------------------- main
 
+__device__ __forceinline__ int64_t ds_ubase(const AttnArgs& a, const Seq& s, int z);
+
 template <int DQK, int DV, int OCK, int OCV, int BM, typename TIn, typename TOut>
 __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
   constexpr int BN = 128;
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
   const int kvh = blockIdx.x % a.heads_kv;
   const int ch = blockIdx.x / a.heads_kv;
-  const int kt = blockIdx.y;
+  const int kt = a.kt0 + blockIdx.y;
   const int z = blockIdx.z;
   const Seq s = load_seq(a, z);
   const int j0 = kt * BN;
@@ -186,19 +188,19 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
   const int pr = perm32(lq);
   const int nqt = (s.qlen + BM - 1) / BM;
   const int total = a.group * nqt;
-  // Query tiles whose last position precedes this workgroup's first key see
-  // none of its keys and are skipped (causal tile skipping).
+  // Query blocks whose enclosing 64-row dS tile precedes this workgroup's
+  // first key see none of its keys and are skipped (causal tile skipping).
+  // Visibility is decided per 64-row tile, because the dQ kernel reads whole
+  // tiles: both halves of a visible tile are visited (a half that sees no
+  // key stores zeros).
   auto visible = [&](int u) -> bool {
     if (!a.causal) return true;
-    const int i0 = (u % nqt) * BM;
+    const int t0 = ((u % nqt) * BM) & ~63;
     int lo, hi;
-    qpos_range(a, s, i0, min(i0 + BM, s.qlen), lo, hi);
+    qpos_range(a, s, t0, min(t0 + 64, s.qlen), lo, hi);
     return hi >= gkpos_lo;
   };
-  // Workgroups of one head that run at the same time walk the query tiles
-  // from different starting points, so their dQ atomics hit different rows.
-  const int rot = (int)(((int64_t)kt * 37) % (total > 0 ? total : 1));
-  auto tile_of = [&](int k) -> int { return k + rot < total ? k + rot : k + rot - total; };
+  auto tile_of = [&](int k) -> int { return k; };
   auto next_visible = [&](int k) -> int {
     while (k < total && !visible(tile_of(k))) ++k;
     return k;
@@ -353,35 +355,21 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
     }
     __syncthreads();
 
-    // dQ tile (BM x OCK) = dS (BM x 128 keys) K (128 keys x OCK), split into
-    // 32x32 blocks over the four waves, added to the fp32 accumulator.
-    float* accbase = a.dq_acc +
-                     (a.thd ? s.q_row0 * a.acc_stride[1] : (int64_t)z * a.acc_stride[0]) +
-                     (int64_t)h * a.acc_stride[2] + ch * OCK + lq;
-    const bool full_rows = i0 + BM <= s.qlen;
-    for (int b = wave; b < NQB * NDK; b += 4) {
-      const int qb = b / NDK, db = b % NDK;
-      f32x16 acc;
+    // dS of this 32-row block to the workspace tile (the dQ kernel reduces
+    // it): wave w stores the chunks of keys 32w..32w+31, read transposed from
+    // dS^T in LDS.  Column chunk 0 only (all chunks compute the same dS).
+    static_assert(BM == 32, "dS chunks of 32 query rows");
+    if (ch == 0) {
+      const int ut = i0 >> 6, qb2 = (i0 >> 5) & 1;
+      bf16* dst = static_cast<bf16*>(a.ds) +
+                  (((int64_t)h * a.ds_nu + ds_ubase(a, s, z) + ut) * a.ds_nb + (kt - a.kt0)) *
+                      (64 * 128) +
+                  ((int64_t)(qb2 * 8 + 2 * wave) * 64 + lane) * 8;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-#pragma unroll
-      for (int t = 0; t < BN / 16; ++t) {
-        const int k0 = 16 * t + 8 * (grp >> 1);
-        acc = mfma32(lds_tr8(dSt, SP, k0, qb * 32 + 16 * (grp & 1), gl),
-                     lds_tr8(Ks, KP, k0, db * 32 + 16 * (grp & 1), gl), acc);
-      }
-      float* p0 = accbase + (int64_t)(i0 + qb * 32 + 4 * hh) * a.acc_stride[1] + db * 32;
-      const int64_t rs = a.acc_stride[1];
-      if (full_rows) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) atomicAdd(p0 + (8 * (v >> 2) + (v & 3)) * rs, acc[v]);
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int dr = 8 * (v >> 2) + (v & 3);
-          if (i0 + qb * 32 + 4 * hh + dr < s.qlen) atomicAdd(p0 + dr * rs, acc[v]);
-        }
-      }
+      for (int j = 0; j < 2; ++j)
+        __builtin_nontemporal_store(
+            lds_tr8(dSt, SP, 16 * (2 * wave + j) + 8 * (grp >> 1), 16 * (grp & 1), gl),
+            reinterpret_cast<bf16x8*>(dst + 512 * j));
     }
     k = kn;
   }
@@ -858,15 +846,19 @@ __device__ __forceinline__ int dq_last_block(const AttnArgs& a, const Seq& s, in
   return b < nkb - 1 ? b : nkb - 1;
 }
 
-template <int DQK, typename TIn>
+// DC: dQ columns per workgroup (the whole head dim up to 256; the 512 dim
+// runs two column chunks, each reading the same dS tiles).
+template <int DQK, int DC, typename TIn>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
-  constexpr int BN = 128, NT = 512, NDK = DQK / 32;
-  constexpr int KP = lds_pitch(DQK);
+  constexpr int BN = 128, NT = 512, NDK = DC / 32;
+  constexpr int KP = lds_pitch(DC);
+  static_assert(DQK % DC == 0, "whole column chunks");
   __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
-  const int h = blockIdx.x;
+  const int h = blockIdx.x % a.heads_q;
+  const int c0 = (blockIdx.x / a.heads_q) * DC;
   const int kvh = h / a.group;
   const int z = blockIdx.z;
   const Seq s = load_seq(a, z);
@@ -885,7 +877,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
 
   const TIn* K = static_cast<const TIn*>(a.k);
   const int64_t kbase = (a.thd ? s.k_row0 * a.k_stride[1] : (int64_t)z * a.k_stride[0]) +
-                        (int64_t)kvh * a.k_stride[2];
+                        (int64_t)kvh * a.k_stride[2] + c0;
   // (waves past the sequence's last tile read that tile and discard it)
   const int nqt = (s.qlen + 63) / 64;
   const int utc = ut < nqt ? ut : nqt - 1;
@@ -905,19 +897,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[d][v] = 0.f;
 
-  // Two fragment buffers used in turn (no register copy between
-  // iterations, which would force a wait for the prefetched loads).
-  TileStage<BN, DQK, TIn, NT, true> kst;
-  bf16x8 fa[8], fb[8], fc[8];
+  // dS fragments AHEAD key blocks ahead, in AHEAD + 1 register sets used in
+  // turn (no register copy between iterations, which would force a wait for
+  // the prefetched loads).  Wide column chunks keep one block ahead so the
+  // accumulators fit without spilling.
+  constexpr int AHEAD = NDK > 6 ? 1 : 2;
+  TileStage<BN, DC, TIn, NT, true> kst;
+  bf16x8 fa[8], fb[8], fc[AHEAD == 2 ? 8 : 1];
   kst.load(K + kbase, a.k_stride[1], kt_begin * BN, s.klen, tid);
   load_frags(kt_begin, fa);
-  if (kt_begin + 1 < kt_end) load_frags(kt_begin + 1, fb);
-  // dS fragments two blocks ahead (three register sets in turn).
+  if (AHEAD == 2 && kt_begin + 1 < kt_end) load_frags(kt_begin + 1, fb);
   auto body = [&](int kt, const bf16x8 (&cur)[8], bf16x8 (&nn)[8]) {
     __syncthreads();
     kst.store(Ks, KP, tid);
     if (kt + 1 < kt_end) kst.load(K + kbase, a.k_stride[1], (kt + 1) * BN, s.klen, tid);
-    if (kt + 2 < kt_end) load_frags(kt + 2, nn);
+    if (kt + AHEAD < kt_end) load_frags(kt + AHEAD, nn);
     __syncthreads();
     if (kt <= my_last) {
 #pragma unroll
@@ -928,15 +922,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
                                            db * 32 + 16 * (grp & 1), gl), acc[db]);
     }
   };
-  for (int kt = kt_begin; kt < kt_end; kt += 3) {
-    body(kt, fa, fc);
-    if (kt + 1 < kt_end) body(kt + 1, fb, fa);
-    if (kt + 2 < kt_end) body(kt + 2, fc, fb);
+  if constexpr (AHEAD == 2) {
+    for (int kt = kt_begin; kt < kt_end; kt += 3) {
+      body(kt, fa, fc);
+      if (kt + 1 < kt_end) body(kt + 1, fb, fa);
+      if (kt + 2 < kt_end) body(kt + 2, fc, fb);
+    }
+  } else {
+    for (int kt = kt_begin; kt < kt_end; kt += 2) {
+      body(kt, fa, fb);
+      if (kt + 1 < kt_end) body(kt + 1, fb, fa);
+    }
   }
   if (my_last < kt_begin) return;
   // Accumulator update: all loads, then all stores (the rows are distinct).
   float* accbase = a.dq_acc + (a.thd ? s.q_row0 * a.acc_stride[1] : (int64_t)z * a.acc_stride[0]) +
-                   (int64_t)h * a.acc_stride[2] + lq;
+                   (int64_t)h * a.acc_stride[2] + c0 + lq;
   const int64_t rs = a.acc_stride[1];
   const int rbase = ut * 64 + qb2 * 32;
   float* p0 = accbase + (int64_t)(rbase + 4 * hh) * rs;
@@ -961,14 +962,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
 
 template <int DQK, int DV>
 struct BwdCfg {
-  // dS-materialising path (kv + dq kernels) for the small head dims; the
-  // 256/512 dims keep the single key-outer kernel with dQ atomics.
-  static constexpr bool DS_PATH = DQK + DV <= 320;
+  // Key-outer kernel: the 8-wave kv kernel for the small head dims; the
+  // 256/512 dims take the 4-wave kernel with 32-row query blocks (for 512 in
+  // two column chunks of dK, dV).  Both store dS for the dq kernel.
+  static constexpr bool KV_KERNEL = DQK + DV <= 320;
   static constexpr bool BIG = DQK > 256 || DV > 256;
   static constexpr int OCK = BIG ? DQK / 2 : DQK;
   static constexpr int OCV = BIG ? DV / 2 : DV;
   static constexpr int NCH = DQK / OCK;
-  static constexpr int BM = DQK + DV > 320 ? 32 : 64;
+  static constexpr int BM = 32;
+  static constexpr int DQ_COLS = DQK > 256 ? 256 : DQK;
 };
 
 template <int DQK, int DV, typename TIn, typename TOut>
@@ -982,27 +985,25 @@ static hipError_t bwd_variant(const AttnArgs& a, int step, hipStream_t st) {
     const int64_t pairs = (int64_t)qrows * a.heads_q;
     dim3 g((unsigned)((pairs + PB - 1) / PB), 1, a.nseq);
     hipLaunchKernelGGL((bwd_pre_kernel<DV, DQK, TIn>), g, dim3(256), 0, st, a);
-    if constexpr (C::DS_PATH) {
+    if constexpr (C::KV_KERNEL) {
       const int qtiles = (qrows + 63) / 64;
       hipLaunchKernelGGL(bwd_tiles_kernel, dim3((qtiles + 63) / 64, 1, a.nseq), dim3(64), 0, st, a);
     }
   }
   if (step == 1 && krows > 0) {
-    if constexpr (C::DS_PATH) {
+    if constexpr (C::KV_KERNEL) {
       dim3 g(a.heads_kv, a.ds_nb, a.nseq);
       hipLaunchKernelGGL((bwd_kv_kernel<DQK, DV, TIn, TOut>), g, dim3(512), 0, st, a);
     } else {
-      dim3 g(a.heads_kv * C::NCH, (krows + 127) / 128, a.nseq);
+      dim3 g(a.heads_kv * C::NCH, a.ds_nb, a.nseq);
       hipLaunchKernelGGL((bwd_main_kernel<DQK, DV, C::OCK, C::OCV, C::BM, TIn, TOut>), g,
                          dim3(256), 0, st, a);
     }
   }
-  if constexpr (C::DS_PATH) {
-    if (step == 2 && krows > 0 && qrows > 0) {
-      const int qtiles = (qrows + 63) / 64;
-      dim3 g(a.heads_q, (qtiles + 3) / 4, a.nseq);
-      hipLaunchKernelGGL((bwd_dq_kernel<DQK, TIn>), g, dim3(512), 0, st, a);
-    }
+  if (step == 2 && krows > 0 && qrows > 0) {
+    const int qtiles = (qrows + 63) / 64;
+    dim3 g(a.heads_q * (DQK / C::DQ_COLS), (qtiles + 3) / 4, a.nseq);
+    hipLaunchKernelGGL((bwd_dq_kernel<DQK, C::DQ_COLS, TIn>), g, dim3(512), 0, st, a);
   }
   if (step == 3 && qrows > 0) {
     constexpr int PB = 256 / pow2_at_least(DQK / 8);
@@ -1022,7 +1023,7 @@ static hipError_t bwd_dtypes(const AttnArgs& a, int in_dt, int out_dt, int step,
 }
 
 // step 0: D and dQ-accumulator zeroing; 1: key-outer kernel; 2: dQ
-// accumulation from the stored dS (no-op on the atomic path); 3: dQ cast.
+// accumulation from the stored dS; 3: dQ cast.
 hipError_t launch_bwd(const AttnArgs& a, int d_qk, int d_v, int in_dt, int out_dt, int step,
                       hipStream_t st) {
   if (d_qk == 64 && d_v == 64) return bwd_dtypes<64, 64>(a, in_dt, out_dt, step, st);
@@ -1032,7 +1033,5 @@ hipError_t launch_bwd(const AttnArgs& a, int d_qk, int d_v, int in_dt, int out_d
   if (d_qk == 512 && d_v == 512) return bwd_dtypes<512, 512>(a, in_dt, out_dt, step, st);
   return hipErrorInvalidValue;
 }
-
-bool bwd_uses_ds(int d_qk, int d_v) { return d_qk + d_v <= 320; }
 
 }  // namespace cpa

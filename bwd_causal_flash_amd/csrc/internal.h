@@ -88,13 +88,11 @@ struct PackArgs {
 hipError_t launch_fwd(const AttnArgs& a, int d_qk, int d_v, int in_dt,
                       int out_dt, hipStream_t s);
 // step 0: D = rowsum(dO*O) and zeroing of the dQ accumulator; step 1: the
-// key-outer kernel (dK, dV and, on the dS path, the dS tiles of the band);
-// step 2: dQ accumulator += dS K for the band (dS path only); step 3: dQ =
-// s * accumulator in the output dtype.
+// key-outer kernel (dK, dV and the dS tiles of the band); step 2: dQ
+// accumulator += dS K for the band; step 3: dQ = s * accumulator in the
+// output dtype.
 hipError_t launch_bwd(const AttnArgs& a, int d_qk, int d_v, int in_dt,
                       int out_dt, int step, hipStream_t s);
-// Whether a head-dim pair takes the dS-materialising backward.
-bool bwd_uses_ds(int d_qk, int d_v);
 hipError_t launch_meta_check(const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& m, int acc_dt, int part_dt,
                         int out_dt, hipStream_t s);

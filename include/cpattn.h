@@ -158,9 +158,9 @@ cpa_status attn_fwd(const cpa_problem* p, const void* q, const void* k,
                     size_t ws_bytes, cpa_stream_t stream);
 
 /* Bytes of workspace attn_bwd needs (host, pure) for its fastest schedule:
- * the error flag, D = rowsum(dO*O), an fp32 dQ accumulator and, for head
- * dims with d_qk + d_v <= 320, the bf16 dS tiles of the whole key range
- * (16 KiB per query head, 64-row query tile and 128-key block: about
+ * the error flag, D = rowsum(dO*O), an fp32 dQ accumulator, a small table
+ * of query positions per 64-row tile and the bf16 dS tiles of the whole key
+ * range (16 KiB per query head, 64-row query tile and 128-key block: about
  * 2 * heads_q * S_q * S_k bytes).  Same problem -> same size. */
 size_t attn_bwd_workspace_size(const cpa_problem* p);
 
@@ -174,19 +174,18 @@ size_t attn_bwd_workspace_min(const cpa_problem* p);
  * writes dq, dk, dv (out_dtype) for every real row, with exact zeros where a
  * row or key has no visible partner; THD padding rows are untouched.
  *
- * Head dims with d_qk + d_v <= 320 (64/64, 128/128, 192/128): a key-outer
- * kernel writes dK, dV and the bf16 dS tiles; a query-outer kernel then
- * adds dS K into the dQ accumulator with a fixed order and no atomics, so
- * the result is bitwise deterministic and CPA_FLAG_DETERMINISTIC is
- * honoured.  (FlashAttention-2's backward adds dS K to dQ with atomics; on
- * this GPU fp32 atomics retire at about 1.35 TB/s, which would bound the
- * whole backward, so dS is stored and reduced per query tile instead.)
- * Head dims 256 and 512 add dQ with fp32 atomics, so its low bits may vary
- * from run to run (the pages' backward kernels are nondeterministic too,
- * PR 3699), and CPA_FLAG_DETERMINISTIC is declined with
- * CPA_ERR_UNSUPPORTED.  Outputs must not overlap each other or the inputs;
- * ws holds at least attn_bwd_workspace_min(p) bytes (first int32 = THD
- * metadata error flag, as for attn_fwd).
+ * A key-outer kernel writes dK, dV and the bf16 dS tiles; a query-outer
+ * kernel then adds dS K into the dQ accumulator with a fixed order and no
+ * atomics, so at every head dim the result is bitwise deterministic and
+ * CPA_FLAG_DETERMINISTIC (accepted, asks for nothing more) is honoured.
+ * (FlashAttention-2's backward adds dS K to dQ with atomics, and the pages'
+ * backward kernels are nondeterministic, PR 3699; on this GPU fp32 atomics
+ * retire at about 1.35 TB/s, which would bound the whole backward, so dS is
+ * stored and reduced per query tile instead.)  The dK, dV of a workspace
+ * band split are bitwise those of the full workspace; dQ adds the bands in
+ * order, so its rounding depends on the split.  Outputs must not overlap
+ * each other or the inputs; ws holds at least attn_bwd_workspace_min(p)
+ * bytes (first int32 = THD metadata error flag, as for attn_fwd).
  */
 cpa_status attn_bwd(const cpa_problem* p, const void* q, const void* k,
                     const void* v, const void* o, const void* dout,
@@ -202,10 +201,8 @@ cpa_status attn_bwd(const cpa_problem* p, const void* q, const void* k,
  *   attn_bwd_pre   writes the metadata flag, D = rowsum(dO*O) (fp32, from
  *                  the given O) and zeroes the fp32 dQ accumulator;
  *   attn_bwd_main  recomputes P from the LSE, writes dK, dV (to dk, dv) and
- *                  either stores dS in the workspace (d_qk + d_v <= 320) or
- *                  adds dS K to the dQ accumulator with atomics;
- *   attn_bwd_dq    adds dS K for the same key range to the accumulator
- *                  (no-op for head dims 256 and 512);
+ *                  stores dS in the workspace;
+ *   attn_bwd_dq    adds dS K for the same key range to the accumulator;
  *   attn_bwd_post  writes dq = softmax_scale * accumulator.
  * attn_bwd_main followed by attn_bwd_dq may be repeated between one pre and
  * one post, with K/V (and k_pos_begin) of different key blocks, to

@@ -86,12 +86,12 @@ def main():
         return lib.attn_bwd(ctypes.byref(p), ptr(1), ptr(2), ptr(3), ptr(40), ptr(50), ptr(60),
                             ptr(dq), ptr(dk), ptr(dv), ptr(200), wsb, flags, None)
 
-    p = good_problem(d_qk=256, d_v=256)
-    case("bwd_deterministic_declined_atomic_dims", "CPA_ERR_UNSUPPORTED", bwd(p, flags=1))
+    # The backward has no atomics at any head dim, so the flag is accepted:
+    # validation passes and only the launch, with no GPU visible, fails.
+    for d in (128, 256, 512):
+        p = good_problem(d_qk=d, d_v=d)
+        case(f"bwd_deterministic_accepted_d{d}", "CPA_ERR_LAUNCH", bwd(p, flags=1))
     p = good_problem()
-    # The dS path honours the flag: validation passes and only the launch,
-    # with no GPU visible, fails.
-    case("bwd_deterministic_accepted_ds_dims", "CPA_ERR_LAUNCH", bwd(p, flags=1))
     case("bwd_unknown_flag", "CPA_ERR_UNSUPPORTED", bwd(p, flags=2))
     need = lib.attn_bwd_workspace_size(ctypes.byref(p))
     least = lib.attn_bwd_workspace_min(ctypes.byref(p))
@@ -105,9 +105,9 @@ def main():
     case("bwd_output_overlaps_input", "CPA_ERR_OVERLAP", bwd(p, dq=2))
     out["bwd_workspace_bytes"] = ["int", int(need)]
     out["bwd_workspace_min_bytes"] = ["int", int(least)]
-    p = good_problem(d_qk=256, d_v=256)
-    out["bwd_workspace_atomic_dims"] = ["int", int(lib.attn_bwd_workspace_size(ctypes.byref(p))),
-                                        int(lib.attn_bwd_workspace_min(ctypes.byref(p)))]
+    p = good_problem(d_qk=512, d_v=512)
+    out["bwd_workspace_d512"] = ["int", int(lib.attn_bwd_workspace_size(ctypes.byref(p))),
+                                 int(lib.attn_bwd_workspace_min(ctypes.byref(p)))]
 
     md = _lib.MergeDesc()
     md.batch, md.heads, md.d_v, md.seqlen = 1, 4, 128, 64

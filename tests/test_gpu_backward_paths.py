@@ -1,4 +1,4 @@
-"""Backward paths beyond one full call, on the dS path (d_qk + d_v <= 320):
+"""Backward paths beyond one full call (head dims 192/128, and 256/512 below):
 
 * CPA_FLAG_DETERMINISTIC: repeated calls, also on a side stream, give
   bitwise identical dQ, dK, dV;
@@ -137,3 +137,47 @@ def test_ring_step_backward(problem):
     say("ring-step bwd: post")
     call("attn_bwd_post", *blocks[-1])
     _check(p, dq, dk, dv, "ring_step")
+
+
+@pytest.mark.parametrize("d", [256, 512])
+def test_large_head_dims_deterministic_and_banded(d):
+    """Head dims 256/512 (the 4-wave key-outer kernel storing dS, the dq
+    kernel in 256-column chunks): repeated calls are bitwise identical, and a
+    one-key-block band split gives bitwise equal dK, dV; every result meets
+    the accuracy criterion.  Ragged 200 queries and 330 keys, GQA 4/2."""
+    b_, sq, sk, hq, hkv = 1, 200, 330, 4, 2
+    scale = 1.0 / math.sqrt(d)
+    segs = [(0, sk - sq)]
+    g = torch.Generator().manual_seed(23 + d)
+    q = torch.randn(b_, sq, hq, d, generator=g)
+    k = torch.randn(b_, sk, hkv, d, generator=g)
+    v = torch.randn(b_, sk, hkv, d, generator=g)
+    do = torch.randn(b_, sq, hq, d, generator=g)
+    ref = {}
+    for kind, f in (("true", true64), ("naive", naive64)):
+        dq, dk, dv = oracle.bshd_backward(f(q), f(k), f(v), f(do), scale, segs, 0, True)
+        ref[kind] = dict(dq=dq, dk=dk, dv=dv)
+    dv_ = dev()
+    qi, ki, vi, doi = (x.to(torch.bfloat16).to(dv_) for x in (q, k, v, do))
+    say(f"d{d} fwd for determinism test")
+    o, lse = cpa.forward(qi, ki, vi, scale=scale, q_segments=segs)
+    p = dict(q=qi, k=ki, v=vi, do=doi, o=o, lse=lse, ref=ref)
+
+    def run(ws=None):
+        dq, dk, dv = _outputs(p)
+        cpa.attn_bwd(qi, ki, vi, o, doi, lse, dq, dk, dv, scale=scale, q_segments=segs,
+                     workspace=ws, flags=DETERMINISTIC)
+        return dq, dk, dv
+
+    say(f"d{d} bwd x3")
+    first = run()
+    _check(p, *first, f"d{d}_full")
+    for _ in range(2):
+        for a, b in zip(first, run()):
+            assert torch.equal(_bits(a), _bits(b))
+    least = cpa.bwd_workspace_bytes(qi, ki, vi, minimum=True)
+    say(f"d{d} bwd in one-block bands")
+    banded = run(torch.empty(least, dtype=torch.uint8, device=dv_))
+    _check(p, *banded, f"d{d}_bands")
+    assert torch.equal(_bits(first[1]), _bits(banded[1]))
+    assert torch.equal(_bits(first[2]), _bits(banded[2]))
