@@ -653,6 +653,23 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   int hg = 0, ut = 0;
   seek(hg, ut);
   if (hg < a.group) fetch(hg, ut);
+  // A tile's two dS chunks are stored at the top of the next iteration,
+  // right after the wait for the fetched Q/dO tile, and their registers stay
+  // live until the wait after that.  (vmcnt counts loads and stores alike;
+  // with both kinds in flight every wait is a wait for everything, so a
+  // store issued late in an iteration, or a register of a pending store
+  // reused early, would stall the next wait on the store's completion.)
+  int64_t prev_tile = -1;   // element offset of the tile whose dS sits in Tw
+  bf16x8 sd0 = zero8(), sd1 = zero8();
+  auto store_prev = [&]() {
+    sd0 = lds_tr8(Tw, TP, 8 * (grp >> 1), 16 * (grp & 1), gl);
+    sd1 = lds_tr8(Tw, TP, 16 + 8 * (grp >> 1), 16 * (grp & 1), gl);
+    bf16* dst = ds + prev_tile + chunk_off;
+    // streamed once, by another kernel: non-temporal, so the chunks do not
+    // push the query tiles other workgroups reuse out of L2
+    __builtin_nontemporal_store(sd0, reinterpret_cast<bf16x8*>(dst));
+    __builtin_nontemporal_store(sd1, reinterpret_cast<bf16x8*>(dst + 512));
+  };
   while (hg < a.group) {
     const int h = kvh * a.group + hg;
     const int i0 = ut * BM;
@@ -666,6 +683,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
       Dl[tid] = pre_d;
       Ps[tid] = pre_p;
     }
+    asm volatile("" :: "v"(sd0), "v"(sd1));   // the previous stores' registers
+    if (prev_tile >= 0) store_prev();
     int nhg = hg, nut = ut + 1;
     seek(nhg, nut);
     __syncthreads();
@@ -678,6 +697,9 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
     const int wlo = qh ? tp.lo1 : tp.lo0;
     const bool wave_on = on[qh];
     const bool need_mask = (jw + 32 > s.klen) || (a.causal && wlo < wkpos_hi);
+    // Next tile's Q/dO into registers (outside the per-wave branch, so the
+    // compiler sees one set of loads).
+    if (nhg < a.group) fetch(nhg, nut);
     if (wave_on) {
       f32x16 sacc, pacc;
 #pragma unroll
@@ -707,9 +729,6 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // Prefetch the next tile only now: its staging registers are then not
-      // live during the S and dP products, where the pressure peaks.
-      if (nhg < a.group) fetch(nhg, nut);
       // This lane's 16 rows are two runs of 8: qh*32 + 16*vh + 8*hh + e.
 #pragma unroll
       for (int vh = 0; vh < 2; ++vh) {
@@ -762,7 +781,6 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
         }
       }
     } else {
-      if (nhg < a.group) fetch(nhg, nut);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
         *reinterpret_cast<bf16x8*>(&Tw[lq * TP + 16 * tt + 8 * hh]) = zero8();
@@ -793,20 +811,14 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // This wave's two dS chunks for the dQ step (zeros when the half is off),
-    // stored non-temporally: they are read once, by another kernel, and
-    // would otherwise push the query tiles that other workgroups reuse out
-    // of L2.
-    bf16* dst = ds + (((int64_t)h * a.ds_nu + ubase + ut) * a.ds_nb + (kt - a.kt0)) *
-                         kDsTileElems + chunk_off;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_nontemporal_store(lds_tr8(Tw, TP, 16 * j + 8 * (grp >> 1), 16 * (grp & 1), gl),
-                                  reinterpret_cast<bf16x8*>(dst + 512 * j));
+    // This wave's two dS chunks (zeros when the half is off) go out at the
+    // top of the next iteration.
+    prev_tile = (((int64_t)h * a.ds_nu + ubase + ut) * a.ds_nb + (kt - a.kt0)) * kDsTileElems;
     hg = nhg;
     ut = nut;
   }
 
+  if (prev_tile >= 0) store_prev();
   // dK: each wave holds complete sums for its column blocks.  dV: the two
   // query halves' partials are summed through LDS into the qh = 0 waves.
   auto key_row = [&](void* outp, const int64_t* st) -> TOut* {
