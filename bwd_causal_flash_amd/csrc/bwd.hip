@@ -676,8 +676,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
     const int i1 = min(i0 + BM, s.qlen);
     const TilePos tp = {tpos[4 * ut], tpos[4 * ut + 1], tpos[4 * ut + 2], tpos[4 * ut + 3]};
     __syncthreads();
-    qst.store(Qs, QP, tid);
-    dost.store(dOs, OP, tid);
+    qst.store_rperm(Qs, QP, tid);   // Q and dO tiles are row-permuted (rperm16)
+    dost.store_rperm(dOs, OP, tid);
     if (tid < BM) {
       Ls[tid] = (pre_l == -kInf) ? kInf : pre_l * kLog2e;   // P = 0 on keyless rows
       Dl[tid] = pre_d;
@@ -711,11 +711,11 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
         bf16x8 qa[NS], kb[NS], oa[NS], vb[NS];
         auto rd = [&](int i) {
           if (i < KSQ) {
-            qa[i] = lds_row8(Qs, QP, qh * 32 + pr, i * 16 + hh * 8);
+            qa[i] = lds_row8(Qs, QP, rperm16(qh * 32 + pr), i * 16 + hh * 8);
             kb[i] = lds_row8(Ks, KP, kg * 32 + lq, i * 16 + hh * 8);
           }
           if (i < KSV) {
-            oa[i] = lds_row8(dOs, OP, qh * 32 + pr, i * 16 + hh * 8);
+            oa[i] = lds_row8(dOs, OP, rperm16(qh * 32 + pr), i * 16 + hh * 8);
             vb[i] = lds_row8(Vs, VP, kg * 32 + lq, i * 16 + hh * 8);
           }
         };
@@ -769,7 +769,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
         bf16x8 oa[N];
         auto rd = [&](int i) {
           const int tt = i / NDV, db = i % NDV;
-          oa[i] = lds_tr8(dOs, OP, 32 * qh + 16 * tt + 8 * (grp >> 1), db * 32 + 16 * (grp & 1), gl);
+          oa[i] = lds_tr8p(dOs, OP, 32 * qh + 16 * tt + 8 * (grp >> 1), db * 32 + 16 * (grp & 1), gl);
         };
 #pragma unroll
         for (int i = 0; i < AHEAD; ++i) rd(i);
@@ -799,7 +799,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
       bf16x8 qa[N];
       auto rd = [&](int i) {
         const int tt = i / NDKH, j = i % NDKH;
-        qa[i] = lds_tr8(Qs, QP, 32 * qq + 16 * tt + 8 * (grp >> 1),
+        qa[i] = lds_tr8p(Qs, QP, 32 * qq + 16 * tt + 8 * (grp >> 1),
                         (qh * NDKH + j) * 32 + 16 * (grp & 1), gl);
       };
 #pragma unroll
@@ -863,7 +863,7 @@ __device__ __forceinline__ int dq_last_block(const AttnArgs& a, const Seq& s, in
 template <int DQK, int DC, typename TIn>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   constexpr int BN = 128, NT = 512, NDK = DC / 32;
-  constexpr int KP = lds_pitch(DC);
+  constexpr int KP = tr_pitch(DC);   // K is read only through transpose reads
   static_assert(DQK % DC == 0, "whole column chunks");
   __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KP];
 

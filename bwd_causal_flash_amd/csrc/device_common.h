@@ -63,6 +63,20 @@ constexpr bool pitch_ok(int p) {
   }
   return true;
 }
+// LDS row pitch (elements) for a bf16 tile read only through the transpose
+// reads.  A half-wave's transpose read covers 4 consecutive rows x 64 bytes
+// (the LDS serves 256 bytes per clock, 32 lanes of 8 bytes); a pitch that
+// is an odd multiple of 64 bytes modulo 256 puts the 4 row windows on
+// disjoint bank ranges, where the 16-byte-read pitch above lets two of them
+// overlap (a 2-way conflict on every transpose read).
+constexpr int tr_pitch(int d) {
+  int p = d;
+  while (p % 128 != 32 && p % 128 != 96) p += 32;
+  return p;
+}
+static_assert(tr_pitch(64) == 96 && tr_pitch(128) == 160 && tr_pitch(192) == 224 &&
+                  tr_pitch(256) == 288,
+              "transpose pitch rule");
 constexpr int lds_pitch(int d) {
   int p = d + 8;
   while (!pitch_ok(p)) p += 16;
@@ -114,6 +128,26 @@ __device__ __forceinline__ bf16x8 lds_tr8(const bf16* tile, int pitch, int k0,
                                           int m0, int s) {
   const bf16* p0 = tile + (k0 + (s >> 2)) * pitch + m0 + 4 * (s & 3);
   const bf16* p1 = p0 + 4 * pitch;
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Row-permuted tiles: logical row 16b + 4a + i is stored at row 16b + 4i + a
+// (a 4x4 transpose inside every 16-row block).  With a pitch that is an odd
+// multiple of 16 bytes modulo 256 (lds_pitch), both ways of reading such a
+// tile are then free of bank conflicts: a 16-byte row read of 16 consecutive
+// logical rows still touches 16 distinct rows of one block, and the 4
+// logical rows of a half-wave transpose read land on rows 4 apart, whose
+// 64-byte windows fall on disjoint banks.
+__device__ __forceinline__ int rperm16(int r) {
+  return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3);
+}
+// lds_tr8 on a row-permuted tile (k0 a multiple of 8): the second read's
+// rows k0+4.. are the next physical row.
+__device__ __forceinline__ bf16x8 lds_tr8p(const bf16* tile, int pitch, int k0, int m0, int s) {
+  const bf16* p0 = tile + rperm16(k0 + (s >> 2)) * pitch + m0 + 4 * (s & 3);
+  const bf16* p1 = p0 + pitch;
   const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
   const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -283,6 +317,15 @@ struct TileStage {
 #pragma unroll
       for (int j = 0; j < CJ; ++j)
         *reinterpret_cast<bf16x8*>(tile + (rg + RP * i) * pitch + cp + 64 * j) = v[i][j];
+  }
+  // The same into a row-permuted tile (row r goes to rperm16(r)).
+  __device__ __forceinline__ void store_rperm(bf16* tile, int pitch, int tid) const {
+    const int rg = tid >> 3, cp = (tid & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < RI; ++i)
+#pragma unroll
+      for (int j = 0; j < CJ; ++j)
+        *reinterpret_cast<bf16x8*>(tile + rperm16(rg + RP * i) * pitch + cp + 64 * j) = v[i][j];
   }
 };
 

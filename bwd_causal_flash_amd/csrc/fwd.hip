@@ -34,7 +34,7 @@ constexpr int fwd_blocks_per_cu() { return DSUM <= 320 ? 2 : 1; }
 template <int DQK, int DVC, int NCH, typename TIn, typename TOut>
 __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kernel(const AttnArgs a) {
   constexpr int BM = 128, BN = 64;
-  constexpr int KP = lds_pitch(DQK), VP = lds_pitch(DVC);
+  constexpr int KP = lds_pitch(DQK), VP = tr_pitch(DVC);   // V: transpose reads only
   constexpr int KS = DQK / 16;
   constexpr int NDB = DVC / 32;
   __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KP];
