@@ -30,8 +30,10 @@ attention and its exact gradient, written out in float64:
   Description: packing preserves the FP32 log-sum-exp values).
 
 Visibility is given by explicit positions: key j is visible to query i iff
-it is a real key of the same sequence and (not causal or k_pos[j] <=
-q_pos[i]).  Top-left causal is q_pos = arange(S_q), k_pos = arange(S_k);
+it is a real key of the same sequence, (not causal or k_pos[j] <= q_pos[i])
+and, with a sliding window (left, right), q_pos[i] - left <= k_pos[j] <=
+q_pos[i] + right where -1 leaves that side unbounded (PR 3527, commits on
+sliding window).  Top-left causal is q_pos = arange(S_q), k_pos = arange(S_k);
 bottom-right adds S_k - S_q to q_pos (PR 3699 "Add cuDNN OSS backward
 dispatch for context parallel attention", Implementation and supported
 scope; PR 3527 commit on the all_gather path).

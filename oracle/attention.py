@@ -34,11 +34,28 @@ def positions_from_segments(n_rows, segments):
     return pos
 
 
-def _visible(qp, kp, causal):
-    """Boolean [rows, keys]: key j visible to query i."""
-    if not causal:
-        return np.ones((qp.shape[0], kp.shape[0]), dtype=bool)
-    return kp[None, :] <= qp[:, None]
+def _visible(qp, kp, causal, window=None):
+    """Boolean [rows, keys]: key j visible to query i.
+
+    causal: k_pos[j] <= q_pos[i].  window = (left, right), -1 meaning no
+    bound on that side: q_pos[i] - left <= k_pos[j] <= q_pos[i] + right, so
+    ``left`` keys before the diagonal stay visible besides the diagonal
+    itself (PR 3527, commits on sliding window: a diagonal alignment plus a
+    two-sided band; the window applies to every mask type, -1 is unbounded,
+    and a causal mask keeps the right bound at the diagonal, so a
+    non-causal (w, 0) window is the causal band of width w).
+    """
+    d = kp[None, :] - qp[:, None]          # key position minus query position
+    vis = np.ones(d.shape, dtype=bool)
+    if causal:
+        vis &= d <= 0
+    if window is not None:
+        left, right = window
+        if left >= 0:
+            vis &= d >= -left
+        if right >= 0:
+            vis &= d <= right
+    return vis
 
 
 def _row_softmax(s, vis):
@@ -59,7 +76,7 @@ def _row_softmax(s, vis):
 
 
 def forward(q, k, v, scale, q_pos=None, k_pos=None, causal=True,
-            heads=None, row_block=512):
+            heads=None, row_block=512, window=None):
     """Attention forward for one sequence.
 
     q [Sq, Hq, Dqk], k [Sk, Hkv, Dqk], v [Sk, Hkv, Dv]; query head h reads
@@ -81,14 +98,14 @@ def forward(q, k, v, scale, q_pos=None, k_pos=None, causal=True,
         for r0 in range(0, sq, row_block):
             r1 = min(sq, r0 + row_block)
             s = scale * (q[r0:r1, h, :] @ k[:, kh, :].T)
-            p, l = _row_softmax(s, _visible(qp[r0:r1], kp, causal))
+            p, l = _row_softmax(s, _visible(qp[r0:r1], kp, causal, window))
             o[r0:r1, h, :] = p @ v[:, kh, :]
             lse[h, r0:r1] = l
     return o, lse
 
 
 def forward_rows(q, k, v, scale, rows, q_pos=None, k_pos=None, causal=True,
-                 heads=None):
+                 heads=None, window=None):
     """Forward for selected query rows only (sampled checks at full size).
 
     Returns o [len(rows), Hq, Dv] and lse [Hq, len(rows)].
@@ -97,11 +114,11 @@ def forward_rows(q, k, v, scale, rows, q_pos=None, k_pos=None, causal=True,
     sq = q.shape[0]
     qp = np.arange(sq) if q_pos is None else np.asarray(q_pos, np.int64)
     return forward(np.asarray(q)[rows], k, v, scale, q_pos=qp[rows],
-                   k_pos=k_pos, causal=causal, heads=heads)
+                   k_pos=k_pos, causal=causal, heads=heads, window=window)
 
 
 def backward(q, k, v, do, scale, q_pos=None, k_pos=None, causal=True,
-             heads=None, row_block=512):
+             heads=None, row_block=512, window=None):
     """Exact gradient of O = softmax(s Q K^T + mask) V for one sequence.
 
     With P the masked softmax, dP = dO V^T and the softmax Jacobian
@@ -126,7 +143,7 @@ def backward(q, k, v, do, scale, q_pos=None, k_pos=None, causal=True,
         for r0 in range(0, sq, row_block):
             r1 = min(sq, r0 + row_block)
             s = scale * (q[r0:r1, h, :] @ k[:, kh, :].T)
-            p, _ = _row_softmax(s, _visible(qp[r0:r1], kp, causal))
+            p, _ = _row_softmax(s, _visible(qp[r0:r1], kp, causal, window))
             dp = do[r0:r1, h, :] @ v[:, kh, :].T
             rs = (p * dp).sum(axis=1)
             ds = p * (dp - rs[:, None])
@@ -160,7 +177,7 @@ def merge(parts):
 # ---------------------------------------------------------------- layouts
 
 def bshd_forward(q, k, v, scale, segments=None, k_pos_begin=0, causal=True,
-                 heads=None):
+                 heads=None, window=None):
     """Dense BSHD: q [B, Sq, Hq, D].  ``segments`` as in
     positions_from_segments (default: one segment at position 0, i.e.
     top-left); key j has position k_pos_begin + j.  Returns o [B, Sq, Hq,
@@ -171,19 +188,21 @@ def bshd_forward(q, k, v, scale, segments=None, k_pos_begin=0, causal=True,
     kp = k_pos_begin + np.arange(sk)
     os_, ls = [], []
     for i in range(b):
-        o, l = forward(q[i], k[i], v[i], scale, qp, kp, causal, heads)
+        o, l = forward(q[i], k[i], v[i], scale, qp, kp, causal, heads,
+                       window=window)
         os_.append(o)
         ls.append(l)
     return np.stack(os_), np.stack(ls)
 
 
 def bshd_backward(q, k, v, do, scale, segments=None, k_pos_begin=0,
-                  causal=True, heads=None):
+                  causal=True, heads=None, window=None):
     b, sq = q.shape[:2]
     sk = k.shape[1]
     qp = positions_from_segments(sq, segments or [(0, 0)])
     kp = k_pos_begin + np.arange(sk)
-    res = [backward(q[i], k[i], v[i], do[i], scale, qp, kp, causal, heads)
+    res = [backward(q[i], k[i], v[i], do[i], scale, qp, kp, causal, heads,
+                    window=window)
            for i in range(b)]
     return tuple(np.stack([r[j] for r in res]) for j in range(3))
 
@@ -197,7 +216,7 @@ def _thd_docs(cu_q, cu_k, used_q, used_k, bottom_right):
 
 
 def thd_forward(q, k, v, scale, cu_q, cu_k, used_q, used_k, causal=True,
-                bottom_right=False, heads=None):
+                bottom_right=False, heads=None, window=None):
     """Packed THD: q [Tq, Hq, D] with document n on physical rows
     [cu_q[n], cu_q[n] + used_q[n]) (padded offsets plus visible lengths, PR
     3149 "Enable FA4 for context-parallel attention", Description).  Padding
@@ -211,14 +230,14 @@ def thd_forward(q, k, v, scale, cu_q, cu_k, used_q, used_k, causal=True,
         if nq == 0:
             continue
         od, ld = forward(q[q0:q0 + nq], k[k0:k0 + nk], v[k0:k0 + nk], scale,
-                         qp, kp, causal, heads)
+                         qp, kp, causal, heads, window=window)
         o[q0:q0 + nq] = od
         lse[:, q0:q0 + nq] = ld
     return o, lse
 
 
 def thd_backward(q, k, v, do, scale, cu_q, cu_k, used_q, used_k, causal=True,
-                 bottom_right=False, heads=None):
+                 bottom_right=False, heads=None, window=None):
     """Gradients for packed THD; padding rows are left NaN."""
     dq = np.full(q.shape, np.nan)
     dk = np.full(k.shape, np.nan)
@@ -226,7 +245,8 @@ def thd_backward(q, k, v, do, scale, cu_q, cu_k, used_q, used_k, causal=True,
     for q0, nq, k0, nk, qp, kp in _thd_docs(cu_q, cu_k, used_q, used_k,
                                             bottom_right):
         a, b_, c = backward(q[q0:q0 + nq], k[k0:k0 + nk], v[k0:k0 + nk],
-                            do[q0:q0 + nq], scale, qp, kp, causal, heads)
+                            do[q0:q0 + nq], scale, qp, kp, causal, heads,
+                            window=window)
         dq[q0:q0 + nq] = a
         dk[k0:k0 + nk] = b_
         dvv[k0:k0 + nk] = c
