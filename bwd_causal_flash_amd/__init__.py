@@ -80,7 +80,7 @@ def _strides3(t: torch.Tensor, thd: bool):
 
 
 def _fill_problem(q, k, v, *, causal, scale, out_dtype, q_segments, k_pos_begin,
-                  varlen: Optional[Varlen]) -> Problem:
+                  varlen: Optional[Varlen], window=None) -> Problem:
     p = Problem()
     thd = q.dim() == 3
     if thd != (varlen is not None):
@@ -117,6 +117,9 @@ def _fill_problem(q, k, v, *, causal, scale, out_dtype, q_segments, k_pos_begin,
         p.q_seg_row[i] = int(r)
         p.q_seg_pos[i] = int(pos)
     p.k_pos_begin = int(k_pos_begin)
+    if window is not None:
+        p.window = 1
+        p.window_left, p.window_right = (int(w) for w in window)
     return p
 
 
@@ -133,17 +136,20 @@ def workspace_error_flag(ws: torch.Tensor) -> int:
 
 
 def attn_fwd(q, k, v, o, lse, *, causal=True, scale=None, q_segments=None, k_pos_begin=0,
-             varlen: Optional[Varlen] = None, workspace=None, stream=None) -> torch.Tensor:
+             varlen: Optional[Varlen] = None, workspace=None, stream=None,
+             window=None) -> torch.Tensor:
     """Forward into preallocated o (bf16 or fp32) and lse (fp32).
 
     q_segments: BSHD query positions as [(row_begin, pos_begin), ...]
     (default: one segment at 0, top-left causal); k_pos_begin: position of
-    key row 0.  Returns the workspace (its first int32 is the THD metadata
-    error flag).
+    key row 0; window: (left, right) sliding window / band, -1 = unbounded
+    on that side (None: no window).  Returns the workspace (its first int32
+    is the THD metadata error flag).
     """
     lib = _lib.load()
     p = _fill_problem(q, k, v, causal=causal, scale=scale, out_dtype=_dtype_code(o),
-                      q_segments=q_segments, k_pos_begin=k_pos_begin, varlen=varlen)
+                      q_segments=q_segments, k_pos_begin=k_pos_begin, varlen=varlen,
+                      window=window)
     thd = p.layout == 1
     p.o_stride = _strides3(o, thd)
     p.lse_stride = _lse_strides(lse, thd)
@@ -158,7 +164,7 @@ def attn_fwd(q, k, v, o, lse, *, causal=True, scale=None, q_segments=None, k_pos
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, *, causal=True, scale=None, q_segments=None,
              k_pos_begin=0, varlen: Optional[Varlen] = None, workspace=None, flags=0,
-             stream=None, step: str = "attn_bwd") -> torch.Tensor:
+             stream=None, step: str = "attn_bwd", window=None) -> torch.Tensor:
     """Backward into preallocated dq, dk, dv.  Returns the workspace.
 
     ``step`` selects the C entry point: "attn_bwd" (all four steps), or one
@@ -169,7 +175,8 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, *, causal=True, scale=None, q_se
         raise TypeError("o and dout must have q's dtype")
     lib = _lib.load()
     p = _fill_problem(q, k, v, causal=causal, scale=scale, out_dtype=_dtype_code(dq),
-                      q_segments=q_segments, k_pos_begin=k_pos_begin, varlen=varlen)
+                      q_segments=q_segments, k_pos_begin=k_pos_begin, varlen=varlen,
+                      window=window)
     thd = p.layout == 1
     p.o_stride = _strides3(o, thd)
     p.do_stride = _strides3(dout, thd)
@@ -284,24 +291,26 @@ def _lse_shape(q, thd):
 
 
 def forward(q, k, v, *, out_dtype=None, causal=True, scale=None, q_segments=None,
-            k_pos_begin=0, varlen=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+            k_pos_begin=0, varlen=None, stream=None,
+            window=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Allocate o, lse and run attn_fwd.  THD padding rows of the returned
     tensors are uninitialised (the kernels never write them)."""
     thd = q.dim() == 3
     o = torch.empty(*q.shape[:-1], v.shape[-1], dtype=out_dtype or q.dtype, device=q.device)
     lse = torch.empty(*_lse_shape(q, thd), dtype=torch.float32, device=q.device)
     attn_fwd(q, k, v, o, lse, causal=causal, scale=scale, q_segments=q_segments,
-             k_pos_begin=k_pos_begin, varlen=varlen, stream=stream)
+             k_pos_begin=k_pos_begin, varlen=varlen, stream=stream, window=window)
     return o, lse
 
 
 def backward(q, k, v, o, dout, lse, *, out_dtype=None, causal=True, scale=None,
-             q_segments=None, k_pos_begin=0, varlen=None, stream=None):
+             q_segments=None, k_pos_begin=0, varlen=None, stream=None, window=None):
     """Allocate dq, dk, dv and run attn_bwd."""
     dt = out_dtype or q.dtype
     dq = torch.empty(q.shape, dtype=dt, device=q.device)
     dk = torch.empty(k.shape, dtype=dt, device=q.device)
     dv = torch.empty(v.shape, dtype=dt, device=q.device)
     attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, causal=causal, scale=scale,
-             q_segments=q_segments, k_pos_begin=k_pos_begin, varlen=varlen, stream=stream)
+             q_segments=q_segments, k_pos_begin=k_pos_begin, varlen=varlen, stream=stream,
+             window=window)
     return dq, dk, dv

@@ -50,6 +50,8 @@ class Problem(ctypes.Structure):
         ("num_q_segments", ctypes.c_int32),
         ("q_seg_row", I64xS), ("q_seg_pos", I64xS),
         ("k_pos_begin", ctypes.c_int64),
+        ("window", ctypes.c_int32), ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
     ]
 
 

@@ -98,6 +98,16 @@ cpa_status check_problem(const cpa_problem* p) {
                             !p->seqused_k))
       return CPA_ERR_NULL;
   }
+  if (p->window != 0 && p->window != 1) return CPA_ERR_SHAPE;
+  if (p->window) {
+    // window offsets are added to int32 positions (|pos| < 2^30) in the kernels
+    const int64_t lim = 1ll << 30;
+    if (p->window_left < -1 || p->window_left >= lim || p->window_right < -1 ||
+        p->window_right >= lim)
+      return CPA_ERR_SHAPE;
+    if (p->layout == CPA_LAYOUT_THD && (p->seqlen_q >= lim || p->seqlen_k >= lim))
+      return CPA_ERR_SHAPE;
+  }
   if (!strides_ok(p->q_stride, 3) || !strides_ok(p->k_stride, 3) || !strides_ok(p->v_stride, 3))
     return CPA_ERR_STRIDE;
   if (p->lse_stride[0] < 0 || p->lse_stride[1] < 0) return CPA_ERR_STRIDE;
@@ -131,7 +141,12 @@ AttnArgs make_args(const cpa_problem* p) {
   a.max_k = p->max_seqlen_k;
   a.scale = p->softmax_scale;
   a.scale_log2 = (float)((double)p->softmax_scale * 1.4426950408889634);
-  a.causal = p->causal != 0;
+  // Band: right bound pos_k <= pos_q + win_r (causal: 0; a window's right
+  // bound otherwise), left bound pos_k >= pos_q - win_l.
+  a.causal = p->causal != 0 || (p->window && p->window_right >= 0);
+  a.win_r = p->causal ? 0 : (p->window && p->window_right >= 0 ? p->window_right : 0);
+  a.left = p->window && p->window_left >= 0;
+  a.win_l = a.left ? p->window_left : 0;
   a.bottom_right = p->thd_bottom_right != 0;
   if (p->layout == CPA_LAYOUT_BSHD && p->num_q_segments > 0) {
     a.nseg = p->num_q_segments;

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(const AttnArgs a) {
 
 __device__ __forceinline__ int64_t ds_ubase(const AttnArgs& a, const Seq& s, int z);
 
-template <int DQK, int DV, int OCK, int OCV, int BM, typename TIn, typename TOut>
+template <int DQK, int DV, int OCK, int OCV, int BM, typename TIn, typename TOut, bool WIN>
 __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
   constexpr int BN = 128;
   constexpr int QP = lds_pitch(DQK), OP = lds_pitch(DV), SP = lds_pitch(BM), KP = lds_pitch(OCK);
@@ -149,6 +149,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
   const int j0 = kt * BN;
   if (j0 >= s.klen) return;
   const int kp0 = kpos0(a);
+  const Band<WIN> bd(a);
 
   const int jw = j0 + wave * 32;
   const int my_key = jw + lq;
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
   const bool wave_has_keys = jw < s.klen;
   const int wk_last = min(jw + 31, s.klen - 1);
   const int wkpos_lo = kp0 + jw, wkpos_hi = kp0 + wk_last;
-  const int gkpos_lo = kp0 + j0;
+  const int gkpos_lo = kp0 + j0, gkpos_hi = kp0 + min(j0 + BN, s.klen) - 1;
 
   const TIn* Q = static_cast<const TIn*>(a.q);
   const TIn* K = static_cast<const TIn*>(a.k);
@@ -194,11 +195,11 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
   // tiles: both halves of a visible tile are visited (a half that sees no
   // key stores zeros).
   auto visible = [&](int u) -> bool {
-    if (!a.causal) return true;
+    if (!a.causal && !bd.left) return true;
     const int t0 = ((u % nqt) * BM) & ~63;
     int lo, hi;
     qpos_range(a, s, t0, min(t0 + 64, s.qlen), lo, hi);
-    return hi >= gkpos_lo;
+    return (!a.causal || hi + bd.wr >= gkpos_lo) && (!bd.left || lo - bd.wl <= gkpos_hi);
   };
   auto tile_of = [&](int k) -> int { return k; };
   auto next_visible = [&](int k) -> int {
@@ -266,9 +267,11 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
     if (PREFETCH && kn < total) fetch(tile_of(kn));
     __syncthreads();
 
-    const bool wave_on = wave_has_keys && (!a.causal || thi >= wkpos_lo);
+    const bool wave_on = wave_has_keys && (!a.causal || thi + bd.wr >= wkpos_lo) &&
+                         (!bd.left || tlo - bd.wl <= wkpos_hi);
     if (wave_on) {
-      const bool need_mask = (jw + 32 > s.klen) || (a.causal && tlo < wkpos_hi);
+      const bool need_mask = (jw + 32 > s.klen) || (a.causal && tlo + bd.wr < wkpos_hi) ||
+                             (bd.left && thi - bd.wl > wkpos_lo);
       // One 32-row query block at a time keeps a single block's S and dP
       // live; the unrolled loop lets block qb+1's products overlap block
       // qb's exponentials.
@@ -319,7 +322,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
         for (int v = 0; v < 16; ++v) {
           float p = fast_exp2(__builtin_fmaf(sacc[v], a.scale_log2, -lrow[v]));
           if (need_mask) {
-            const bool vis = key_valid && (!a.causal || my_kpos <= Ps[qb * 32 + acc_row_perm(v, hh)]);
+            const bool vis = key_valid && band_vis<WIN>(a, my_kpos, Ps[qb * 32 + acc_row_perm(v, hh)]);
             p = vis ? p : 0.f;
           }
           sacc[v] = p;
@@ -536,7 +539,7 @@ __device__ __forceinline__ void store_key_acc(const f32x16 (&acc)[ND], TOut* o, 
     }
 }
 
-template <int DQK, int DV, typename TIn, typename TOut>
+template <int DQK, int DV, typename TIn, typename TOut, bool WIN>
 __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   using L = KvSmem<DQK, DV>;
   constexpr int BN = L::BN, BM = L::BM, NT = 512;
@@ -567,6 +570,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   const int j0 = kt * BN;
   if (j0 >= s.klen) return;
   const int kp0 = kpos0(a);
+  const Band<WIN> bd(a);
 
   const int jw = j0 + kg * 32;
   const int my_key = jw + lq;
@@ -574,7 +578,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   const int my_kpos = kp0 + my_key;
   const bool wave_has_keys = jw < s.klen;
   const int wkpos_lo = kp0 + jw, wkpos_hi = kp0 + min(jw + 31, s.klen - 1);
-  const int gkpos_lo = kp0 + j0;
+  const int gkpos_lo = kp0 + j0, gkpos_hi = kp0 + min(j0 + BN, s.klen) - 1;
 
   const TIn* Q = static_cast<const TIn*>(a.q);
   const TIn* K = static_cast<const TIn*>(a.k);
@@ -607,17 +611,21 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   // so the uniform reads become scalar loads)
   typedef const __attribute__((address_space(4))) int* ConstInt;
   const ConstInt tpos = (ConstInt)(uintptr_t)a.tile_pos + 4 * ubase;
-  auto tile_hi = [&](int ut) -> int {
+  // Whether query tile ut sees a key of the block (causal / band bounds; an
+  // empty half has lo = INT32_MAX, hi = INT32_MIN).
+  auto tile_sees = [&](int ut) -> bool {
     const int h0 = tpos[4 * ut + 1], h1 = tpos[4 * ut + 3];
-    return h0 > h1 ? h0 : h1;
+    const int l0 = tpos[4 * ut], l1 = tpos[4 * ut + 2];
+    return (!a.causal || (h0 > h1 ? h0 : h1) + bd.wr >= gkpos_lo) &&
+           (!bd.left || (l0 < l1 ? l0 : l1) - bd.wl <= gkpos_hi);
   };
   // Next (query head, tile) at or after (hg, ut) whose tile sees a key of
   // the block.  Every workgroup walks the tiles in the same order, so the
   // ones that run together on an XCD read each Q / dO tile while it is in L2.
   auto seek = [&](int& hg, int& ut) {
     while (hg < a.group) {
-      if (a.causal)
-        while (ut < nqt && tile_hi(ut) < gkpos_lo) ++ut;
+      if (a.causal || bd.left)
+        while (ut < nqt && !tile_sees(ut)) ++ut;
       if (ut < nqt) return;
       ++hg;
       ut = 0;
@@ -692,11 +700,15 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
     // Query halves: rows [i0 + 32*qq, +32) of the tile, handled by waves
     // (kg, qq); a half with no visible (row, key) pair skips its products
     // and contributes dS = 0.
-    const bool on[2] = {wave_has_keys && i0 < i1 && (!a.causal || tp.hi0 >= wkpos_lo),
-                        wave_has_keys && i0 + 32 < i1 && (!a.causal || tp.hi1 >= wkpos_lo)};
-    const int wlo = qh ? tp.lo1 : tp.lo0;
+    const bool on[2] = {wave_has_keys && i0 < i1 && (!a.causal || tp.hi0 + bd.wr >= wkpos_lo) &&
+                            (!bd.left || tp.lo0 - bd.wl <= wkpos_hi),
+                        wave_has_keys && i0 + 32 < i1 &&
+                            (!a.causal || tp.hi1 + bd.wr >= wkpos_lo) &&
+                            (!bd.left || tp.lo1 - bd.wl <= wkpos_hi)};
+    const int wlo = qh ? tp.lo1 : tp.lo0, whi = qh ? tp.hi1 : tp.hi0;
     const bool wave_on = on[qh];
-    const bool need_mask = (jw + 32 > s.klen) || (a.causal && wlo < wkpos_hi);
+    const bool need_mask = (jw + 32 > s.klen) || (a.causal && wlo + bd.wr < wkpos_hi) ||
+                           (bd.left && whi - bd.wl > wkpos_lo);
     // Next tile's Q/dO into registers (outside the per-wave branch, so the
     // compiler sees one set of loads).
     if (nhg < a.group) fetch(nhg, nut);
@@ -744,7 +756,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
           const int v = 8 * vh + e;
           float p = fast_exp2(__builtin_fmaf(sacc[v], a.scale_log2, -lr[e]));
           if (need_mask) {
-            const bool vis = key_valid && (!a.causal || my_kpos <= Ps[rr + e]);
+            const bool vis = key_valid && band_vis<WIN>(a, my_kpos, Ps[rr + e]);
             p = vis ? p : 0.f;
           }
           sacc[v] = p;
@@ -845,17 +857,28 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   }
 }
 
-// Last key block (inclusive) that query tile ut of sequence s sees, or -1.
-__device__ __forceinline__ int dq_last_block(const AttnArgs& a, const Seq& s, int ut, int nkb,
-                                             int kp0) {
+// Key blocks [first, last] that query tile ut of sequence s sees (last = -1
+// when none).  The same bounds decide which tiles the key-outer kernels
+// visit, so every dS tile read here was written.
+__device__ __forceinline__ void dq_block_range(const AttnArgs& a, const Seq& s, int ut, int nkb,
+                                               int kp0, int& first, int& last) {
+  first = 0;
+  last = -1;
   const int nqt = (s.qlen + 63) / 64;
-  if (ut >= nqt || nkb <= 0) return -1;
-  if (!a.causal) return nkb - 1;
-  int lo, hi;
-  qpos_range(a, s, ut * 64, min(ut * 64 + 64, s.qlen), lo, hi);
-  if (hi < kp0) return -1;
-  const int b = (hi - kp0) / 128;
-  return b < nkb - 1 ? b : nkb - 1;
+  if (ut >= nqt || nkb <= 0) return;
+  int lo = 0, hi = 0;
+  if (a.causal || a.left) qpos_range(a, s, ut * 64, min(ut * 64 + 64, s.qlen), lo, hi);
+  last = nkb - 1;
+  if (a.causal) {
+    if (hi + a.win_r < kp0) { last = -1; return; }
+    const int b = (hi + a.win_r - kp0) / 128;
+    last = b < last ? b : last;
+  }
+  if (a.left) {
+    const int x = lo - a.win_l - kp0;   // first visible key of the tile's lowest row
+    if (x > s.klen - 1) { last = -1; return; }
+    first = x <= 0 ? 0 : x / 128;
+  }
 }
 
 // DC: dQ columns per workgroup (the whole head dim up to 256; the 512 dim
@@ -879,11 +902,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   const int qb2 = wave & 1;
   const int nkb = (s.klen + BN - 1) / BN;
   const int kp0 = kpos0(a);
-  const int my_last = dq_last_block(a, s, ut, nkb, kp0);
-  int wg_last = -1;
+  int my_first, my_last;
+  dq_block_range(a, s, ut, nkb, kp0, my_first, my_last);
+  int wg_first = nkb, wg_last = -1;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) wg_last = max(wg_last, dq_last_block(a, s, ut0 + t, nkb, kp0));
-  const int kt_begin = a.kt0;
+  for (int t = 0; t < 4; ++t) {
+    int f, l;
+    dq_block_range(a, s, ut0 + t, nkb, kp0, f, l);
+    if (l >= f) {
+      wg_first = min(wg_first, f);
+      wg_last = max(wg_last, l);
+    }
+  }
+  const int kt_begin = max(a.kt0, wg_first);
   const int kt_end = min(wg_last + 1, a.kt0 + a.ds_nb);
   if (kt_begin >= kt_end) return;   // uniform over the workgroup
 
@@ -925,7 +956,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
     if (kt + 1 < kt_end) kst.load(K + kbase, a.k_stride[1], (kt + 1) * BN, s.klen, tid);
     if (kt + AHEAD < kt_end) load_frags(kt + AHEAD, nn);
     __syncthreads();
-    if (kt <= my_last) {
+    if (kt >= my_first && kt <= my_last) {
 #pragma unroll
       for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -946,7 +977,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
       if (kt + 1 < kt_end) body(kt + 1, fb, fa);
     }
   }
-  if (my_last < kt_begin) return;
+  if (max(my_first, kt_begin) > min(my_last, kt_end - 1)) return;   // nothing added
   // Accumulator update: all loads, then all stores (the rows are distinct).
   float* accbase = a.dq_acc + (a.thd ? s.q_row0 * a.acc_stride[1] : (int64_t)z * a.acc_stride[0]) +
                    (int64_t)h * a.acc_stride[2] + c0 + lq;
@@ -1005,11 +1036,18 @@ static hipError_t bwd_variant(const AttnArgs& a, int step, hipStream_t st) {
   if (step == 1 && krows > 0) {
     if constexpr (C::KV_KERNEL) {
       dim3 g(a.heads_kv, a.ds_nb, a.nseq);
-      hipLaunchKernelGGL((bwd_kv_kernel<DQK, DV, TIn, TOut>), g, dim3(512), 0, st, a);
+      if (needs_band(a))
+        hipLaunchKernelGGL((bwd_kv_kernel<DQK, DV, TIn, TOut, true>), g, dim3(512), 0, st, a);
+      else
+        hipLaunchKernelGGL((bwd_kv_kernel<DQK, DV, TIn, TOut, false>), g, dim3(512), 0, st, a);
     } else {
       dim3 g(a.heads_kv * C::NCH, a.ds_nb, a.nseq);
-      hipLaunchKernelGGL((bwd_main_kernel<DQK, DV, C::OCK, C::OCV, C::BM, TIn, TOut>), g,
-                         dim3(256), 0, st, a);
+      if (needs_band(a))
+        hipLaunchKernelGGL((bwd_main_kernel<DQK, DV, C::OCK, C::OCV, C::BM, TIn, TOut, true>), g,
+                           dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((bwd_main_kernel<DQK, DV, C::OCK, C::OCV, C::BM, TIn, TOut, false>), g,
+                           dim3(256), 0, st, a);
     }
   }
   if (step == 2 && krows > 0 && qrows > 0) {

@@ -224,6 +224,27 @@ __device__ __forceinline__ int qpos(const AttnArgs& a, const Seq& s, int i) {
   return p;
 }
 
+// Key position pk visible to query position pq under the band: causal (or a
+// window's right bound) keeps pk <= pq + win_r, a window's left bound keeps
+// pk >= pq - win_l.  Positions and bounds are below 2^30, so the sums fit.
+// WIN = false: kernels built for plain causal / full masks (win_r = 0, no
+// left bound), which keep the band arithmetic out of their code.
+template <bool WIN>
+__device__ __forceinline__ bool band_vis(const AttnArgs& a, int pk, int pq) {
+  if constexpr (!WIN) return !a.causal || pk <= pq;
+  return (!a.causal || pk <= pq + a.win_r) && (!a.left || pk >= pq - a.win_l);
+}
+// Band bounds as a kernel sees them (compile-time zero without WIN).
+template <bool WIN>
+struct Band {
+  bool left;
+  int wr, wl;
+  __device__ __forceinline__ explicit Band(const AttnArgs& a)
+      : left(WIN && a.left), wr(WIN ? a.win_r : 0), wl(WIN ? a.win_l : 0) {}
+};
+// Whether a launch needs the band-capable kernels.
+inline bool needs_band(const AttnArgs& a) { return a.left || a.win_r != 0; }
+
 // Min and max query position over local rows [r0, r1) (r1 > r0).
 __device__ __forceinline__ void qpos_range(const AttnArgs& a, const Seq& s, int r0, int r1,
                                            int& lo, int& hi) {

@@ -31,7 +31,7 @@ namespace cpa {
 template <int DSUM>
 constexpr int fwd_blocks_per_cu() { return DSUM <= 320 ? 2 : 1; }
 
-template <int DQK, int DVC, int NCH, typename TIn, typename TOut>
+template <int DQK, int DVC, int NCH, typename TIn, typename TOut, bool WIN>
 __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kernel(const AttnArgs a) {
   constexpr int BM = 128, BN = 64;
   constexpr int KP = lds_pitch(DQK), VP = tr_pitch(DVC);   // V: transpose reads only
@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
   const int i0 = tile * BM;
   if (i0 >= s.qlen) return;
   const int kvh = h / a.group;
+  const Band<WIN> bd(a);
 
   const TIn* Q = static_cast<const TIn*>(a.q);
   const TIn* K = static_cast<const TIn*>(a.k);
@@ -72,11 +73,18 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
   int glo, ghi;
   qpos_range(a, s, i0, min(i0 + BM, s.qlen), glo, ghi);
   const int kp0 = kpos0(a);
+  // Keys [kbeg, kend) can be visible to some row of the workgroup.
   int kend = s.klen;
   if (a.causal) {
-    const int64_t lim = (int64_t)ghi - kp0 + 1;
+    const int64_t lim = (int64_t)ghi + bd.wr - kp0 + 1;
     kend = (int)(lim < 0 ? 0 : (lim < kend ? lim : kend));
   }
+  int kbeg = 0;
+  if (bd.left) {
+    const int64_t first = (int64_t)glo - bd.wl - kp0;
+    kbeg = (int)(first <= 0 ? 0 : (first < kend ? first : kend));
+  }
+  const int t0 = kbeg / BN;
   const int ntiles = (kend + BN - 1) / BN;
 
   // This lane's query row as the B operand of S^T = K Q^T, for all k-steps.
@@ -100,12 +108,12 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
   // tile t is being computed.
   TileStage<BN, DQK, TIn, 256, true> kst;   // limit = klen >= 1 when ntiles > 0
   TileStage<BN, DVC, TIn, 256, true> vst;
-  if (ntiles > 0) {
-    kst.load(Kb, a.k_stride[1], 0, s.klen, tid);
-    vst.load(Vb, a.v_stride[1], 0, s.klen, tid);
+  if (t0 < ntiles) {
+    kst.load(Kb, a.k_stride[1], t0 * BN, s.klen, tid);
+    vst.load(Vb, a.v_stride[1], t0 * BN, s.klen, tid);
   }
 
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t0; t < ntiles; ++t) {
     const int j0 = t * BN;
     __syncthreads();
     kst.store(Ks, KP, tid);
@@ -115,7 +123,9 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
       vst.load(Vb, a.v_stride[1], j0 + BN, s.klen, tid);
     }
     __syncthreads();
-    if (!wave_active || (a.causal && kp0 + j0 > whi)) continue;
+    if (!wave_active || (a.causal && kp0 + j0 > whi + bd.wr) ||
+        (bd.left && kp0 + j0 + BN - 1 < wlo - bd.wl))
+      continue;
 
     f32x16 sacc[2];
 #pragma unroll
@@ -128,14 +138,15 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
       for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = mfma32(lds_row8(Ks, KP, kb * 32 + kr, ks * 16 + hh * 8), qreg[ks], sacc[kb]);
 
-    const bool need_mask = (j0 + BN > s.klen) || (a.causal && kp0 + j0 + BN - 1 > wlo);
+    const bool need_mask = (j0 + BN > s.klen) || (a.causal && kp0 + j0 + BN - 1 > wlo + bd.wr) ||
+                           (bd.left && kp0 + j0 < whi - bd.wl);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int j = j0 + kb * 32 + acc_row_perm(v, hh);
-          const bool vis = j < s.klen && (!a.causal || kp0 + j <= my_pos);
+          const bool vis = j < s.klen && band_vis<WIN>(a, kp0 + j, my_pos);
           sacc[kb][v] = vis ? sacc[kb][v] : -kInf;
         }
     }
@@ -238,7 +249,10 @@ static hipError_t fwd_variant(const AttnArgs& a, hipStream_t st) {
   const int ntile = (qrows + 127) / 128;
   if (ntile == 0 || a.nseq == 0) return hipSuccess;
   dim3 grid(a.heads_q * NCH, ntile, a.nseq);
-  hipLaunchKernelGGL((fwd_kernel<DQK, DVC, NCH, TIn, TOut>), grid, dim3(256), 0, st, a);
+  if (needs_band(a))
+    hipLaunchKernelGGL((fwd_kernel<DQK, DVC, NCH, TIn, TOut, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<DQK, DVC, NCH, TIn, TOut, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -48,7 +48,10 @@ struct AttnArgs {
 
   float scale;        // softmax scale s
   float scale_log2;   // s * log2(e)
-  int causal;
+  int causal;         // right bound on: key visible only if pos_k <= pos_q + win_r
+  int win_r;          // >= 0 (0 for causal)
+  int left;           // left bound on: key visible only if pos_k >= pos_q - win_l
+  int win_l;          // >= 0
   int bottom_right;
   int nseg;
   int seg_row[CPA_MAX_SEGMENTS];   // positions and rows fit in int32

@@ -22,7 +22,13 @@
  * PR 3510 "Add head-parallel FA4 backward for cuDNN CP attention", Diagram).
  *
  * Visibility.  Key j is visible to query i iff it is a real key of the same
- * sequence and, when causal, pos_k(j) <= pos_q(i).  Positions make top-left
+ * sequence, when causal pos_k(j) <= pos_q(i), and with a sliding window
+ * (window = 1) pos_q(i) - window_left <= pos_k(j) <= pos_q(i) + window_right,
+ * where -1 leaves that side unbounded (PR 3527 "cuDNN FROST attention backend
+ * for head_dim in (256, 512]", commits on sliding window: one mechanism, a
+ * diagonal alignment plus a two-sided band; a causal mask keeps the right
+ * bound at the diagonal, so window (w, 0) without causal is the causal band
+ * of width w, and window (0, 0) leaves only the diagonal).  Positions make top-left
  * causal (the default), bottom-right causal (PR 3699 "Add cuDNN OSS backward
  * dispatch for context parallel attention", Implementation and supported
  * scope) and the dual-chunk query rows of a load-balanced CP rank (PR 3510,
@@ -134,6 +140,13 @@ typedef struct cpa_problem {
   int64_t q_seg_row[CPA_MAX_SEGMENTS];
   int64_t q_seg_pos[CPA_MAX_SEGMENTS];
   int64_t k_pos_begin;
+
+  /* Sliding window / band (see Visibility): window = 0 (no window, the
+   * zero-initialised default) or 1; window_left, window_right in
+   * [-1, 2^30), -1 = unbounded on that side.  With a window, THD row counts
+   * must stay below 2^30 (else CPA_ERR_SHAPE). */
+  int32_t window;
+  int32_t window_left, window_right;
 } cpa_problem;
 
 /* Human-readable name of a status code (host, static string). */

@@ -81,6 +81,14 @@ def main():
     case("thd_missing_metadata", "CPA_ERR_NULL", fwd(p))
     p = good_problem(); p.seqlen_q = 1 << 31
     case("seqlen_too_large", "CPA_ERR_SHAPE", fwd(p))
+    p = good_problem(); p.window = 2
+    case("window_flag_not_0_or_1", "CPA_ERR_SHAPE", fwd(p))
+    p = good_problem(); p.window = 1; p.window_left = -2
+    case("window_left_below_minus_1", "CPA_ERR_SHAPE", fwd(p))
+    p = good_problem(); p.window = 1; p.window_right = 1 << 30
+    case("window_right_too_large", "CPA_ERR_SHAPE", fwd(p))
+    p = good_problem(); p.window = 1; p.window_left = 100; p.window_right = -1
+    case("window_valid_reaches_launch", "CPA_ERR_LAUNCH", fwd(p))
 
     def bwd(p, flags=0, wsb=1 << 30, dq=100, dk=120, dv=140):
         return lib.attn_bwd(ctypes.byref(p), ptr(1), ptr(2), ptr(3), ptr(40), ptr(50), ptr(60),

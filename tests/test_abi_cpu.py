@@ -59,7 +59,7 @@ int main(void) {
   printf("cpa_pack_desc %zu\n", sizeof(struct cpa_pack_desc));
   F(cpa_problem, seqlen_q) F(cpa_problem, cu_seqlens_q) F(cpa_problem, q_stride)
   F(cpa_problem, lse_stride) F(cpa_problem, softmax_scale) F(cpa_problem, q_seg_row)
-  F(cpa_problem, k_pos_begin)
+  F(cpa_problem, k_pos_begin) F(cpa_problem, window) F(cpa_problem, window_right)
   F(cpa_merge_desc, seqlen) F(cpa_merge_desc, acc_stride) F(cpa_merge_desc, lse_out_stride)
   F(cpa_pack_desc, seqlen) F(cpa_pack_desc, o_stride) F(cpa_pack_desc, force_int64)
   return 0;
