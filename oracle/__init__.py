@@ -28,6 +28,8 @@ attention and its exact gradient, written out in float64:
   interleaved with KV exchange and LSE correction).
 * pack/unpack: a byte permutation of O and the raw fp32 LSE bits (PR 3510,
   Description: packing preserves the FP32 log-sum-exp values).
+* exchange buffers: the byte permutation of any row tensors and LSEs into
+  per-peer segments for the head-parallel all-to-alls (PR 3510, Diagram).
 
 Visibility is given by explicit positions: key j is visible to query i iff
 it is a real key of the same sequence, (not causal or k_pos[j] <= q_pos[i])
@@ -49,3 +51,4 @@ from .attention import (  # noqa: F401
     thd_backward, positions_from_segments, forward_rows,
 )
 from .pack import pack_saved, unpack_saved, pack_layout  # noqa: F401
+from .xchg import xchg_layout, xchg_pack, xchg_unpack  # noqa: F401
