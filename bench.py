@@ -175,6 +175,30 @@ def main():
             b.record(stream)
             torch.cuda.synchronize()
             phases[name] = round(a.elapsed_time(b) / 5, 4)
+        # head-parallel exchange buffer: this rank's Q, K, V, O, dO rows and LSE
+        # packed seq -> heads into 4 head-group segments (and unpacked back)
+        import bwd_causal_flash_amd as cpa
+        rows = torch.cat([torch.arange(c[0], c[0] + c[1]) for c in chunks]).to(dev)
+        kpos = torch.cat([torch.arange(c[2], c[2] + c[1]) for c in chunks]).to(dev)
+        fields = [rs.q, k[:, kpos].contiguous(), v[:, kpos].contiguous(), rs.o, rs.dout,
+                  rs.lse]
+        every = [[(0, int(rows.numel()))]] * w.cp
+        xbuf = cpa.xchg_pack(fields, groups=w.cp, ranges=every, split=True, stream=stream)
+        outs = [torch.empty_like(f) for f in fields]
+        for name, fn in (("xchg_pack", lambda: cpa.xchg_pack(fields, groups=w.cp, ranges=every,
+                                                             split=True, buf=xbuf, stream=stream)),
+                         ("xchg_unpack", lambda: cpa.xchg_unpack(xbuf, outs, groups=w.cp,
+                                                                 ranges=every, split=True,
+                                                                 stream=stream))):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(10):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / 10
+            phases[name] = round(ms, 4)
+            phases[name + "_GBps(read+write)"] = round(2 * xbuf.numel() / (ms * 1e-3) / 1e9, 1)
         print(json.dumps({"phase_ms": phases, "main_ms": round(main_ms, 4),
                           "fwd_tflops": round(f_fwd / 1e12, 4),
                           "bwd_tflops": round(f_bwd / 1e12, 4)}), file=sys.stderr)

@@ -284,6 +284,87 @@ def unpack_saved(buf, o, lse, groups, *, force_int64=False, stream=None):
     return o, lse
 
 
+def xchg_desc(tensors, *, groups, ranges, split):
+    """Exchange-buffer description (include/cpattn.h, cpa_xchg_desc).
+
+    tensors: row tensors [B, R, H, D] (bf16 or fp32, moved as raw bits) and
+    LSE tensors [B, H, R] (fp32), in buffer order; ranges: per segment a list
+    of (row_begin, count); split: one bool for all fields or one per field
+    (True: heads split over the segments)."""
+    if not tensors or len(tensors) > _lib.CPA_XCHG_MAX_FIELDS:
+        raise ValueError("1..8 tensors")
+    if len(ranges) != groups or groups > _lib.CPA_XCHG_MAX_GROUPS:
+        raise ValueError("one range list per segment, at most 8 segments")
+    splits = list(split) if isinstance(split, (list, tuple)) else [split] * len(tensors)
+    d = _lib.XchgDesc()
+    d.groups, d.nfields = int(groups), len(tensors)
+    rows = None
+    for f, (x, sp) in enumerate(zip(tensors, splits)):
+        fd = d.field[f]
+        if x.stride(-1) != 1:
+            raise ValueError("last dim must be contiguous")
+        if x.dim() == 4:
+            b, r, h, dim = x.shape
+            fd.kind, fd.elem_bytes, fd.heads, fd.dim = (_lib.CPA_XCHG_ROWS, x.element_size(),
+                                                        h, dim)
+            fd.stride = tuple(x.stride()[:3])
+        elif x.dim() == 3 and x.dtype == torch.float32:
+            b, h, r = x.shape
+            fd.kind, fd.elem_bytes, fd.heads, fd.dim = _lib.CPA_XCHG_LSE, 4, h, 1
+            fd.stride = (x.stride(0), x.stride(1), 0)
+        else:
+            raise ValueError("row tensors are [B, R, H, D], LSE tensors fp32 [B, H, R]")
+        fd.split = int(bool(sp))
+        if rows is None:
+            d.batch, rows = b, r
+        elif (b, r) != (d.batch, rows):
+            raise ValueError("all tensors need the same batch and rows")
+    d.rows = rows
+    for g, rg in enumerate(ranges):
+        if len(rg) > _lib.CPA_XCHG_MAX_RANGES:
+            raise ValueError("at most 4 ranges per segment")
+        d.nranges[g] = len(rg)
+        for i, (r0, n) in enumerate(rg):
+            d.range_row[g][i], d.range_len[g][i] = int(r0), int(n)
+    return d
+
+
+def xchg_offsets(d) -> list:
+    """Segment byte offsets [groups + 1] (the last is the buffer size)."""
+    lib = _lib.load()
+    offs = [int(lib.xchg_segment_offset(ctypes.byref(d), g)) for g in range(d.groups + 1)]
+    if offs[-1] == 0 and d.rows > 0:
+        raise ValueError("invalid exchange description")
+    return offs
+
+
+def _ptr_array(tensors):
+    return (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+
+
+def xchg_pack(tensors, *, groups, ranges, split, buf=None, stream=None) -> torch.Tensor:
+    """Pack every segment of ``tensors`` into one uint8 buffer (returned)."""
+    lib = _lib.load()
+    d = xchg_desc(tensors, groups=groups, ranges=ranges, split=split)
+    need = xchg_offsets(d)[-1]
+    if buf is None:
+        buf = torch.empty(need, dtype=torch.uint8, device=tensors[0].device)
+    st = lib.xchg_pack(ctypes.byref(d), _ptr_array(tensors), _ptr(buf), buf.numel(),
+                       _stream_handle(stream))
+    _lib.check(st, "xchg_pack")
+    return buf
+
+
+def xchg_unpack(buf, tensors, *, groups, ranges, split, stream=None):
+    """Unpack a (received) buffer into ``tensors`` in place."""
+    lib = _lib.load()
+    d = xchg_desc(tensors, groups=groups, ranges=ranges, split=split)
+    st = lib.xchg_unpack(ctypes.byref(d), _ptr(buf), buf.numel(), _ptr_array(tensors),
+                         _stream_handle(stream))
+    _lib.check(st, "xchg_unpack")
+    return tensors
+
+
 # ------------------------------------------------------------- allocating
 
 def _lse_shape(q, thd):

@@ -79,6 +79,31 @@ class PackDesc(ctypes.Structure):
     ]
 
 
+CPA_XCHG_MAX_FIELDS, CPA_XCHG_MAX_GROUPS, CPA_XCHG_MAX_RANGES = 8, 8, 4
+CPA_XCHG_ROWS, CPA_XCHG_LSE = 0, 1
+
+
+class XchgField(ctypes.Structure):
+    """Mirror of struct cpa_xchg_field."""
+    _fields_ = [
+        ("kind", ctypes.c_int32), ("elem_bytes", ctypes.c_int32),
+        ("heads", ctypes.c_int32), ("dim", ctypes.c_int32), ("split", ctypes.c_int32),
+        ("stride", I64x3),
+    ]
+
+
+class XchgDesc(ctypes.Structure):
+    """Mirror of struct cpa_xchg_desc."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("groups", ctypes.c_int32), ("nfields", ctypes.c_int32),
+        ("rows", ctypes.c_int64),
+        ("nranges", ctypes.c_int32 * CPA_XCHG_MAX_GROUPS),
+        ("range_row", (ctypes.c_int64 * CPA_XCHG_MAX_RANGES) * CPA_XCHG_MAX_GROUPS),
+        ("range_len", (ctypes.c_int64 * CPA_XCHG_MAX_RANGES) * CPA_XCHG_MAX_GROUPS),
+        ("field", XchgField * CPA_XCHG_MAX_FIELDS),
+    ]
+
+
 EXPORTS = {
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_fwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Problem)]),
@@ -102,6 +127,11 @@ EXPORTS = {
                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "unpack_saved": (ctypes.c_int, [ctypes.POINTER(PackDesc), ctypes.c_void_p, ctypes.c_size_t,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "xchg_segment_offset": (ctypes.c_size_t, [ctypes.POINTER(XchgDesc), ctypes.c_int32]),
+    "xchg_pack": (ctypes.c_int, [ctypes.POINTER(XchgDesc), ctypes.POINTER(ctypes.c_void_p),
+                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "xchg_unpack": (ctypes.c_int, [ctypes.POINTER(XchgDesc), ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]),
 }
 
 _lib = None

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcpattn.so")
-SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "merge_pack.hip"]
+SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "merge_pack.hip", "xchg.hip"]
 
 ARCH = os.environ.get("CPATTN_ARCH", "gfx950")
 FLAGS = [

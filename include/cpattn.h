@@ -308,6 +308,80 @@ cpa_status unpack_saved(const cpa_pack_desc* d, const void* buf,
                         size_t buf_bytes, void* o, float* lse,
                         cpa_stream_t stream);
 
+/*
+ * Exchange buffers for the head-parallel all-to-alls (PR 3510 "Add
+ * head-parallel FA4 backward for cuDNN CP attention", Diagram: the sequence
+ * partition's Q, K, V, O, dO and LSE go to a head partition with one
+ * all-to-all, each rank runs a full-sequence backward on its head group, and
+ * dQ, dK, dV come back the same way).  One call packs every peer's segment
+ * of up to CPA_XCHG_MAX_FIELDS tensors into one buffer, or unpacks a
+ * received buffer, bit for bit; the all-to-all itself (RCCL) is the
+ * caller's.
+ *
+ * Fields.  A row field is a [batch, rows, heads, dim] tensor of 2- or 4-byte
+ * elements (element (b, r, h, d) at base + b*stride[0] + r*stride[1] +
+ * h*stride[2] + d, strides in elements, rows 16-byte aligned); an LSE field
+ * is fp32 [batch, heads, rows] (element (b, h, r) at base + b*stride[0] +
+ * h*stride[1] + r).  With split = 1, segment g holds heads
+ * [g*heads/groups, (g+1)*heads/groups); with split = 0 it holds all heads.
+ *
+ * Segments.  Segment g (g = 0 .. groups-1, one per peer) covers the rows
+ * given by its ranges, concatenated in order (n_g rows), and holds each
+ * field in turn, starting at a multiple of 256 bytes: a row field's element
+ * (b, i, hh, d) at ((b*n_g + i)*Hf + hh)*dim + d, an LSE field's element
+ * (b, hh, i) at (b*Hf + hh)*n_g + i (Hf = heads of the segment).  Segment
+ * g starts at xchg_segment_offset(d, g); segments are 256-byte multiples.
+ * Pad bytes are neither read nor written.
+ *
+ * Sequence -> heads: each rank packs with split = 1 and one range (all its
+ * rows); after the all-to-all, receiver g's buffer is the senders' segments
+ * g in rank order, which it unpacks with split = 0 into its head-group
+ * tensors, segment r having sender r's rows as ranges (two ranges for a
+ * dual-chunk rank).  Heads -> sequence swaps the two descriptions.
+ */
+enum { CPA_XCHG_MAX_FIELDS = 8, CPA_XCHG_MAX_GROUPS = 8, CPA_XCHG_MAX_RANGES = 4 };
+enum { CPA_XCHG_ROWS = 0, CPA_XCHG_LSE = 1 };
+
+typedef struct cpa_xchg_field {
+  int32_t kind;         /* CPA_XCHG_ROWS or CPA_XCHG_LSE */
+  int32_t elem_bytes;   /* ROWS: 2 or 4 (moved as raw bits); LSE: 4 */
+  int32_t heads;        /* heads of the local tensor (> 0) */
+  int32_t dim;          /* ROWS: elements per (row, head), dim*elem_bytes a
+                           multiple of 16; LSE: ignored */
+  int32_t split;        /* 1: heads split over the segments; 0: all heads */
+  int64_t stride[3];    /* elements; ROWS [batch, row, head]; LSE [batch,
+                           head] (rows contiguous, stride[2] ignored) */
+} cpa_xchg_field;
+
+typedef struct cpa_xchg_desc {
+  int32_t batch;        /* >= 1 */
+  int32_t groups;       /* segments (peers), 1 .. CPA_XCHG_MAX_GROUPS */
+  int32_t nfields;      /* 1 .. CPA_XCHG_MAX_FIELDS */
+  int64_t rows;         /* rows of the local tensors; ranges lie inside */
+  int32_t nranges[CPA_XCHG_MAX_GROUPS];                   /* 0 .. 4 */
+  int64_t range_row[CPA_XCHG_MAX_GROUPS][CPA_XCHG_MAX_RANGES];
+  int64_t range_len[CPA_XCHG_MAX_GROUPS][CPA_XCHG_MAX_RANGES];
+  cpa_xchg_field field[CPA_XCHG_MAX_FIELDS];
+} cpa_xchg_desc;
+
+/* Byte offset of segment g (host, pure); g = groups gives the total buffer
+ * size.  0 for an invalid descriptor or g outside [0, groups]. */
+size_t xchg_segment_offset(const cpa_xchg_desc* d, int32_t g);
+
+/* tensors[f] (host array of nfields device pointers) -> buf.  buf: device,
+ * 16-byte aligned, at least xchg_segment_offset(d, groups) bytes (else
+ * CPA_ERR_SHAPE), not overlapping any tensor (CPA_ERR_OVERLAP).  Row
+ * tensors 16-byte aligned, LSE tensors 4-byte aligned. */
+cpa_status xchg_pack(const cpa_xchg_desc* d, const void* const* tensors,
+                     void* buf, size_t buf_bytes, cpa_stream_t stream);
+
+/* buf -> tensors[f] (exact inverse for the bytes the segments cover; other
+ * elements are left as they were).  The tensors must not overlap the
+ * buffer or each other. */
+cpa_status xchg_unpack(const cpa_xchg_desc* d, const void* buf,
+                       size_t buf_bytes, void* const* tensors,
+                       cpa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -147,6 +147,42 @@ def main():
          lib.pack_saved(ctypes.byref(pd), ptr(1), ptr(2), ptr(1), n, None))
     case("unpack_buffer_overlaps_lse", "CPA_ERR_OVERLAP",
          lib.unpack_saved(ctypes.byref(pd), ptr(2), n, ptr(1), ptr(2), None))
+    # exchange buffers: one row field and one LSE field, 2 segments
+    def xdesc():
+        d = _lib.XchgDesc()
+        d.batch, d.groups, d.nfields, d.rows = 1, 2, 2, 64
+        for g in range(2):
+            d.nranges[g] = 1
+            d.range_row[g][0], d.range_len[g][0] = 0, 64
+        f0, f1 = d.field[0], d.field[1]
+        f0.kind, f0.elem_bytes, f0.heads, f0.dim, f0.split = 0, 2, 4, 128, 1
+        f0.stride = (64 * 4 * 128, 4 * 128, 128)
+        f1.kind, f1.elem_bytes, f1.heads, f1.dim, f1.split = 1, 4, 4, 1, 1
+        f1.stride = (4 * 64, 64, 0)
+        return d
+    ptrs = (ctypes.c_void_p * 2)(A * 1, A * 2)
+    xpack = lambda d, buf=ptr(8), n=1 << 24: lib.xchg_pack(ctypes.byref(d), ptrs, buf, n, None)
+    d = xdesc()
+    seg1 = lib.xchg_segment_offset(ctypes.byref(d), 1)
+    total = lib.xchg_segment_offset(ctypes.byref(d), 2)
+    # segment: 64 rows x 2 heads x 128 bf16 = 32 KiB, LSE 2 x 64 x 4 = 512 B
+    out["xchg_offsets"] = ["int", int(seg1), int(total)]
+    case("xchg_valid_reaches_launch", "CPA_ERR_LAUNCH", xpack(d))
+    case("xchg_buffer_small", "CPA_ERR_SHAPE", xpack(d, n=total - 1))
+    case("xchg_buffer_overlaps_tensor", "CPA_ERR_OVERLAP", xpack(d, buf=ptr(0)))
+    d = xdesc(); d.range_len[1][0] = 65
+    case("xchg_range_past_rows", "CPA_ERR_SHAPE", xpack(d))
+    d = xdesc(); d.field[0].heads = 3
+    case("xchg_split_heads_not_divisible", "CPA_ERR_SHAPE", xpack(d))
+    d = xdesc(); d.field[0].dim = 4
+    case("xchg_row_bytes_not_16", "CPA_ERR_SHAPE", xpack(d))
+    d = xdesc(); d.field[0].elem_bytes = 8
+    case("xchg_bad_elem_bytes", "CPA_ERR_DTYPE", xpack(d))
+    d = xdesc(); d.groups = 9
+    case("xchg_too_many_groups", "CPA_ERR_SHAPE", xpack(d))
+    out["xchg_invalid_offset_is_zero"] = ["int", int(lib.xchg_segment_offset(ctypes.byref(d), 1))]
+    d = xdesc()
+    case("xchg_misaligned_buffer", "CPA_ERR_ALIGN", xpack(d, buf=ctypes.c_void_p(A * 8 + 4)))
     print(json.dumps(out))
 
 

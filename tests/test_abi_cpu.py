@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_bwd", "attn_merge_lse", "pack_saved", "unpack_saved",
               "attn_fwd_workspace_size", "attn_bwd_workspace_size", "pack_saved_size",
-              "attn_status_string"):
+              "attn_status_string", "xchg_segment_offset", "xchg_pack", "xchg_unpack"):
         assert n in names, n
 
 
@@ -57,6 +57,10 @@ int main(void) {
   printf("cpa_problem %zu\n", sizeof(struct cpa_problem));
   printf("cpa_merge_desc %zu\n", sizeof(struct cpa_merge_desc));
   printf("cpa_pack_desc %zu\n", sizeof(struct cpa_pack_desc));
+  printf("cpa_xchg_desc %zu\n", sizeof(struct cpa_xchg_desc));
+  printf("cpa_xchg_field %zu\n", sizeof(struct cpa_xchg_field));
+  F(cpa_xchg_desc, rows) F(cpa_xchg_desc, range_row) F(cpa_xchg_desc, range_len)
+  F(cpa_xchg_desc, field) F(cpa_xchg_field, split) F(cpa_xchg_field, stride)
   F(cpa_problem, seqlen_q) F(cpa_problem, cu_seqlens_q) F(cpa_problem, q_stride)
   F(cpa_problem, lse_stride) F(cpa_problem, softmax_scale) F(cpa_problem, q_seg_row)
   F(cpa_problem, k_pos_begin) F(cpa_problem, window) F(cpa_problem, window_right)
@@ -73,7 +77,8 @@ int main(void) {
         lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
     got = dict(l.split() for l in lines if l.strip())
     mirrors = {"cpa_problem": _lib.Problem, "cpa_merge_desc": _lib.MergeDesc,
-               "cpa_pack_desc": _lib.PackDesc}
+               "cpa_pack_desc": _lib.PackDesc, "cpa_xchg_desc": _lib.XchgDesc,
+               "cpa_xchg_field": _lib.XchgField}
     for k, v in got.items():
         if "." in k:
             s, f = k.split(".")
@@ -92,6 +97,8 @@ def test_argument_errors_are_rejected_before_launch():
     bad = {k: v for k, v in res.items() if v[0] != "int" and v[0] != v[1]}
     assert not bad, bad
     assert res["pack_size_invalid_is_zero"][1] == 0
+    assert res["xchg_offsets"][1:] == [32768 + 512, 2 * (32768 + 512)]
+    assert res["xchg_invalid_offset_is_zero"][1] == 0
     assert res["pack_size_valid"][1] % 256 == 0 and res["pack_size_valid"][1] > 0
     # flag + D + fp32 dQ accumulator + query-tile position table (4 tiles x
     # 16 B, padded to 256), then dS tiles: 4 heads x 4 query tiles x 16 KiB
