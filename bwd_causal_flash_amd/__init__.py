@@ -26,7 +26,7 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 from . import _lib
-from ._lib import (CPA_BF16, CPA_FP32, CPA_FLAG_DETERMINISTIC, CpaError,  # noqa: F401
+from ._lib import (CPA_BF16, CPA_FP16, CPA_FP32, CPA_FLAG_DETERMINISTIC, CpaError,  # noqa: F401
                    MergeDesc, PackDesc, Problem, STATUS_CODE)
 
 __all__ = [
@@ -58,7 +58,9 @@ def _dtype_code(t: torch.Tensor) -> int:
         return CPA_BF16
     if t.dtype == torch.float32:
         return CPA_FP32
-    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+    if t.dtype == torch.float16:
+        return CPA_FP16
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16, fp16 or fp32)")
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -12,7 +12,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcpattn.so")
 
-CPA_BF16, CPA_FP32 = 0, 1
+CPA_BF16, CPA_FP32, CPA_FP16 = 0, 1, 2
 CPA_LAYOUT_BSHD, CPA_LAYOUT_THD = 0, 1
 CPA_MAX_SEGMENTS = 8
 CPA_FLAG_DETERMINISTIC = 1

@@ -13,8 +13,12 @@ namespace {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-bool dtype_ok(int dt) { return dt == CPA_BF16 || dt == CPA_FP32; }
-int dtype_bytes(int dt) { return dt == CPA_BF16 ? 2 : 4; }
+bool dtype_ok(int dt) { return dt == CPA_BF16 || dt == CPA_FP32 || dt == CPA_FP16; }
+int dtype_bytes(int dt) { return dt == CPA_FP32 ? 4 : 2; }
+// fp16 inputs pair with fp16 or fp32 outputs, bf16 / fp32 inputs with bf16 or fp32.
+bool dtype_pair_ok(int in_dt, int out_dt) {
+  return in_dt == CPA_FP16 ? out_dt != CPA_BF16 : out_dt != CPA_FP16;
+}
 
 bool heads_supported(int dqk, int dv) {
   return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128) ||
@@ -69,6 +73,7 @@ cpa_status check_problem(const cpa_problem* p) {
   if (!p) return CPA_ERR_NULL;
   if (p->layout != CPA_LAYOUT_BSHD && p->layout != CPA_LAYOUT_THD) return CPA_ERR_SHAPE;
   if (!dtype_ok(p->in_dtype) || !dtype_ok(p->out_dtype)) return CPA_ERR_DTYPE;
+  if (!dtype_pair_ok(p->in_dtype, p->out_dtype)) return CPA_ERR_UNSUPPORTED;
   if (p->heads_q <= 0 || p->heads_kv <= 0 || p->heads_q % p->heads_kv) return CPA_ERR_SHAPE;
   if (p->d_qk <= 0 || p->d_v <= 0 || (p->d_qk & 7) || (p->d_v & 7)) return CPA_ERR_UNSUPPORTED;
   if (!heads_supported(p->d_qk, p->d_v)) return CPA_ERR_UNSUPPORTED;

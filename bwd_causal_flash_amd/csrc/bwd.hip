@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a) {
     // dO enters the products rounded to bf16, so D uses the same rounded dO:
     // then D_i = sum_j P_ij dP_ij holds for the kernel's own dP.
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += to_f32(O[ob + e]) * (float)(bf16)dO[db + e];
+    for (int e = 0; e < 8; ++e) acc += to_f32(O[ob + e]) * (float)(ct_t<TIn>)dO[db + e];
   }
 #pragma unroll
   for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, G);
@@ -95,10 +95,10 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(const AttnArgs a) {
     const float4 x1 = reinterpret_cast<const float4*>(accrow)[2 * c + 1];
     const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
     if constexpr (sizeof(TOut) == 2) {
-      bf16x8 w;
+      vec8<TOut> w;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = (bf16)(v[e] * a.scale);
-      reinterpret_cast<bf16x8*>(out)[c] = w;
+      for (int e = 0; e < 8; ++e) w[e] = (TOut)(v[e] * a.scale);
+      reinterpret_cast<vec8<TOut>*>(out)[c] = w;
     } else {
       reinterpret_cast<float4*>(out)[2 * c] =
           make_float4(v[0] * a.scale, v[1] * a.scale, v[2] * a.scale, v[3] * a.scale);
@@ -115,6 +115,8 @@ __device__ __forceinline__ int64_t ds_ubase(const AttnArgs& a, const Seq& s, int
 template <int DQK, int DV, int OCK, int OCV, int BM, typename TIn, typename TOut, bool WIN>
 __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
   constexpr int BN = 128;
+  using CT = ct_t<TIn>;   // matrix-core operand type
+  using CT8 = vec8<CT>;
   constexpr int QP = lds_pitch(DQK), OP = lds_pitch(DV), SP = lds_pitch(BM), KP = lds_pitch(OCK);
   constexpr int NQB = BM / 32;
   constexpr int KSQ = DQK / 16, KSV = DV / 16;
@@ -130,11 +132,11 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
   constexpr bool V_FROM_LDS = SMALL;
   constexpr bool PREFETCH = SMALL;
   constexpr int VP = lds_pitch(DV);
-  __shared__ __attribute__((aligned(16))) bf16 Qs[BM * QP];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[BM * OP];
-  __shared__ __attribute__((aligned(16))) bf16 dSt[BN * SP];
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[V_FROM_LDS ? BN * VP : 8];
+  __shared__ __attribute__((aligned(16))) CT Qs[BM * QP];
+  __shared__ __attribute__((aligned(16))) CT dOs[BM * OP];
+  __shared__ __attribute__((aligned(16))) CT dSt[BN * SP];
+  __shared__ __attribute__((aligned(16))) CT Ks[BN * KP];
+  __shared__ __attribute__((aligned(16))) CT Vs[V_FROM_LDS ? BN * VP : 8];
   __shared__ __attribute__((aligned(16))) float Ls[BM];
   __shared__ __attribute__((aligned(16))) float Dl[BM];
   __shared__ int Ps[BM];
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
         } else {
 #pragma unroll 4
           for (int ks = 0; ks < KSQ; ++ks) {
-            const bf16x8 b = key_valid ? Elem<TIn>::load8(krow + ks * 16 + hh * 8) : zero8();
+            const CT8 b = key_valid ? Elem<TIn>::load8(krow + ks * 16 + hh * 8) : zero8<CT>();
             sacc = mfma32(lds_row8(Qs, QP, qb * 32 + pr, ks * 16 + hh * 8), b, sacc);
           }
         }
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
         } else {
 #pragma unroll 4
           for (int ks = 0; ks < KSV; ++ks) {
-            const bf16x8 b = key_valid ? Elem<TIn>::load8(vrow + ks * 16 + hh * 8) : zero8();
+            const CT8 b = key_valid ? Elem<TIn>::load8(vrow + ks * 16 + hh * 8) : zero8<CT>();
             pacc = mfma32(lds_row8(dOs, OP, qb * 32 + pr, ks * 16 + hh * 8), b, pacc);
           }
         }
@@ -330,11 +332,11 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
         }
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          bf16x8 pb, sb;
+          CT8 pb, sb;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            pb[e] = (bf16)sacc[8 * tt + e];
-            sb[e] = (bf16)pacc[8 * tt + e];
+            pb[e] = (CT)sacc[8 * tt + e];
+            sb[e] = (CT)pacc[8 * tt + e];
           }
           const int k0 = 32 * qb + 16 * tt + 8 * (grp >> 1);
 #pragma unroll
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
           for (int db = 0; db < NDK; ++db)
             dkacc[db] = mfma32(lds_tr8(Qs, QP, k0, ch * OCK + db * 32 + 16 * (grp & 1), gl), sb,
                                dkacc[db]);
-          *reinterpret_cast<bf16x8*>(&dSt[(wave * 32 + lq) * SP + qb * 32 + 16 * tt + 8 * hh]) = sb;
+          *reinterpret_cast<CT8*>(&dSt[(wave * 32 + lq) * SP + qb * 32 + 16 * tt + 8 * hh]) = sb;
         }
       }
     } else {
@@ -353,8 +355,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int hv = 0; hv < 2; ++hv)
-          *reinterpret_cast<bf16x8*>(&dSt[(wave * 32 + lq) * SP + qb * 32 + 16 * hv + 8 * hh]) =
-              zero8();
+          *reinterpret_cast<CT8*>(&dSt[(wave * 32 + lq) * SP + qb * 32 + 16 * hv + 8 * hh]) =
+              zero8<CT>();
     }
     __syncthreads();
 
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
     static_assert(BM == 32, "dS chunks of 32 query rows");
     if (ch == 0) {
       const int ut = i0 >> 6, qb2 = (i0 >> 5) & 1;
-      bf16* dst = static_cast<bf16*>(a.ds) +
+      CT* dst = static_cast<CT*>(a.ds) +
                   (((int64_t)h * a.ds_nu + ds_ubase(a, s, z) + ut) * a.ds_nb + (kt - a.kt0)) *
                       (64 * 128) +
                   ((int64_t)(qb2 * 8 + 2 * wave) * 64 + lane) * 8;
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
       for (int j = 0; j < 2; ++j)
         __builtin_nontemporal_store(
             lds_tr8(dSt, SP, 16 * (2 * wave + j) + 8 * (grp >> 1), 16 * (grp & 1), gl),
-            reinterpret_cast<bf16x8*>(dst + 512 * j));
+            reinterpret_cast<CT8*>(dst + 512 * j));
     }
     k = kn;
   }
@@ -392,10 +394,10 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
     for (int a4 = 0; a4 < 4; ++a4) {
       const int d = db * 32 + 8 * a4 + 4 * hh;
       if constexpr (sizeof(TOut) == 2) {
-        bf16x4 w;
+        vec4<TOut> w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)(dkacc[db][4 * a4 + e] * a.scale);
-        *reinterpret_cast<bf16x4*>(dK + d) = w;
+        for (int e = 0; e < 4; ++e) w[e] = (TOut)(dkacc[db][4 * a4 + e] * a.scale);
+        *reinterpret_cast<vec4<TOut>*>(dK + d) = w;
       } else {
         *reinterpret_cast<float4*>(dK + d) =
             make_float4(dkacc[db][4 * a4] * a.scale, dkacc[db][4 * a4 + 1] * a.scale,
@@ -408,10 +410,10 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
     for (int a4 = 0; a4 < 4; ++a4) {
       const int d = db * 32 + 8 * a4 + 4 * hh;
       if constexpr (sizeof(TOut) == 2) {
-        bf16x4 w;
+        vec4<TOut> w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)dvacc[db][4 * a4 + e];
-        *reinterpret_cast<bf16x4*>(dV + d) = w;
+        for (int e = 0; e < 4; ++e) w[e] = (TOut)dvacc[db][4 * a4 + e];
+        *reinterpret_cast<vec4<TOut>*>(dV + d) = w;
       } else {
         *reinterpret_cast<float4*>(dV + d) = make_float4(
             dvacc[db][4 * a4], dvacc[db][4 * a4 + 1], dvacc[db][4 * a4 + 2], dvacc[db][4 * a4 + 3]);
@@ -527,10 +529,10 @@ __device__ __forceinline__ void store_key_acc(const f32x16 (&acc)[ND], TOut* o, 
     for (int a4 = 0; a4 < 4; ++a4) {
       const int d = db * 32 + 8 * a4 + 4 * hh;
       if constexpr (sizeof(TOut) == 2) {
-        bf16x4 w;
+        vec4<TOut> w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * a4 + e] * mul);
-        *reinterpret_cast<bf16x4*>(o + d) = w;
+        for (int e = 0; e < 4; ++e) w[e] = (TOut)(acc[db][4 * a4 + e] * mul);
+        *reinterpret_cast<vec4<TOut>*>(o + d) = w;
       } else {
         *reinterpret_cast<float4*>(o + d) =
             make_float4(acc[db][4 * a4] * mul, acc[db][4 * a4 + 1] * mul,
@@ -542,6 +544,8 @@ __device__ __forceinline__ void store_key_acc(const f32x16 (&acc)[ND], TOut* o, 
 template <int DQK, int DV, typename TIn, typename TOut, bool WIN>
 __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   using L = KvSmem<DQK, DV>;
+  using CT = ct_t<TIn>;   // matrix-core operand type
+  using CT8 = vec8<CT>;
   constexpr int BN = L::BN, BM = L::BM, NT = 512;
   constexpr int QP = L::QP, OP = L::OP, KP = L::KP, VP = L::VP, TP = L::TP;
   constexpr int KSQ = DQK / 16, KSV = DV / 16;
@@ -549,10 +553,10 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   constexpr int NDKH = NDK / 2;   // dK^T column blocks per query-half wave
   static_assert(NDK % 2 == 0, "dK column split");
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
-  bf16* Ks = reinterpret_cast<bf16*>(smem + L::K_OFF);
-  bf16* Vs = reinterpret_cast<bf16*>(smem + L::V_OFF);
-  bf16* Qs = reinterpret_cast<bf16*>(smem + L::Q_OFF);
-  bf16* dOs = reinterpret_cast<bf16*>(smem + L::O_OFF);
+  CT* Ks = reinterpret_cast<CT*>(smem + L::K_OFF);
+  CT* Vs = reinterpret_cast<CT*>(smem + L::V_OFF);
+  CT* Qs = reinterpret_cast<CT*>(smem + L::Q_OFF);
+  CT* dOs = reinterpret_cast<CT*>(smem + L::O_OFF);
   float* Ls = reinterpret_cast<float*>(smem + L::L_OFF);
   float* Dl = reinterpret_cast<float*>(smem + L::D_OFF);
   int* Ps = reinterpret_cast<int*>(smem + L::P_OFF);
@@ -560,8 +564,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
   const int kg = wave & 3, qh = wave >> 2;
-  bf16* Ts = reinterpret_cast<bf16*>(smem + L::T_OFF);
-  bf16* Tw = Ts + wave * 32 * TP;
+  CT* Ts = reinterpret_cast<CT*>(smem + L::T_OFF);
+  CT* Tw = Ts + wave * 32 * TP;
   int kvh, kt;
   xcd_remap(kvh, kt);
   kt += a.kt0;
@@ -603,7 +607,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
 
   const int pr = perm32(lq);
   const int nqt = (s.qlen + BM - 1) / BM;
-  bf16* const ds = static_cast<bf16*>(a.ds);
+  CT* const ds = static_cast<CT*>(a.ds);
   const int64_t ubase = ds_ubase(a, s, z);
   // Query positions of the sequence's 64-row tiles (min and max of each
   // 32-row half), written by the pre step; uniform scalar loads.
@@ -668,15 +672,15 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   // store issued late in an iteration, or a register of a pending store
   // reused early, would stall the next wait on the store's completion.)
   int64_t prev_tile = -1;   // element offset of the tile whose dS sits in Tw
-  bf16x8 sd0 = zero8(), sd1 = zero8();
+  CT8 sd0 = zero8<CT>(), sd1 = zero8<CT>();
   auto store_prev = [&]() {
     sd0 = lds_tr8(Tw, TP, 8 * (grp >> 1), 16 * (grp & 1), gl);
     sd1 = lds_tr8(Tw, TP, 16 + 8 * (grp >> 1), 16 * (grp & 1), gl);
-    bf16* dst = ds + prev_tile + chunk_off;
+    CT* dst = ds + prev_tile + chunk_off;
     // streamed once, by another kernel: non-temporal, so the chunks do not
     // push the query tiles other workgroups reuse out of L2
-    __builtin_nontemporal_store(sd0, reinterpret_cast<bf16x8*>(dst));
-    __builtin_nontemporal_store(sd1, reinterpret_cast<bf16x8*>(dst + 512));
+    __builtin_nontemporal_store(sd0, reinterpret_cast<CT8*>(dst));
+    __builtin_nontemporal_store(sd1, reinterpret_cast<CT8*>(dst + 512));
   };
   while (hg < a.group) {
     const int h = kvh * a.group + hg;
@@ -720,7 +724,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
       // are read before the products of step i.
       {
         constexpr int NS = KSQ > KSV ? KSQ : KSV, AHEAD = 2;
-        bf16x8 qa[NS], kb[NS], oa[NS], vb[NS];
+        CT8 qa[NS], kb[NS], oa[NS], vb[NS];
         auto rd = [&](int i) {
           if (i < KSQ) {
             qa[i] = lds_row8(Qs, QP, rperm16(qh * 32 + pr), i * 16 + hh * 8);
@@ -763,22 +767,22 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
           pacc[v] = p * (pacc[v] - dr[e]);
         }
       }
-      bf16x8 wp[2];
+      CT8 wp[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        bf16x8 wd;
+        CT8 wd;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          wp[tt][e] = (bf16)sacc[8 * tt + e];
-          wd[e] = (bf16)pacc[8 * tt + e];
+          wp[tt][e] = (CT)sacc[8 * tt + e];
+          wd[e] = (CT)pacc[8 * tt + e];
         }
         // dS^T block of this wave: row = key, column = query row (natural order)
-        *reinterpret_cast<bf16x8*>(&Tw[lq * TP + 16 * tt + 8 * hh]) = wd;
+        *reinterpret_cast<CT8*>(&Tw[lq * TP + 16 * tt + 8 * hh]) = wd;
       }
       // dV^T += dO^T P over the wave's 32 query rows, operands 2 steps ahead.
       {
         constexpr int N = 2 * NDV, AHEAD = 2;
-        bf16x8 oa[N];
+        CT8 oa[N];
         auto rd = [&](int i) {
           const int tt = i / NDV, db = i % NDV;
           oa[i] = lds_tr8p(dOs, OP, 32 * qh + 16 * tt + 8 * (grp >> 1), db * 32 + 16 * (grp & 1), gl);
@@ -795,7 +799,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
     } else {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
-        *reinterpret_cast<bf16x8*>(&Tw[lq * TP + 16 * tt + 8 * hh]) = zero8();
+        *reinterpret_cast<CT8*>(&Tw[lq * TP + 16 * tt + 8 * hh]) = zero8<CT>();
     }
     __syncthreads();   // both query halves' dS blocks are in LDS
 
@@ -805,10 +809,10 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
       if (!on[qq]) continue;
-      const bf16* Tq = Ts + (kg + 4 * qq) * 32 * TP;
-      const bf16x8 wd[2] = {lds_row8(Tq, TP, lq, 8 * hh), lds_row8(Tq, TP, lq, 16 + 8 * hh)};
+      const CT* Tq = Ts + (kg + 4 * qq) * 32 * TP;
+      const CT8 wd[2] = {lds_row8(Tq, TP, lq, 8 * hh), lds_row8(Tq, TP, lq, 16 + 8 * hh)};
       constexpr int N = 2 * NDKH, AHEAD = 2;
-      bf16x8 qa[N];
+      CT8 qa[N];
       auto rd = [&](int i) {
         const int tt = i / NDKH, j = i % NDKH;
         qa[i] = lds_tr8p(Qs, QP, 32 * qq + 16 * tt + 8 * (grp >> 1),
@@ -886,9 +890,11 @@ __device__ __forceinline__ void dq_block_range(const AttnArgs& a, const Seq& s, 
 template <int DQK, int DC, typename TIn>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   constexpr int BN = 128, NT = 512, NDK = DC / 32;
+  using CT = ct_t<TIn>;   // matrix-core operand type
+  using CT8 = vec8<CT>;
   constexpr int KP = tr_pitch(DC);   // K is read only through transpose reads
   static_assert(DQK % DC == 0, "whole column chunks");
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KP];
+  __shared__ __attribute__((aligned(16))) CT Ks[BN * KP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
@@ -924,14 +930,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   // (waves past the sequence's last tile read that tile and discard it)
   const int nqt = (s.qlen + 63) / 64;
   const int utc = ut < nqt ? ut : nqt - 1;
-  const bf16* dsw = static_cast<const bf16*>(a.ds) +
+  const CT* dsw = static_cast<const CT*>(a.ds) +
                     ((int64_t)h * a.ds_nu + ds_ubase(a, s, z) + utc) * a.ds_nb * kDsTileElems +
                     ((int64_t)qb2 * 8 * 64 + lane) * 8;
-  auto load_frags = [&](int kt, bf16x8* f) {
-    const bf16* p = dsw + (int64_t)(kt - a.kt0) * kDsTileElems;
+  auto load_frags = [&](int kt, CT8* f) {
+    const CT* p = dsw + (int64_t)(kt - a.kt0) * kDsTileElems;
 #pragma unroll
     for (int t = 0; t < 8; ++t)   // streamed once: non-temporal, K keeps L2
-      f[t] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p + 512 * t));
+      f[t] = __builtin_nontemporal_load(reinterpret_cast<const CT8*>(p + 512 * t));
   };
 
   f32x16 acc[NDK];
@@ -946,11 +952,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   // accumulators fit without spilling.
   constexpr int AHEAD = NDK > 6 ? 1 : 2;
   TileStage<BN, DC, TIn, NT, true> kst;
-  bf16x8 fa[8], fb[8], fc[AHEAD == 2 ? 8 : 1];
+  CT8 fa[8], fb[8], fc[AHEAD == 2 ? 8 : 1];
   kst.load(K + kbase, a.k_stride[1], kt_begin * BN, s.klen, tid);
   load_frags(kt_begin, fa);
   if (AHEAD == 2 && kt_begin + 1 < kt_end) load_frags(kt_begin + 1, fb);
-  auto body = [&](int kt, const bf16x8 (&cur)[8], bf16x8 (&nn)[8]) {
+  auto body = [&](int kt, const CT8 (&cur)[8], CT8 (&nn)[8]) {
     __syncthreads();
     kst.store(Ks, KP, tid);
     if (kt + 1 < kt_end) kst.load(K + kbase, a.k_stride[1], (kt + 1) * BN, s.klen, tid);
@@ -1069,6 +1075,8 @@ static hipError_t bwd_dtypes(const AttnArgs& a, int in_dt, int out_dt, int step,
   if (in_dt == CPA_BF16 && out_dt == CPA_BF16) return bwd_variant<DQK, DV, bf16, bf16>(a, step, st);
   if (in_dt == CPA_BF16 && out_dt == CPA_FP32) return bwd_variant<DQK, DV, bf16, float>(a, step, st);
   if (in_dt == CPA_FP32 && out_dt == CPA_BF16) return bwd_variant<DQK, DV, float, bf16>(a, step, st);
+  if (in_dt == CPA_FP16 && out_dt == CPA_FP16) return bwd_variant<DQK, DV, f16, f16>(a, step, st);
+  if (in_dt == CPA_FP16 && out_dt == CPA_FP32) return bwd_variant<DQK, DV, f16, float>(a, step, st);
   return bwd_variant<DQK, DV, float, float>(a, step, st);
 }
 

@@ -1,6 +1,6 @@
-// Device helpers for the gfx950 attention kernels: bf16 vector types, the
-// 32x32x16 bf16 matrix-core product, element loads with bf16 rounding, LDS
-// transpose reads, and per-sequence position bookkeeping.
+// Device helpers for the gfx950 attention kernels: bf16 / fp16 vector types,
+// the 32x32x16 matrix-core products, element loads with rounding to the
+// operand type, LDS transpose reads, and per-sequence position bookkeeping.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -15,6 +15,42 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x4_tr __attribute__((__vector_size__(8)));   // transpose-read result
+typedef __attribute__((address_space(3))) fp16x4_tr lds_f16x4;
+
+// Vectors of a 2-byte element type.
+template <typename T>
+struct Vec;
+template <>
+struct Vec<bf16> {
+  using x8 = bf16x8;
+  using x4 = bf16x4;
+};
+template <>
+struct Vec<f16> {
+  using x8 = f16x8;
+  using x4 = f16x4;
+};
+template <typename T>
+using vec8 = typename Vec<T>::x8;
+template <typename T>
+using vec4 = typename Vec<T>::x4;
+
+// Matrix-core operand type for an input type: fp16 inputs stay fp16; bf16
+// and fp32 inputs run as bf16 (fp32 is rounded on load).
+template <typename TIn>
+struct Compute {
+  using T = bf16;
+};
+template <>
+struct Compute<f16> {
+  using T = f16;
+};
+template <typename TIn>
+using ct_t = typename Compute<TIn>::T;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -27,6 +63,10 @@ constexpr float kInf = __builtin_huge_valf();
 // in-bounds probe before any kernel was written.)
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// The same product with fp16 operands (same register layout).
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Accumulator row of element v for a lane in half `hh` when the A operand's
@@ -97,6 +137,12 @@ struct Elem<bf16> {
   }
 };
 template <>
+struct Elem<f16> {
+  static __device__ __forceinline__ f16x8 load8(const f16* p) {
+    return *reinterpret_cast<const f16x8*>(p);
+  }
+};
+template <>
 struct Elem<float> {
   // 8 consecutive fp32, 16-byte aligned, rounded to bf16 (nearest even).
   static __device__ __forceinline__ bf16x8 load8(const float* p) {
@@ -112,11 +158,20 @@ struct Elem<float> {
 template <typename T>
 __device__ __forceinline__ float to_f32(T x) { return (float)x; }
 
-__device__ __forceinline__ bf16x8 zero8() {
-  bf16x8 z;
+template <typename T = bf16>
+__device__ __forceinline__ vec8<T> zero8() {
+  vec8<T> z;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) z[i] = (bf16)0.0f;
+  for (int i = 0; i < 8; ++i) z[i] = (T)0.0f;
   return z;
+}
+
+// One ds_read_b64_tr_b16 of a bf16 or fp16 tile.
+__device__ __forceinline__ bf16x4 lds_tr4(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+__device__ __forceinline__ f16x4 lds_tr4(const f16* p) {
+  return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4*)p));
 }
 
 // Two LDS transpose reads (ds_read_b64_tr_b16) assemble one 8-element MFMA
@@ -124,12 +179,12 @@ __device__ __forceinline__ bf16x8 zero8() {
 // group of 16 lanes, output lane j receives M[k0+e][m0+j] for e = 0..3 when
 // source lane s points at M[k0 + s/4][m0 + 4*(s%4)]; the second read covers
 // k0+4..k0+7.  The caller picks k0, m0 per 16-lane group.
-__device__ __forceinline__ bf16x8 lds_tr8(const bf16* tile, int pitch, int k0,
-                                          int m0, int s) {
-  const bf16* p0 = tile + (k0 + (s >> 2)) * pitch + m0 + 4 * (s & 3);
-  const bf16* p1 = p0 + 4 * pitch;
-  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
-  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
+template <typename T>
+__device__ __forceinline__ vec8<T> lds_tr8(const T* tile, int pitch, int k0, int m0, int s) {
+  const T* p0 = tile + (k0 + (s >> 2)) * pitch + m0 + 4 * (s & 3);
+  const T* p1 = p0 + 4 * pitch;
+  const vec4<T> a = lds_tr4(p0);
+  const vec4<T> b = lds_tr4(p1);
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -145,18 +200,19 @@ __device__ __forceinline__ int rperm16(int r) {
 }
 // lds_tr8 on a row-permuted tile (k0 a multiple of 8): the second read's
 // rows k0+4.. are the next physical row.
-__device__ __forceinline__ bf16x8 lds_tr8p(const bf16* tile, int pitch, int k0, int m0, int s) {
-  const bf16* p0 = tile + rperm16(k0 + (s >> 2)) * pitch + m0 + 4 * (s & 3);
-  const bf16* p1 = p0 + pitch;
-  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
-  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
+template <typename T>
+__device__ __forceinline__ vec8<T> lds_tr8p(const T* tile, int pitch, int k0, int m0, int s) {
+  const T* p0 = tile + rperm16(k0 + (s >> 2)) * pitch + m0 + 4 * (s & 3);
+  const T* p1 = p0 + pitch;
+  const vec4<T> a = lds_tr4(p0);
+  const vec4<T> b = lds_tr4(p1);
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Operand from a row-major LDS tile read along rows (16-byte read).
-__device__ __forceinline__ bf16x8 lds_row8(const bf16* tile, int pitch, int r,
-                                           int c) {
-  return *reinterpret_cast<const bf16x8*>(tile + r * pitch + c);
+template <typename T>
+__device__ __forceinline__ vec8<T> lds_row8(const T* tile, int pitch, int r, int c) {
+  return *reinterpret_cast<const vec8<T>*>(tile + r * pitch + c);
 }
 
 // Combine a per-lane value over the two 32-lane halves of a wave.  With the
@@ -271,7 +327,7 @@ __device__ __forceinline__ void qpos_range(const AttnArgs& a, const Seq& s, int 
 
 __device__ __forceinline__ int kpos0(const AttnArgs& a) { return a.thd ? 0 : a.k_pos0; }
 
-// Cooperative staging of a [ROWS x D] bf16 tile through registers: thread
+// Cooperative staging of a [ROWS x D] tile (operand type ct_t<TIn>) through registers: thread
 // t owns rows (t/8) + 32*i and 16-byte column chunks (t%8) + 8*j, so eight
 // neighbouring threads read one row's 128 contiguous bytes and every offset
 // is a compile-time immediate.  load() fetches rows [r0, r0+ROWS) of the
@@ -286,7 +342,8 @@ struct TileStage {
   static constexpr int RP = NT / 8;   // rows covered per pass
   static constexpr int RI = ROWS / RP, CJ = D / 64;
   static_assert(ROWS % RP == 0 && D % 64 == 0, "tile shape");
-  bf16x8 v[RI][CJ];
+  using CT = ct_t<TIn>;
+  vec8<CT> v[RI][CJ];
   __device__ __forceinline__ void load(const TIn* base, int64_t row_stride, int r0, int limit,
                                        int tid) {
     const int rg = tid >> 3, cp = (tid & 7) * 8;
@@ -307,46 +364,48 @@ struct TileStage {
         const TIn* p = base + (int64_t)rc * row_stride + cp;
 #pragma unroll
         for (int j = 0; j < CJ; ++j) {
-          const bf16x8 x = Elem<TIn>::load8(p + 64 * j);
-          v[i][j] = r < limit ? x : zero8();
+          const vec8<CT> x = Elem<TIn>::load8(p + 64 * j);
+          v[i][j] = r < limit ? x : zero8<CT>();
         }
       } else {
         const TIn* p = base + (int64_t)r * row_stride + cp;
 #pragma unroll
-        for (int j = 0; j < CJ; ++j) v[i][j] = r < limit ? Elem<TIn>::load8(p + 64 * j) : zero8();
+        for (int j = 0; j < CJ; ++j)
+          v[i][j] = r < limit ? Elem<TIn>::load8(p + 64 * j) : zero8<CT>();
       }
     }
   }
   // Direct copy with few registers live (at most two chunks in flight).
   static __device__ __forceinline__ void copy(const TIn* base, int64_t row_stride, int r0,
-                                              int limit, bf16* tile, int pitch, int tid) {
+                                              int limit, CT* tile, int pitch, int tid) {
     const int rg = tid >> 3, cp = (tid & 7) * 8;
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
       const int r = r0 + rg + RP * i;
       const TIn* p = base + (int64_t)r * row_stride + cp;
-      bf16* t = tile + (rg + RP * i) * pitch + cp;
+      CT* t = tile + (rg + RP * i) * pitch + cp;
 #pragma unroll 2
       for (int j = 0; j < CJ; ++j)
-        *reinterpret_cast<bf16x8*>(t + 64 * j) = r < limit ? Elem<TIn>::load8(p + 64 * j) : zero8();
+        *reinterpret_cast<vec8<CT>*>(t + 64 * j) =
+            r < limit ? Elem<TIn>::load8(p + 64 * j) : zero8<CT>();
     }
   }
-  __device__ __forceinline__ void store(bf16* tile, int pitch, int tid) const {
+  __device__ __forceinline__ void store(CT* tile, int pitch, int tid) const {
     const int rg = tid >> 3, cp = (tid & 7) * 8;
 #pragma unroll
     for (int i = 0; i < RI; ++i)
 #pragma unroll
       for (int j = 0; j < CJ; ++j)
-        *reinterpret_cast<bf16x8*>(tile + (rg + RP * i) * pitch + cp + 64 * j) = v[i][j];
+        *reinterpret_cast<vec8<CT>*>(tile + (rg + RP * i) * pitch + cp + 64 * j) = v[i][j];
   }
   // The same into a row-permuted tile (row r goes to rperm16(r)).
-  __device__ __forceinline__ void store_rperm(bf16* tile, int pitch, int tid) const {
+  __device__ __forceinline__ void store_rperm(CT* tile, int pitch, int tid) const {
     const int rg = tid >> 3, cp = (tid & 7) * 8;
 #pragma unroll
     for (int i = 0; i < RI; ++i)
 #pragma unroll
       for (int j = 0; j < CJ; ++j)
-        *reinterpret_cast<bf16x8*>(tile + rperm16(rg + RP * i) * pitch + cp + 64 * j) = v[i][j];
+        *reinterpret_cast<vec8<CT>*>(tile + rperm16(rg + RP * i) * pitch + cp + 64 * j) = v[i][j];
   }
 };
 

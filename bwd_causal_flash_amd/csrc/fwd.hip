@@ -34,11 +34,13 @@ constexpr int fwd_blocks_per_cu() { return DSUM <= 320 ? 2 : 1; }
 template <int DQK, int DVC, int NCH, typename TIn, typename TOut, bool WIN>
 __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kernel(const AttnArgs a) {
   constexpr int BM = 128, BN = 64;
+  using CT = ct_t<TIn>;   // matrix-core operand type
+  using CT8 = vec8<CT>;
   constexpr int KP = lds_pitch(DQK), VP = tr_pitch(DVC);   // V: transpose reads only
   constexpr int KS = DQK / 16;
   constexpr int NDB = DVC / 32;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[BN * VP];
+  __shared__ __attribute__((aligned(16))) CT Ks[BN * KP];
+  __shared__ __attribute__((aligned(16))) CT Vs[BN * VP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
@@ -88,12 +90,12 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
   const int ntiles = (kend + BN - 1) / BN;
 
   // This lane's query row as the B operand of S^T = K Q^T, for all k-steps.
-  bf16x8 qreg[KS];
+  CT8 qreg[KS];
   {
     const TIn* qrow = Q + qbase + (int64_t)qi * a.q_stride[1] + (int64_t)h * a.q_stride[2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qreg[ks] = qvalid ? Elem<TIn>::load8(qrow + ks * 16 + hh * 8) : zero8();
+      qreg[ks] = qvalid ? Elem<TIn>::load8(qrow + ks * 16 + hh * 8) : zero8<CT>();
   }
 
   f32x16 oacc[NDB];
@@ -185,9 +187,9 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
 
 #pragma unroll
     for (int st = 0; st < BN / 16; ++st) {
-      bf16x8 pb;
+      CT8 pb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (bf16)x[st >> 1][8 * (st & 1) + e];
+      for (int e = 0; e < 8; ++e) pb[e] = (CT)x[st >> 1][8 * (st & 1) + e];
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
         oacc[db] = mfma32(lds_tr8(Vs, VP, 16 * st + 8 * (grp >> 1), db * 32 + 16 * (grp & 1), gl),
@@ -204,10 +206,10 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
     for (int a4 = 0; a4 < 4; ++a4) {
       const int d = db * 32 + 8 * a4 + 4 * hh;
       if constexpr (sizeof(TOut) == 2) {
-        bf16x4 w;
+        vec4<TOut> w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)(oacc[db][4 * a4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + d) = w;
+        for (int e = 0; e < 4; ++e) w[e] = (TOut)(oacc[db][4 * a4 + e] * inv);
+        *reinterpret_cast<vec4<TOut>*>(orow + d) = w;
       } else {
         float4 w = make_float4(oacc[db][4 * a4 + 0] * inv, oacc[db][4 * a4 + 1] * inv,
                                oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv);
@@ -261,6 +263,8 @@ static hipError_t fwd_dtypes(const AttnArgs& a, int in_dt, int out_dt, hipStream
   if (in_dt == CPA_BF16 && out_dt == CPA_BF16) return fwd_variant<DQK, DV, bf16, bf16>(a, st);
   if (in_dt == CPA_BF16 && out_dt == CPA_FP32) return fwd_variant<DQK, DV, bf16, float>(a, st);
   if (in_dt == CPA_FP32 && out_dt == CPA_BF16) return fwd_variant<DQK, DV, float, bf16>(a, st);
+  if (in_dt == CPA_FP16 && out_dt == CPA_FP16) return fwd_variant<DQK, DV, f16, f16>(a, st);
+  if (in_dt == CPA_FP16 && out_dt == CPA_FP32) return fwd_variant<DQK, DV, f16, float>(a, st);
   return fwd_variant<DQK, DV, float, float>(a, st);
 }
 

@@ -26,18 +26,23 @@ struct Vec4<float> {
     *reinterpret_cast<float4*>(p) = v;
   }
 };
-template <>
-struct Vec4<bf16> {
-  static __device__ __forceinline__ float4 load(const bf16* p) {
-    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+// 2-byte types (bf16, fp16): converted to and from fp32 (nearest even).
+template <typename T>
+struct Vec4Half {
+  static __device__ __forceinline__ float4 load(const T* p) {
+    const vec4<T> v = *reinterpret_cast<const vec4<T>*>(p);
     return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
   }
-  static __device__ __forceinline__ void store(bf16* p, float4 v) {
-    bf16x4 w;
-    w[0] = (bf16)v.x; w[1] = (bf16)v.y; w[2] = (bf16)v.z; w[3] = (bf16)v.w;
-    *reinterpret_cast<bf16x4*>(p) = w;
+  static __device__ __forceinline__ void store(T* p, float4 v) {
+    vec4<T> w;
+    w[0] = (T)v.x; w[1] = (T)v.y; w[2] = (T)v.z; w[3] = (T)v.w;
+    *reinterpret_cast<vec4<T>*>(p) = w;
   }
 };
+template <>
+struct Vec4<bf16> : Vec4Half<bf16> {};
+template <>
+struct Vec4<f16> : Vec4Half<f16> {};
 
 template <typename TA, typename TP, typename TO, int G>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs m) {
@@ -101,20 +106,23 @@ static hipError_t merge_variant(const MergeArgs& m, hipStream_t st) {
 
 template <typename TA, typename TP>
 static hipError_t merge_out(const MergeArgs& m, int out_dt, hipStream_t st) {
-  return out_dt == CPA_BF16 ? merge_variant<TA, TP, bf16>(m, st)
-                            : merge_variant<TA, TP, float>(m, st);
+  if (out_dt == CPA_BF16) return merge_variant<TA, TP, bf16>(m, st);
+  if (out_dt == CPA_FP16) return merge_variant<TA, TP, f16>(m, st);
+  return merge_variant<TA, TP, float>(m, st);
 }
 
 template <typename TA>
 static hipError_t merge_part(const MergeArgs& m, int part_dt, int out_dt, hipStream_t st) {
-  return part_dt == CPA_BF16 ? merge_out<TA, bf16>(m, out_dt, st)
-                             : merge_out<TA, float>(m, out_dt, st);
+  if (part_dt == CPA_BF16) return merge_out<TA, bf16>(m, out_dt, st);
+  if (part_dt == CPA_FP16) return merge_out<TA, f16>(m, out_dt, st);
+  return merge_out<TA, float>(m, out_dt, st);
 }
 
 hipError_t launch_merge(const MergeArgs& m, int acc_dt, int part_dt, int out_dt,
                         hipStream_t st) {
-  return acc_dt == CPA_BF16 ? merge_part<bf16>(m, part_dt, out_dt, st)
-                            : merge_part<float>(m, part_dt, out_dt, st);
+  if (acc_dt == CPA_BF16) return merge_part<bf16>(m, part_dt, out_dt, st);
+  if (acc_dt == CPA_FP16) return merge_part<f16>(m, part_dt, out_dt, st);
+  return merge_part<float>(m, part_dt, out_dt, st);
 }
 
 // ------------------------------------------------------------------- pack

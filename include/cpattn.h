@@ -48,10 +48,13 @@
  * LSE is fp32: BSHD element (b, h, s) at lse + b*lse_stride[0] +
  * h*lse_stride[1] + s; THD element (h, t) at lse + h*lse_stride[1] + t.
  *
- * Data types.  Inputs are bf16 or fp32 (fp32 inputs are rounded to bf16,
- * round-to-nearest-even, as they are loaded: the matrix products always run
- * as bf16 x bf16 -> fp32 on the matrix cores).  Softmax statistics and all
- * accumulation are fp32.  Outputs are bf16 or fp32.
+ * Data types.  Inputs are bf16, fp32 or fp16.  bf16 and fp32 inputs run
+ * the matrix products as bf16 x bf16 -> fp32 (fp32 inputs are rounded to
+ * bf16, round-to-nearest-even, as they are loaded); fp16 inputs run them as
+ * fp16 x fp16 -> fp32, with P and dS rounded to fp16 (the pages cover FP16
+ * and BF16: TransformerEngine PR 3510, Description).  Softmax statistics and
+ * all accumulation are fp32.  Outputs are bf16 or fp32 for bf16 / fp32
+ * inputs, fp16 or fp32 for fp16 inputs (other pairs are declined).
  *
  * Ownership and errors.  The caller owns every buffer, the workspace and
  * the stream; the library allocates nothing and keeps no per-call state, so
@@ -92,7 +95,7 @@ typedef enum cpa_status {
   CPA_ERR_LAUNCH = 9       /* the HIP runtime reported a launch error */
 } cpa_status;
 
-enum { CPA_BF16 = 0, CPA_FP32 = 1 };
+enum { CPA_BF16 = 0, CPA_FP32 = 1, CPA_FP16 = 2 };
 enum { CPA_LAYOUT_BSHD = 0, CPA_LAYOUT_THD = 1 };
 enum { CPA_MAX_SEGMENTS = 8 };
 enum { CPA_FLAG_DETERMINISTIC = 1 };
@@ -260,7 +263,7 @@ cpa_status attn_bwd_post(const cpa_problem* p, const void* q, const void* k,
 typedef struct cpa_merge_desc {
   int32_t batch, heads, d_v;
   int64_t seqlen;
-  int32_t acc_dtype, part_dtype, out_dtype;    /* CPA_BF16 / CPA_FP32 */
+  int32_t acc_dtype, part_dtype, out_dtype;    /* CPA_BF16 / CPA_FP32 / CPA_FP16 */
   int64_t acc_stride[3], part_stride[3], out_stride[3];
   int64_t lse_acc_stride[2], lse_part_stride[2], lse_out_stride[2];
 } cpa_merge_desc;

@@ -50,6 +50,10 @@ def main():
          lib.attn_fwd(None, ptr(1), ptr(2), ptr(3), ptr(4), ptr(5), ptr(6), 256, None))
     p = good_problem(); p.in_dtype = 7
     case("bad_dtype", "CPA_ERR_DTYPE", fwd(p))
+    p = good_problem(); p.in_dtype, p.out_dtype = 2, 0
+    case("fp16_in_bf16_out_declined", "CPA_ERR_UNSUPPORTED", fwd(p))
+    p = good_problem(); p.in_dtype, p.out_dtype = 0, 2
+    case("bf16_in_fp16_out_declined", "CPA_ERR_UNSUPPORTED", fwd(p))
     p = good_problem(); p.heads_q = 3
     case("gqa_not_divisible", "CPA_ERR_SHAPE", fwd(p))
     p = good_problem(d_qk=96, d_v=96)

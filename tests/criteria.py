@@ -60,16 +60,23 @@ def round_bf16(x):
     return torch.from_numpy(np.ascontiguousarray(as64(x))).to(torch.bfloat16).double().numpy()
 
 
+def round_fp16(x):
+    """Round to IEEE half (nearest even) and return fp64."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(as64(x))).to(torch.float16).double().numpy()
+
+
 def _ratio(err, floor):
     return err / (2 * floor) if floor > 0 else (0.0 if err == 0 else float("inf"))
 
 
 def evaluate(gpu, true, naive, *, mask=None, grad=False, out_bf16=False):
     """Return a dict with err, floor, ratio (= err / (2*floor)), rel_l2 and
-    pass flags.  ``out_bf16``: the kernel's output dtype is bf16, so the
-    naive reference's results are stored in bf16 too."""
+    pass flags.  ``out_bf16``: the kernel's output dtype is bf16 (True or
+    "bf16") or fp16 ("fp16"), so the naive reference's results are stored
+    in that type too."""
     g, t, n = as64(gpu), as64(true), as64(naive)
-    n_out = round_bf16(n) if out_bf16 else n
+    n_out = round_fp16(n) if out_bf16 == "fp16" else (round_bf16(n) if out_bf16 else n)
     err = max_err(g, t, mask)
     floor = max_err(n_out, t, mask)
     res = {"err": err, "floor": floor, "ratio": _ratio(err, floor),

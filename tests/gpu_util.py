@@ -29,6 +29,12 @@ def naive64(x: torch.Tensor) -> np.ndarray:
     return x.detach().to(torch.bfloat16).to("cpu", torch.float64).numpy()
 
 
+def naive16(x: torch.Tensor) -> np.ndarray:
+    """fp16-rounded draws (nearest even) in fp64: the kernel's inputs on the
+    fp16 path."""
+    return x.detach().to(torch.float16).to("cpu", torch.float64).numpy()
+
+
 def to_gpu(x: torch.Tensor, dtype) -> torch.Tensor:
     return x.to(dtype).to(dev())
 
