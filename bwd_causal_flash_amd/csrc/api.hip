@@ -207,8 +207,13 @@ int64_t ds_key_blocks(const cpa_problem* p) {
   const int64_t kr = p->layout == CPA_LAYOUT_THD ? p->max_seqlen_k : p->seqlen_k;
   return (kr + 127) / 128;
 }
-size_t ds_block_bytes(const cpa_problem* p) {
+// dS tiles of one key block; head dims 256 and 512 also keep the P tiles.
+size_t ds_part_bytes(const cpa_problem* p) {
   return (size_t)p->heads_q * (size_t)ds_tile_rows(p) * kDsTileBytes;
+}
+bool keeps_p(const cpa_problem* p) { return p->d_qk + p->d_v > 320; }
+size_t ds_block_bytes(const cpa_problem* p) {
+  return ds_part_bytes(p) * (keeps_p(p) ? 2 : 1);
 }
 size_t tile_pos_bytes(const cpa_problem* p) {
   return align_up((size_t)ds_tile_rows(p) * 16);
@@ -238,6 +243,8 @@ void set_bwd_ws(AttnArgs& a, const cpa_problem* p, void* ws, size_t ws_bytes) {
   a.ds = base + bwd_base_bytes(p);
   a.ds_nu = ds_tile_rows(p);
   a.ds_nb = (int)((int64_t)room < nkb ? (int64_t)room : nkb);
+  // P tiles follow the dS tiles of the whole band
+  a.ps = keeps_p(p) ? static_cast<char*>(a.ds) + ds_part_bytes(p) * (size_t)a.ds_nb : nullptr;
 }
 
 }  // namespace

@@ -5,25 +5,22 @@
 // Launches on the caller's stream:
 //   pre   D_i = <dO_i, O_i> in fp32 from the saved O, and zero the fp32 dQ
 //         accumulator (only real rows; padding is never touched);
-//   main  key-outer: one workgroup owns 128 keys of one kv head and walks
-//         the query heads of its GQA group and the query tiles that can see
-//         those keys, accumulating dK and dV;
-//   dq    query-outer dQ_acc += dS K from the dS tiles main stored in the
-//         workspace (plain read-add-write, no atomics: deterministic);
+//   main  key-outer: dK, dV and the dS tiles of a band of key blocks
+//         (head dims up to D_qk + D_v = 320: the fused kv kernel; 256 and
+//         512: the sdp kernel writes P and dS tiles, the dkv kernel reduces
+//         dK and dV from them);
+//   dq    query-outer dQ_acc += dS K from the dS tiles in the workspace
+//         (plain read-add-write, no atomics: deterministic);
 //   post  dQ = s * acc, rounded to the output type.
 //
-// Inside main a wave computes S = Q K_w^T and dP = dO V_w^T for its 32 keys
-// (lane = key column), forms P = exp(S - LSE) (zero where masked or where
-// LSE = -inf) and dS = P (dP - D), and accumulates dV^T += dO^T P and
+// In the kv kernel a wave computes S = Q K_w^T and dP = dO V_w^T for its 32
+// keys (lane = key column), forms P = exp(S - LSE) (zero where masked or
+// where LSE = -inf) and dS = P (dP - D), and accumulates dV^T += dO^T P and
 // dK^T += Q^T dS.  The reduction operands dO^T and Q^T are read from the
 // row-major LDS tiles with the transpose reads; P and dS feed the products
 // directly from the accumulators because the Q rows were loaded in perm32
-// order.  All products are bf16 x bf16 -> fp32 on the matrix cores.
-//
-// Head dims up to D_qk + D_v = 320 run the 8-wave kv kernel below; 256 and
-// 512 run a 4-wave kernel over 32-row query blocks, and for 512 dK and dV
-// are produced in two column chunks of 256 by separate workgroups (S and dP
-// recomputed per chunk) with K_w, V_w read from global memory.
+// order.  All products run on the matrix cores (bf16 or fp16 operands,
+// fp32 accumulation).
 #include "device_common.h"
 
 namespace cpa {
@@ -108,318 +105,7 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(const AttnArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- main
-
 __device__ __forceinline__ int64_t ds_ubase(const AttnArgs& a, const Seq& s, int z);
-
-template <int DQK, int DV, int OCK, int OCV, int BM, typename TIn, typename TOut, bool WIN>
-__global__ __launch_bounds__(256, 1) void bwd_main_kernel(const AttnArgs a) {
-  constexpr int BN = 128;
-  using CT = ct_t<TIn>;   // matrix-core operand type
-  using CT8 = vec8<CT>;
-  constexpr int QP = lds_pitch(DQK), OP = lds_pitch(DV), SP = lds_pitch(BM), KP = lds_pitch(OCK);
-  constexpr int NQB = BM / 32;
-  constexpr int KSQ = DQK / 16, KSV = DV / 16;
-  constexpr int NDK = OCK / 32, NDV = OCV / 32;
-  // The workgroup's K tile in LDS serves both the dQ product and, read
-  // along rows, the B operand of S = Q K^T.  For small head dims the V tile
-  // is staged too (B operand of dP = dO V^T) and the next query tile is
-  // prefetched into registers during the current one; large head dims lack
-  // the registers and LDS for that and read V (and K, when only a column
-  // chunk of it is staged) from global memory.
-  constexpr bool SMALL = DQK + DV <= 320;
-  constexpr bool K_FROM_LDS = OCK == DQK;
-  constexpr bool V_FROM_LDS = SMALL;
-  constexpr bool PREFETCH = SMALL;
-  constexpr int VP = lds_pitch(DV);
-  __shared__ __attribute__((aligned(16))) CT Qs[BM * QP];
-  __shared__ __attribute__((aligned(16))) CT dOs[BM * OP];
-  __shared__ __attribute__((aligned(16))) CT dSt[BN * SP];
-  __shared__ __attribute__((aligned(16))) CT Ks[BN * KP];
-  __shared__ __attribute__((aligned(16))) CT Vs[V_FROM_LDS ? BN * VP : 8];
-  __shared__ __attribute__((aligned(16))) float Ls[BM];
-  __shared__ __attribute__((aligned(16))) float Dl[BM];
-  __shared__ int Ps[BM];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
-  const int kvh = blockIdx.x % a.heads_kv;
-  const int ch = blockIdx.x / a.heads_kv;
-  const int kt = a.kt0 + blockIdx.y;
-  const int z = blockIdx.z;
-  const Seq s = load_seq(a, z);
-  const int j0 = kt * BN;
-  if (j0 >= s.klen) return;
-  const int kp0 = kpos0(a);
-  const Band<WIN> bd(a);
-
-  const int jw = j0 + wave * 32;
-  const int my_key = jw + lq;
-  const bool key_valid = my_key < s.klen;
-  const int my_kpos = kp0 + my_key;
-  const bool wave_has_keys = jw < s.klen;
-  const int wk_last = min(jw + 31, s.klen - 1);
-  const int wkpos_lo = kp0 + jw, wkpos_hi = kp0 + wk_last;
-  const int gkpos_lo = kp0 + j0, gkpos_hi = kp0 + min(j0 + BN, s.klen) - 1;
-
-  const TIn* Q = static_cast<const TIn*>(a.q);
-  const TIn* K = static_cast<const TIn*>(a.k);
-  const TIn* V = static_cast<const TIn*>(a.v);
-  const TIn* dO = static_cast<const TIn*>(a.dout);
-  const int64_t kbase = (a.thd ? s.k_row0 * a.k_stride[1] : (int64_t)z * a.k_stride[0]) +
-                        (int64_t)kvh * a.k_stride[2];
-  const int64_t vbase = (a.thd ? s.k_row0 * a.v_stride[1] : (int64_t)z * a.v_stride[0]) +
-                        (int64_t)kvh * a.v_stride[2];
-  const TIn* krow = K + kbase + (int64_t)(key_valid ? my_key : 0) * a.k_stride[1];
-  const TIn* vrow = V + vbase + (int64_t)(key_valid ? my_key : 0) * a.v_stride[1];
-
-  // K tile (this workgroup's column chunk) for the dQ product; V tile.
-  TileStage<BN, OCK, TIn>::copy(K + kbase + ch * OCK, a.k_stride[1], j0, s.klen, Ks, KP, tid);
-  if constexpr (V_FROM_LDS)
-    TileStage<BN, DV, TIn>::copy(V + vbase, a.v_stride[1], j0, s.klen, Vs, VP, tid);
-
-  f32x16 dkacc[NDK], dvacc[NDV];
-#pragma unroll
-  for (int d = 0; d < NDK; ++d)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) dkacc[d][v] = 0.f;
-#pragma unroll
-  for (int d = 0; d < NDV; ++d)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) dvacc[d][v] = 0.f;
-
-  const int pr = perm32(lq);
-  const int nqt = (s.qlen + BM - 1) / BM;
-  const int total = a.group * nqt;
-  // Query blocks whose enclosing 64-row dS tile precedes this workgroup's
-  // first key see none of its keys and are skipped (causal tile skipping).
-  // Visibility is decided per 64-row tile, because the dQ kernel reads whole
-  // tiles: both halves of a visible tile are visited (a half that sees no
-  // key stores zeros).
-  auto visible = [&](int u) -> bool {
-    if (!a.causal && !bd.left) return true;
-    const int t0 = ((u % nqt) * BM) & ~63;
-    int lo, hi;
-    qpos_range(a, s, t0, min(t0 + 64, s.qlen), lo, hi);
-    return (!a.causal || hi + bd.wr >= gkpos_lo) && (!bd.left || lo - bd.wl <= gkpos_hi);
-  };
-  auto tile_of = [&](int k) -> int { return k; };
-  auto next_visible = [&](int k) -> int {
-    while (k < total && !visible(tile_of(k))) ++k;
-    return k;
-  };
-
-  TileStage<PREFETCH ? BM : 32, PREFETCH ? DQK : 64, TIn> qst;
-  TileStage<PREFETCH ? BM : 32, PREFETCH ? DV : 64, TIn> dost;
-  float pre_l = 0.f, pre_d = 0.f;
-  int pre_p = 0;
-  // Fetch query tile u: into registers (prefetch) or straight into LDS.
-  auto fetch = [&](int u) {
-    const int h = kvh * a.group + u / nqt;
-    const int i0 = (u % nqt) * BM;
-    const int64_t qb = (a.thd ? s.q_row0 * a.q_stride[1] : (int64_t)z * a.q_stride[0]) +
-                       (int64_t)h * a.q_stride[2];
-    const int64_t dob = (a.thd ? s.q_row0 * a.do_stride[1] : (int64_t)z * a.do_stride[0]) +
-                        (int64_t)h * a.do_stride[2];
-    if constexpr (PREFETCH) {
-      qst.load(Q + qb, a.q_stride[1], i0, s.qlen, tid);
-      dost.load(dO + dob, a.do_stride[1], i0, s.qlen, tid);
-    } else {
-      TileStage<BM, DQK, TIn>::copy(Q + qb, a.q_stride[1], i0, s.qlen, Qs, QP, tid);
-      TileStage<BM, DV, TIn>::copy(dO + dob, a.do_stride[1], i0, s.qlen, dOs, OP, tid);
-    }
-    if (tid < BM) {
-      const int i = i0 + tid;
-      const bool ok = i < s.qlen;
-      const int64_t lb = (a.thd ? s.q_row0 : (int64_t)z * a.lse_stride[0]) +
-                         (int64_t)h * a.lse_stride[1];
-      const int64_t db = (a.thd ? s.q_row0 : (int64_t)z * a.delta_stride[0]) +
-                         (int64_t)h * a.delta_stride[1];
-      const float l = ok ? a.lse[lb + i] : -kInf;
-      // rows past the end or without any key: P must be exactly 0
-      pre_l = (l == -kInf) ? kInf : l * kLog2e;
-      pre_d = ok ? a.delta[db + i] : 0.f;
-      pre_p = qpos(a, s, i);
-    }
-  };
-
-  int k = next_visible(0);
-  if (PREFETCH && k < total) fetch(tile_of(k));
-  while (k < total) {
-    const int u = tile_of(k);
-    const int hg = u / nqt;
-    const int h = kvh * a.group + hg;
-    const int i0 = (u % nqt) * BM;
-    const int i1 = min(i0 + BM, s.qlen);
-    int tlo, thi;
-    qpos_range(a, s, i0, i1, tlo, thi);
-    __syncthreads();
-    if constexpr (PREFETCH) {
-      qst.store(Qs, QP, tid);
-      dost.store(dOs, OP, tid);
-    } else {
-      fetch(u);
-    }
-    if (tid < BM) {
-      Ls[tid] = pre_l;
-      Dl[tid] = pre_d;
-      Ps[tid] = pre_p;
-    }
-    const int kn = next_visible(k + 1);
-    if (PREFETCH && kn < total) fetch(tile_of(kn));
-    __syncthreads();
-
-    const bool wave_on = wave_has_keys && (!a.causal || thi + bd.wr >= wkpos_lo) &&
-                         (!bd.left || tlo - bd.wl <= wkpos_hi);
-    if (wave_on) {
-      const bool need_mask = (jw + 32 > s.klen) || (a.causal && tlo + bd.wr < wkpos_hi) ||
-                             (bd.left && thi - bd.wl > wkpos_lo);
-      // One 32-row query block at a time keeps a single block's S and dP
-      // live; the unrolled loop lets block qb+1's products overlap block
-      // qb's exponentials.
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        f32x16 sacc, pacc;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
-        if constexpr (K_FROM_LDS) {
-#pragma unroll
-          for (int ks = 0; ks < KSQ; ++ks)
-            sacc = mfma32(lds_row8(Qs, QP, qb * 32 + pr, ks * 16 + hh * 8),
-                          lds_row8(Ks, KP, wave * 32 + lq, ks * 16 + hh * 8), sacc);
-        } else {
-#pragma unroll 4
-          for (int ks = 0; ks < KSQ; ++ks) {
-            const CT8 b = key_valid ? Elem<TIn>::load8(krow + ks * 16 + hh * 8) : zero8<CT>();
-            sacc = mfma32(lds_row8(Qs, QP, qb * 32 + pr, ks * 16 + hh * 8), b, sacc);
-          }
-        }
-        if constexpr (V_FROM_LDS) {
-#pragma unroll
-          for (int ks = 0; ks < KSV; ++ks)
-            pacc = mfma32(lds_row8(dOs, OP, qb * 32 + pr, ks * 16 + hh * 8),
-                          lds_row8(Vs, VP, wave * 32 + lq, ks * 16 + hh * 8), pacc);
-        } else {
-#pragma unroll 4
-          for (int ks = 0; ks < KSV; ++ks) {
-            const CT8 b = key_valid ? Elem<TIn>::load8(vrow + ks * 16 + hh * 8) : zero8<CT>();
-            pacc = mfma32(lds_row8(dOs, OP, qb * 32 + pr, ks * 16 + hh * 8), b, pacc);
-          }
-        }
-        // This lane's 16 rows are two runs of 8: qb*32 + 16*vh + 8*hh + e.
-        float lrow[16], drow[16];
-#pragma unroll
-        for (int vh = 0; vh < 2; ++vh) {
-          const int r0 = qb * 32 + 16 * vh + 8 * hh;
-          const float4 l0 = *reinterpret_cast<const float4*>(&Ls[r0]);
-          const float4 l1 = *reinterpret_cast<const float4*>(&Ls[r0 + 4]);
-          const float4 d0 = *reinterpret_cast<const float4*>(&Dl[r0]);
-          const float4 d1 = *reinterpret_cast<const float4*>(&Dl[r0 + 4]);
-          lrow[8 * vh + 0] = l0.x; lrow[8 * vh + 1] = l0.y; lrow[8 * vh + 2] = l0.z; lrow[8 * vh + 3] = l0.w;
-          lrow[8 * vh + 4] = l1.x; lrow[8 * vh + 5] = l1.y; lrow[8 * vh + 6] = l1.z; lrow[8 * vh + 7] = l1.w;
-          drow[8 * vh + 0] = d0.x; drow[8 * vh + 1] = d0.y; drow[8 * vh + 2] = d0.z; drow[8 * vh + 3] = d0.w;
-          drow[8 * vh + 4] = d1.x; drow[8 * vh + 5] = d1.y; drow[8 * vh + 6] = d1.z; drow[8 * vh + 7] = d1.w;
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float p = fast_exp2(__builtin_fmaf(sacc[v], a.scale_log2, -lrow[v]));
-          if (need_mask) {
-            const bool vis = key_valid && band_vis<WIN>(a, my_kpos, Ps[qb * 32 + acc_row_perm(v, hh)]);
-            p = vis ? p : 0.f;
-          }
-          sacc[v] = p;
-          pacc[v] = p * (pacc[v] - drow[v]);
-        }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          CT8 pb, sb;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            pb[e] = (CT)sacc[8 * tt + e];
-            sb[e] = (CT)pacc[8 * tt + e];
-          }
-          const int k0 = 32 * qb + 16 * tt + 8 * (grp >> 1);
-#pragma unroll
-          for (int db = 0; db < NDV; ++db)
-            dvacc[db] = mfma32(lds_tr8(dOs, OP, k0, ch * OCV + db * 32 + 16 * (grp & 1), gl), pb,
-                               dvacc[db]);
-#pragma unroll
-          for (int db = 0; db < NDK; ++db)
-            dkacc[db] = mfma32(lds_tr8(Qs, QP, k0, ch * OCK + db * 32 + 16 * (grp & 1), gl), sb,
-                               dkacc[db]);
-          *reinterpret_cast<CT8*>(&dSt[(wave * 32 + lq) * SP + qb * 32 + 16 * tt + 8 * hh]) = sb;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int hv = 0; hv < 2; ++hv)
-          *reinterpret_cast<CT8*>(&dSt[(wave * 32 + lq) * SP + qb * 32 + 16 * hv + 8 * hh]) =
-              zero8<CT>();
-    }
-    __syncthreads();
-
-    // dS of this 32-row block to the workspace tile (the dQ kernel reduces
-    // it): wave w stores the chunks of keys 32w..32w+31, read transposed from
-    // dS^T in LDS.  Column chunk 0 only (all chunks compute the same dS).
-    static_assert(BM == 32, "dS chunks of 32 query rows");
-    if (ch == 0) {
-      const int ut = i0 >> 6, qb2 = (i0 >> 5) & 1;
-      CT* dst = static_cast<CT*>(a.ds) +
-                  (((int64_t)h * a.ds_nu + ds_ubase(a, s, z) + ut) * a.ds_nb + (kt - a.kt0)) *
-                      (64 * 128) +
-                  ((int64_t)(qb2 * 8 + 2 * wave) * 64 + lane) * 8;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        __builtin_nontemporal_store(
-            lds_tr8(dSt, SP, 16 * (2 * wave + j) + 8 * (grp >> 1), 16 * (grp & 1), gl),
-            reinterpret_cast<CT8*>(dst + 512 * j));
-    }
-    k = kn;
-  }
-
-  if (!key_valid) return;
-  TOut* dK = static_cast<TOut*>(a.dk) +
-             (a.thd ? (s.k_row0 + my_key) * a.dk_stride[1]
-                    : (int64_t)z * a.dk_stride[0] + (int64_t)my_key * a.dk_stride[1]) +
-             (int64_t)kvh * a.dk_stride[2] + ch * OCK;
-  TOut* dV = static_cast<TOut*>(a.dv) +
-             (a.thd ? (s.k_row0 + my_key) * a.dv_stride[1]
-                    : (int64_t)z * a.dv_stride[0] + (int64_t)my_key * a.dv_stride[1]) +
-             (int64_t)kvh * a.dv_stride[2] + ch * OCV;
-#pragma unroll
-  for (int db = 0; db < NDK; ++db)
-#pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      const int d = db * 32 + 8 * a4 + 4 * hh;
-      if constexpr (sizeof(TOut) == 2) {
-        vec4<TOut> w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (TOut)(dkacc[db][4 * a4 + e] * a.scale);
-        *reinterpret_cast<vec4<TOut>*>(dK + d) = w;
-      } else {
-        *reinterpret_cast<float4*>(dK + d) =
-            make_float4(dkacc[db][4 * a4] * a.scale, dkacc[db][4 * a4 + 1] * a.scale,
-                        dkacc[db][4 * a4 + 2] * a.scale, dkacc[db][4 * a4 + 3] * a.scale);
-      }
-    }
-#pragma unroll
-  for (int db = 0; db < NDV; ++db)
-#pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      const int d = db * 32 + 8 * a4 + 4 * hh;
-      if constexpr (sizeof(TOut) == 2) {
-        vec4<TOut> w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (TOut)dvacc[db][4 * a4 + e];
-        *reinterpret_cast<vec4<TOut>*>(dV + d) = w;
-      } else {
-        *reinterpret_cast<float4*>(dV + d) = make_float4(
-            dvacc[db][4 * a4], dvacc[db][4 * a4 + 1], dvacc[db][4 * a4 + 2], dvacc[db][4 * a4 + 3]);
-      }
-    }
-}
 
 // ------------------------------------------------ dS-materialising path
 //
@@ -1007,19 +693,336 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   }
 }
 
+// ------------------------------------------- materialised path (256, 512)
+//
+// For head dims 256 and 512 one query tile's and one key block's operands do
+// not fit the LDS and registers of a CU together with the dK, dV
+// accumulators, so the backward runs as three tiled products:
+//   sdp  per (query head, 128 query rows, 256 keys): S^T = K Q^T and
+//        dP^T = V dO^T over the head dim in 32-wide chunks staged through
+//        LDS, then P = exp(S - LSE) and dS = P (dP - D), written as tiles in
+//        the dq kernel's chunk layout (K rows are read in perm32 order, so
+//        the accumulators already are that layout: lane = query row, 8
+//        consecutive keys per half);
+//   dkv  per (kv head, 128 keys, 128 columns): dV^T += dO^T P and
+//        dK^T += Q^T dS over the query tiles that see the keys, for every
+//        query head of the group, P and dS read back through LDS;
+//   dq   dQ += dS K as for the other head dims.
+// Tiles a key block does not see are neither written nor read (the same
+// block ranges as the dq kernel).
+
+// Whether 64-row query tile ut sees key block kt (dq_block_range bounds).
+__device__ __forceinline__ bool tile_sees_block(const AttnArgs& a, const Seq& s, int ut, int kt,
+                                                int nkb, int kp0) {
+  int f, l;
+  dq_block_range(a, s, ut, nkb, kp0, f, l);
+  return kt >= f && kt <= l;
+}
+
+template <int D, typename TIn, bool WIN>
+__global__ __launch_bounds__(512, 1) void bwd_sdp_kernel(const AttnArgs a) {
+  using CT = ct_t<TIn>;
+  using CT8 = vec8<CT>;
+  constexpr int BQ = 128, BK = 256, DC = 32, NC = D / DC;
+  // Row pitch 80 bytes = 5 x 16: the 16-byte row reads of 16 consecutive
+  // rows (the only reads of these tiles) fall on 16 distinct bank groups.
+  constexpr int LP = DC + 8;
+  __shared__ __attribute__((aligned(16))) CT Qs[2][BQ * LP];
+  __shared__ __attribute__((aligned(16))) CT Os[2][BQ * LP];
+  __shared__ __attribute__((aligned(16))) CT Ks[2][BK * LP];
+  __shared__ __attribute__((aligned(16))) CT Vs[2][BK * LP];
+  __shared__ float Ls[BQ], Dl[BQ];
+  __shared__ int Ps[BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, lq = lane & 31;
+  const int kg = wave & 3, qh = wave >> 2;   // keys kg*64.., query rows qh*64..
+  const int h = blockIdx.z % a.heads_q, z = blockIdx.z / a.heads_q;
+  const int kvh = h / a.group;
+  const Seq s = load_seq(a, z);
+  const int i0 = blockIdx.y * BQ;
+  const int kb0 = a.kt0 + 2 * (int)blockIdx.x;   // first of the two 128-key blocks
+  const int j0 = kb0 * 128;
+  if (i0 >= s.qlen || j0 >= s.klen) return;
+  const int kp0 = kpos0(a);
+  const int nkb = (s.klen + 127) / 128;
+  const int band_end = a.kt0 + a.ds_nb;
+  const Band<WIN> bd(a);
+  // (ut, kt) pairs of this workgroup that some kernel reads
+  bool want[2][2];
+  bool any = false;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int ut = i0 / 64 + x, kt = kb0 + y;
+      want[x][y] = kt < band_end && kt < nkb && ut * 64 < s.qlen &&
+                   tile_sees_block(a, s, ut, kt, nkb, kp0);
+      any = any || want[x][y];
+    }
+  if (!any) return;   // uniform over the workgroup
+
+  const TIn* Q = static_cast<const TIn*>(a.q) +
+                 (a.thd ? s.q_row0 * a.q_stride[1] : (int64_t)z * a.q_stride[0]) +
+                 (int64_t)h * a.q_stride[2];
+  const TIn* dO = static_cast<const TIn*>(a.dout) +
+                  (a.thd ? s.q_row0 * a.do_stride[1] : (int64_t)z * a.do_stride[0]) +
+                  (int64_t)h * a.do_stride[2];
+  const TIn* K = static_cast<const TIn*>(a.k) +
+                 (a.thd ? s.k_row0 * a.k_stride[1] : (int64_t)z * a.k_stride[0]) +
+                 (int64_t)kvh * a.k_stride[2];
+  const TIn* V = static_cast<const TIn*>(a.v) +
+                 (a.thd ? s.k_row0 * a.v_stride[1] : (int64_t)z * a.v_stride[0]) +
+                 (int64_t)kvh * a.v_stride[2];
+  if (tid < BQ) {
+    const int i = i0 + tid;
+    const bool ok = i < s.qlen;
+    const int64_t lb = (a.thd ? s.q_row0 : (int64_t)z * a.lse_stride[0]) +
+                       (int64_t)h * a.lse_stride[1];
+    const int64_t db = (a.thd ? s.q_row0 : (int64_t)z * a.delta_stride[0]) +
+                       (int64_t)h * a.delta_stride[1];
+    const float l = ok ? a.lse[lb + i] : -kInf;
+    Ls[tid] = (l == -kInf) ? kInf : l * kLog2e;   // P = 0 on keyless rows and padding
+    Dl[tid] = ok ? a.delta[db + i] : 0.f;
+    Ps[tid] = qpos(a, s, i);
+  }
+
+  // Staging of one 32-column chunk: 128 Q and dO rows, 256 K and V rows,
+  // 4 x 16 bytes per row; thread t owns row t/4 (+128) and chunk t%4.
+  const int sr = tid >> 2, sc = (tid & 3) * 8;
+  CT8 stq, sto, stk[2], stv[2];
+  auto load_chunk = [&](int c) {
+    const int col = c * DC + sc;
+    const int qi = i0 + sr;
+    const bool qok = qi < s.qlen;
+    const int qr = qok ? qi : 0;
+    stq = qok ? Elem<TIn>::load8(Q + (int64_t)qr * a.q_stride[1] + col) : zero8<CT>();
+    sto = qok ? Elem<TIn>::load8(dO + (int64_t)qr * a.do_stride[1] + col) : zero8<CT>();
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int kj = j0 + sr + 128 * r;
+      const bool kok = kj < s.klen;
+      const int kr = kok ? kj : 0;
+      stk[r] = kok ? Elem<TIn>::load8(K + (int64_t)kr * a.k_stride[1] + col) : zero8<CT>();
+      stv[r] = kok ? Elem<TIn>::load8(V + (int64_t)kr * a.v_stride[1] + col) : zero8<CT>();
+    }
+  };
+  auto store_chunk = [&](int b) {
+    *reinterpret_cast<CT8*>(&Qs[b][sr * LP + sc]) = stq;
+    *reinterpret_cast<CT8*>(&Os[b][sr * LP + sc]) = sto;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      *reinterpret_cast<CT8*>(&Ks[b][(sr + 128 * r) * LP + sc]) = stk[r];
+      *reinterpret_cast<CT8*>(&Vs[b][(sr + 128 * r) * LP + sc]) = stv[r];
+    }
+  };
+
+  f32x16 sacc[2][2], pacc[2][2];   // [key sub-block][query sub-tile]
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) { sacc[x][y][v] = 0.f; pacc[x][y][v] = 0.f; }
+
+  const int pr = perm32(lq);
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  for (int c = 0; c < NC; ++c) {
+    const int b = c & 1;
+    if (c + 1 < NC) load_chunk(c + 1);
+#pragma unroll
+    for (int ks = 0; ks < DC / 16; ++ks) {
+      CT8 ka[2], va[2], qb[2], ob[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        ka[x] = lds_row8(Ks[b], LP, kg * 64 + x * 32 + pr, ks * 16 + hh * 8);
+        va[x] = lds_row8(Vs[b], LP, kg * 64 + x * 32 + pr, ks * 16 + hh * 8);
+      }
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {
+        qb[y] = lds_row8(Qs[b], LP, qh * 64 + y * 32 + lq, ks * 16 + hh * 8);
+        ob[y] = lds_row8(Os[b], LP, qh * 64 + y * 32 + lq, ks * 16 + hh * 8);
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          sacc[x][y] = mfma32(ka[x], qb[y], sacc[x][y]);
+          pacc[x][y] = mfma32(va[x], ob[y], pacc[x][y]);
+        }
+    }
+    if (c + 1 < NC) store_chunk(b ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: lane = query row (qh*64 + y*32 + lq), element v = key
+  // kg*64 + x*32 + 16*(v/8) + 8*hh + v%8.
+  CT* const ds = static_cast<CT*>(a.ds);
+  CT* const ps = static_cast<CT*>(a.ps);
+  const int64_t ubase = ds_ubase(a, s, z);
+#pragma unroll
+  for (int y = 0; y < 2; ++y) {
+    const int qloc = qh * 64 + y * 32 + lq;
+    const float l2 = Ls[qloc], dd = Dl[qloc];
+    const int qp = Ps[qloc];
+    const int ut = (i0 + qh * 64) / 64;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int ko = kg * 64 + x * 32;           // key offset in the workgroup
+      const int blk = ko / 128;                  // which of the two key blocks
+      if (!want[qh][blk]) continue;              // uniform per wave
+      const int kloc0 = j0 + ko + 8 * hh;        // local key of v = 0
+      const bool need_mask = (j0 + ko + 32 > s.klen) || a.causal || bd.left;
+      CT8 pw[2], sw[2];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float p = fast_exp2(__builtin_fmaf(sacc[x][y][v], a.scale_log2, -l2));
+        if (need_mask) {
+          const int kj = kloc0 + 16 * (v >> 3) + (v & 7);
+          const bool vis = kj < s.klen && band_vis<WIN>(a, kp0 + kj, qp);
+          p = vis ? p : 0.f;
+        }
+        pw[v >> 3][v & 7] = (CT)p;
+        sw[v >> 3][v & 7] = (CT)(p * (pacc[x][y][v] - dd));
+      }
+      const int t0 = (ko % 128) / 16;
+      const int64_t tile = ((int64_t)h * a.ds_nu + ubase + ut) * a.ds_nb + (kb0 + blk - a.kt0);
+      const int64_t off = tile * kDsTileElems + ((int64_t)(y * 8 + t0) * 64 + lane) * 8;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        __builtin_nontemporal_store(pw[j], reinterpret_cast<CT8*>(ps + off + 512 * j));
+        __builtin_nontemporal_store(sw[j], reinterpret_cast<CT8*>(ds + off + 512 * j));
+      }
+    }
+  }
+}
+
+// dK^T and dV^T of 128 keys x 128 columns from the stored P and dS tiles.
+template <int D, typename TIn, typename TOut>
+__global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(const AttnArgs a) {
+  using CT = ct_t<TIn>;
+  using CT8 = vec8<CT>;
+  constexpr int BN = 128, DT = 128, BM = 64, NT = 512;
+  constexpr int TP = tr_pitch(DT), SP = tr_pitch(BN);   // transpose-read-only tiles
+  __shared__ __attribute__((aligned(16))) CT Qs[BM * TP];
+  __shared__ __attribute__((aligned(16))) CT Os[BM * TP];
+  __shared__ __attribute__((aligned(16))) CT Pt[BM * SP];
+  __shared__ __attribute__((aligned(16))) CT St[BM * SP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
+  const int kg = wave & 3, dh = wave >> 2;   // keys kg*32.., columns dh*64..
+  constexpr int NDT = D / DT;
+  const int kvh = blockIdx.x / NDT, c0 = (blockIdx.x % NDT) * DT;
+  const int kt = a.kt0 + blockIdx.y;
+  const int z = blockIdx.z;
+  const Seq s = load_seq(a, z);
+  const int j0 = kt * BN;
+  if (j0 >= s.klen) return;
+  const int kp0 = kpos0(a);
+  const int nkb = (s.klen + BN - 1) / BN;
+  const int nqt = (s.qlen + BM - 1) / BM;
+  const int my_key = j0 + kg * 32 + lq;
+  const bool key_valid = my_key < s.klen;
+  const int64_t ubase = ds_ubase(a, s, z);
+  const CT* const ds = static_cast<const CT*>(a.ds);
+  const CT* const ps = static_cast<const CT*>(a.ps);
+
+  f32x16 acck[2], accv[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { acck[j][v] = 0.f; accv[j][v] = 0.f; }
+
+  // Work items: (query head of the group, query tile that sees the block).
+  auto seek = [&](int& hg, int& ut) {
+    while (hg < a.group) {
+      while (ut < nqt && !tile_sees_block(a, s, ut, kt, nkb, kp0)) ++ut;
+      if (ut < nqt) return;
+      ++hg;
+      ut = 0;
+    }
+  };
+  TileStage<BM, DT, TIn, NT> qst, ost;
+  CT8 pst[2], sst[2];   // this thread's 16-byte pieces of the P and dS tiles
+  auto fetch = [&](int hg, int ut) {
+    const int h = kvh * a.group + hg;
+    const TIn* Q = static_cast<const TIn*>(a.q) +
+                   (a.thd ? s.q_row0 * a.q_stride[1] : (int64_t)z * a.q_stride[0]) +
+                   (int64_t)h * a.q_stride[2] + c0;
+    const TIn* dO = static_cast<const TIn*>(a.dout) +
+                    (a.thd ? s.q_row0 * a.do_stride[1] : (int64_t)z * a.do_stride[0]) +
+                    (int64_t)h * a.do_stride[2] + c0;
+    qst.load(Q, a.q_stride[1], ut * BM, s.qlen, tid);
+    ost.load(dO, a.do_stride[1], ut * BM, s.qlen, tid);
+    const int64_t tile = ((int64_t)h * a.ds_nu + ubase + ut) * a.ds_nb + (kt - a.kt0);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int64_t e = tile * kDsTileElems + (int64_t)(tid + NT * r) * 8;
+      pst[r] = __builtin_nontemporal_load(reinterpret_cast<const CT8*>(ps + e));
+      sst[r] = __builtin_nontemporal_load(reinterpret_cast<const CT8*>(ds + e));
+    }
+  };
+  // Piece n (= tid + 512 r) of a tile is lane n%64 of chunk n/64 = (qb2, t):
+  // rows 32*qb2 + lane%32, keys 16*t + 8*(lane/32) .. +7.
+  auto store_pieces = [&]() {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int n = tid + NT * r, ch = n >> 6, ln = n & 63;
+      const int row = 32 * (ch >> 3) + (ln & 31), col = 16 * (ch & 7) + 8 * (ln >> 5);
+      *reinterpret_cast<CT8*>(&Pt[row * SP + col]) = pst[r];
+      *reinterpret_cast<CT8*>(&St[row * SP + col]) = sst[r];
+    }
+  };
+
+  int hg = 0, ut = 0;
+  seek(hg, ut);
+  if (hg < a.group) fetch(hg, ut);
+  while (hg < a.group) {
+    __syncthreads();
+    qst.store(Qs, TP, tid);
+    ost.store(Os, TP, tid);
+    store_pieces();
+    int nhg = hg, nut = ut + 1;
+    seek(nhg, nut);
+    if (nhg < a.group) fetch(nhg, nut);
+    __syncthreads();
+    // dV^T += dO^T P, dK^T += Q^T dS over the tile's 64 rows
+#pragma unroll
+    for (int ks = 0; ks < BM / 16; ++ks) {
+      const int k0 = ks * 16 + 8 * (grp >> 1);
+      const CT8 pb = lds_tr8(Pt, SP, k0, kg * 32 + 16 * (grp & 1), gl);
+      const CT8 sb = lds_tr8(St, SP, k0, kg * 32 + 16 * (grp & 1), gl);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int m0 = dh * 64 + j * 32 + 16 * (grp & 1);
+        accv[j] = mfma32(lds_tr8(Os, TP, k0, m0, gl), pb, accv[j]);
+        acck[j] = mfma32(lds_tr8(Qs, TP, k0, m0, gl), sb, acck[j]);
+      }
+    }
+    hg = nhg;
+    ut = nut;
+  }
+  if (!key_valid) return;
+  auto key_row = [&](void* outp, const int64_t* st) -> TOut* {
+    return static_cast<TOut*>(outp) +
+           (a.thd ? (s.k_row0 + my_key) * st[1] : (int64_t)z * st[0] + (int64_t)my_key * st[1]) +
+           (int64_t)kvh * st[2] + c0 + dh * 64;
+  };
+  store_key_acc(acck, key_row(a.dk, a.dk_stride), hh, a.scale);
+  store_key_acc(accv, key_row(a.dv, a.dv_stride), hh, 1.f);
+}
+
 // ---------------------------------------------------------------- launch
 
 template <int DQK, int DV>
 struct BwdCfg {
   // Key-outer kernel: the 8-wave kv kernel for the small head dims; the
-  // 256/512 dims take the 4-wave kernel with 32-row query blocks (for 512 in
-  // two column chunks of dK, dV).  Both store dS for the dq kernel.
+  // 256/512 dims take the materialised path (sdp writes P and dS, dkv
+  // reduces dK and dV from them).  Both leave dS for the dq kernel.
   static constexpr bool KV_KERNEL = DQK + DV <= 320;
-  static constexpr bool BIG = DQK > 256 || DV > 256;
-  static constexpr int OCK = BIG ? DQK / 2 : DQK;
-  static constexpr int OCV = BIG ? DV / 2 : DV;
-  static constexpr int NCH = DQK / OCK;
-  static constexpr int BM = 32;
   static constexpr int DQ_COLS = DQK > 256 ? 256 : DQK;
 };
 
@@ -1047,13 +1050,17 @@ static hipError_t bwd_variant(const AttnArgs& a, int step, hipStream_t st) {
       else
         hipLaunchKernelGGL((bwd_kv_kernel<DQK, DV, TIn, TOut, false>), g, dim3(512), 0, st, a);
     } else {
-      dim3 g(a.heads_kv * C::NCH, a.ds_nb, a.nseq);
-      if (needs_band(a))
-        hipLaunchKernelGGL((bwd_main_kernel<DQK, DV, C::OCK, C::OCV, C::BM, TIn, TOut, true>), g,
-                           dim3(256), 0, st, a);
-      else
-        hipLaunchKernelGGL((bwd_main_kernel<DQK, DV, C::OCK, C::OCV, C::BM, TIn, TOut, false>), g,
-                           dim3(256), 0, st, a);
+      static_assert(DQK == DV, "materialised path: symmetric head dims");
+      if ((int64_t)a.heads_q * a.nseq > 65535) return hipErrorInvalidValue;   // grid z
+      if (qrows > 0) {
+        dim3 g1((a.ds_nb + 1) / 2, (qrows + 127) / 128, a.heads_q * a.nseq);
+        if (needs_band(a))
+          hipLaunchKernelGGL((bwd_sdp_kernel<DQK, TIn, true>), g1, dim3(512), 0, st, a);
+        else
+          hipLaunchKernelGGL((bwd_sdp_kernel<DQK, TIn, false>), g1, dim3(512), 0, st, a);
+      }
+      dim3 g2(a.heads_kv * (DQK / 128), a.ds_nb, a.nseq);
+      hipLaunchKernelGGL((bwd_dkv_kernel<DQK, TIn, TOut>), g2, dim3(512), 0, st, a);
     }
   }
   if (step == 2 && krows > 0 && qrows > 0) {

@@ -22,7 +22,8 @@ struct AttnArgs {
   void* dk;
   void* dv;
   float* dq_acc;      // bwd workspace: fp32 [rows][heads_q][d_qk]
-  void* ds;           // bwd workspace: bf16 dS tiles (small head dims)
+  void* ds;           // bwd workspace: dS tiles (operand type)
+  void* ps;           // bwd workspace: P tiles (head dims 256 and 512)
   void* tile_pos;     // bwd workspace: query positions per dS tile row
   int64_t ds_nu;      // dS tile rows per query head
   int ds_nb;          // key blocks per dS band

@@ -107,7 +107,8 @@ def test_argument_errors_are_rejected_before_launch():
     block = 4 * 4 * 64 * 128 * 2
     assert res["bwd_workspace_min_bytes"][1] == base + block
     assert res["bwd_workspace_bytes"][1] == base + 2 * block
-    # head dim 512: only the fp32 accumulator grows; the dS tiles are the same
+    # head dim 512: a larger fp32 accumulator, and the P tiles kept beside
+    # the dS tiles (twice the tile bytes per key block)
     full, least = res["bwd_workspace_d512"][1:]
     base512 = 256 + 4 * 256 * 4 + 256 * 4 * 512 * 4 + 256
-    assert least == base512 + block and full == base512 + 2 * block
+    assert least == base512 + 2 * block and full == base512 + 4 * block
