@@ -175,12 +175,13 @@ cpa_status attn_fwd(const cpa_problem* p, const void* q, const void* k,
 
 /* Bytes of workspace attn_bwd needs (host, pure) for its fastest schedule:
  * the error flag, D = rowsum(dO*O), an fp32 dQ accumulator, a small table
- * of query positions per 64-row tile and the bf16 dS tiles of the whole key
+ * of query positions per 64-row tile and the dS tiles of the whole key
  * range (16 KiB per query head, 64-row query tile and 128-key block: about
- * 2 * heads_q * S_q * S_k bytes).  Same problem -> same size. */
+ * 2 * heads_q * S_q * S_k bytes; twice that for head dims 256 and 512,
+ * which also keep the P tiles).  Same problem -> same size. */
 size_t attn_bwd_workspace_size(const cpa_problem* p);
 
-/* Smallest workspace attn_bwd accepts (host, pure): as above with the dS
+/* Smallest workspace attn_bwd accepts (host, pure): as above with the
  * tiles of one 128-key block.  Between this and attn_bwd_workspace_size,
  * attn_bwd processes the keys in bands of as many blocks as fit. */
 size_t attn_bwd_workspace_min(const cpa_problem* p);
@@ -217,7 +218,8 @@ cpa_status attn_bwd(const cpa_problem* p, const void* q, const void* k,
  *   attn_bwd_pre   writes the metadata flag, D = rowsum(dO*O) (fp32, from
  *                  the given O) and zeroes the fp32 dQ accumulator;
  *   attn_bwd_main  recomputes P from the LSE, writes dK, dV (to dk, dv) and
- *                  stores dS in the workspace;
+ *                  stores dS in the workspace (head dims 256 and 512 store P
+ *                  and dS tiles first and reduce dK, dV from them);
  *   attn_bwd_dq    adds dS K for the same key range to the accumulator;
  *   attn_bwd_post  writes dq = softmax_scale * accumulator.
  * attn_bwd_main followed by attn_bwd_dq may be repeated between one pre and
