@@ -698,7 +698,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
 // For head dims 256 and 512 one query tile's and one key block's operands do
 // not fit the LDS and registers of a CU together with the dK, dV
 // accumulators, so the backward runs as three tiled products:
-//   sdp  per (query head, 128 query rows, 256 keys): S^T = K Q^T and
+//   sdp  per (query head, 128 query rows, 128 keys): S^T = K Q^T and
 //        dP^T = V dO^T over the head dim in 32-wide chunks staged through
 //        LDS, then P = exp(S - LSE) and dS = P (dP - D), written as tiles in
 //        the dq kernel's chunk layout (K rows are read in perm32 order, so
@@ -719,11 +719,17 @@ __device__ __forceinline__ bool tile_sees_block(const AttnArgs& a, const Seq& s,
   return kt >= f && kt <= l;
 }
 
+// Keys per sdp workgroup: 128 keys x 128 query rows keeps the LDS (2 x 40
+// KiB) and registers (<= 128) small enough for two workgroups per CU.
+constexpr int kSdpKeys = 128;
+
 template <int D, typename TIn, bool WIN>
-__global__ __launch_bounds__(512, 1) void bwd_sdp_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void bwd_sdp_kernel(const AttnArgs a) {
   using CT = ct_t<TIn>;
   using CT8 = vec8<CT>;
-  constexpr int BQ = 128, BK = 256, DC = 32, NC = D / DC;
+  constexpr int BQ = 128, BK = kSdpKeys, DC = 32, NC = D / DC;
+  constexpr int NX = BK / 128;   // 32-key sub-blocks per wave (and 128-key blocks per workgroup)
   // Row pitch 80 bytes = 5 x 16: the 16-byte row reads of 16 consecutive
   // rows (the only reads of these tiles) fall on 16 distinct bank groups.
   constexpr int LP = DC + 8;
@@ -731,17 +737,15 @@ __global__ __launch_bounds__(512, 1) void bwd_sdp_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) CT Os[2][BQ * LP];
   __shared__ __attribute__((aligned(16))) CT Ks[2][BK * LP];
   __shared__ __attribute__((aligned(16))) CT Vs[2][BK * LP];
-  __shared__ float Ls[BQ], Dl[BQ];
-  __shared__ int Ps[BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, lq = lane & 31;
-  const int kg = wave & 3, qh = wave >> 2;   // keys kg*64.., query rows qh*64..
+  const int kg = wave & 3, qh = wave >> 2;   // keys kg*32*NX.., query rows qh*64..
   const int h = blockIdx.z % a.heads_q, z = blockIdx.z / a.heads_q;
   const int kvh = h / a.group;
   const Seq s = load_seq(a, z);
   const int i0 = blockIdx.y * BQ;
-  const int kb0 = a.kt0 + 2 * (int)blockIdx.x;   // first of the two 128-key blocks
+  const int kb0 = a.kt0 + NX * (int)blockIdx.x;   // first 128-key block
   const int j0 = kb0 * 128;
   if (i0 >= s.qlen || j0 >= s.klen) return;
   const int kp0 = kpos0(a);
@@ -749,12 +753,12 @@ __global__ __launch_bounds__(512, 1) void bwd_sdp_kernel(const AttnArgs a) {
   const int band_end = a.kt0 + a.ds_nb;
   const Band<WIN> bd(a);
   // (ut, kt) pairs of this workgroup that some kernel reads
-  bool want[2][2];
+  bool want[2][NX];
   bool any = false;
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) {
+    for (int y = 0; y < NX; ++y) {
       const int ut = i0 / 64 + x, kt = kb0 + y;
       want[x][y] = kt < band_end && kt < nkb && ut * 64 < s.qlen &&
                    tile_sees_block(a, s, ut, kt, nkb, kp0);
@@ -774,23 +778,11 @@ __global__ __launch_bounds__(512, 1) void bwd_sdp_kernel(const AttnArgs a) {
   const TIn* V = static_cast<const TIn*>(a.v) +
                  (a.thd ? s.k_row0 * a.v_stride[1] : (int64_t)z * a.v_stride[0]) +
                  (int64_t)kvh * a.v_stride[2];
-  if (tid < BQ) {
-    const int i = i0 + tid;
-    const bool ok = i < s.qlen;
-    const int64_t lb = (a.thd ? s.q_row0 : (int64_t)z * a.lse_stride[0]) +
-                       (int64_t)h * a.lse_stride[1];
-    const int64_t db = (a.thd ? s.q_row0 : (int64_t)z * a.delta_stride[0]) +
-                       (int64_t)h * a.delta_stride[1];
-    const float l = ok ? a.lse[lb + i] : -kInf;
-    Ls[tid] = (l == -kInf) ? kInf : l * kLog2e;   // P = 0 on keyless rows and padding
-    Dl[tid] = ok ? a.delta[db + i] : 0.f;
-    Ps[tid] = qpos(a, s, i);
-  }
 
   // Staging of one 32-column chunk: 128 Q and dO rows, 256 K and V rows,
   // 4 x 16 bytes per row; thread t owns row t/4 (+128) and chunk t%4.
   const int sr = tid >> 2, sc = (tid & 3) * 8;
-  CT8 stq, sto, stk[2], stv[2];
+  CT8 stq, sto, stk[NX], stv[NX];
   auto load_chunk = [&](int c) {
     const int col = c * DC + sc;
     const int qi = i0 + sr;
@@ -799,7 +791,7 @@ __global__ __launch_bounds__(512, 1) void bwd_sdp_kernel(const AttnArgs a) {
     stq = qok ? Elem<TIn>::load8(Q + (int64_t)qr * a.q_stride[1] + col) : zero8<CT>();
     sto = qok ? Elem<TIn>::load8(dO + (int64_t)qr * a.do_stride[1] + col) : zero8<CT>();
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < NX; ++r) {
       const int kj = j0 + sr + 128 * r;
       const bool kok = kj < s.klen;
       const int kr = kok ? kj : 0;
@@ -811,15 +803,15 @@ __global__ __launch_bounds__(512, 1) void bwd_sdp_kernel(const AttnArgs a) {
     *reinterpret_cast<CT8*>(&Qs[b][sr * LP + sc]) = stq;
     *reinterpret_cast<CT8*>(&Os[b][sr * LP + sc]) = sto;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < NX; ++r) {
       *reinterpret_cast<CT8*>(&Ks[b][(sr + 128 * r) * LP + sc]) = stk[r];
       *reinterpret_cast<CT8*>(&Vs[b][(sr + 128 * r) * LP + sc]) = stv[r];
     }
   };
 
-  f32x16 sacc[2][2], pacc[2][2];   // [key sub-block][query sub-tile]
+  f32x16 sacc[NX][2], pacc[NX][2];   // [key sub-block][query sub-tile]
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < NX; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y)
 #pragma unroll
@@ -834,11 +826,11 @@ __global__ __launch_bounds__(512, 1) void bwd_sdp_kernel(const AttnArgs a) {
     if (c + 1 < NC) load_chunk(c + 1);
 #pragma unroll
     for (int ks = 0; ks < DC / 16; ++ks) {
-      CT8 ka[2], va[2], qb[2], ob[2];
+      CT8 ka[NX], va[NX], qb[2], ob[2];
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        ka[x] = lds_row8(Ks[b], LP, kg * 64 + x * 32 + pr, ks * 16 + hh * 8);
-        va[x] = lds_row8(Vs[b], LP, kg * 64 + x * 32 + pr, ks * 16 + hh * 8);
+      for (int x = 0; x < NX; ++x) {
+        ka[x] = lds_row8(Ks[b], LP, kg * 32 * NX + x * 32 + pr, ks * 16 + hh * 8);
+        va[x] = lds_row8(Vs[b], LP, kg * 32 * NX + x * 32 + pr, ks * 16 + hh * 8);
       }
 #pragma unroll
       for (int y = 0; y < 2; ++y) {
@@ -846,7 +838,7 @@ __global__ __launch_bounds__(512, 1) void bwd_sdp_kernel(const AttnArgs a) {
         ob[y] = lds_row8(Os[b], LP, qh * 64 + y * 32 + lq, ks * 16 + hh * 8);
       }
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int x = 0; x < NX; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y) {
           sacc[x][y] = mfma32(ka[x], qb[y], sacc[x][y]);
@@ -864,13 +856,21 @@ __global__ __launch_bounds__(512, 1) void bwd_sdp_kernel(const AttnArgs a) {
   const int64_t ubase = ds_ubase(a, s, z);
 #pragma unroll
   for (int y = 0; y < 2; ++y) {
-    const int qloc = qh * 64 + y * 32 + lq;
-    const float l2 = Ls[qloc], dd = Dl[qloc];
-    const int qp = Ps[qloc];
+    // this lane's query row: LSE (log2 units), D and position
+    const int qi = i0 + qh * 64 + y * 32 + lq;
+    const bool qok = qi < s.qlen;
+    const int64_t lb = (a.thd ? s.q_row0 : (int64_t)z * a.lse_stride[0]) +
+                       (int64_t)h * a.lse_stride[1];
+    const int64_t db = (a.thd ? s.q_row0 : (int64_t)z * a.delta_stride[0]) +
+                       (int64_t)h * a.delta_stride[1];
+    const float lraw = qok ? a.lse[lb + qi] : -kInf;
+    const float l2 = (lraw == -kInf) ? kInf : lraw * kLog2e;   // P = 0 on keyless rows, padding
+    const float dd = qok ? a.delta[db + qi] : 0.f;
+    const int qp = qpos(a, s, qi);
     const int ut = (i0 + qh * 64) / 64;
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int ko = kg * 64 + x * 32;           // key offset in the workgroup
+    for (int x = 0; x < NX; ++x) {
+      const int ko = kg * 32 * NX + x * 32;      // key offset in the workgroup
       const int blk = ko / 128;                  // which of the two key blocks
       if (!want[qh][blk]) continue;              // uniform per wave
       const int kloc0 = j0 + ko + 8 * hh;        // local key of v = 0
@@ -901,7 +901,7 @@ __global__ __launch_bounds__(512, 1) void bwd_sdp_kernel(const AttnArgs a) {
 
 // dK^T and dV^T of 128 keys x 128 columns from the stored P and dS tiles.
 template <int D, typename TIn, typename TOut>
-__global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void bwd_dkv_kernel(const AttnArgs a) {
   using CT = ct_t<TIn>;
   using CT8 = vec8<CT>;
   constexpr int BN = 128, DT = 128, BM = 64, NT = 512;
@@ -1053,7 +1053,8 @@ static hipError_t bwd_variant(const AttnArgs& a, int step, hipStream_t st) {
       static_assert(DQK == DV, "materialised path: symmetric head dims");
       if ((int64_t)a.heads_q * a.nseq > 65535) return hipErrorInvalidValue;   // grid z
       if (qrows > 0) {
-        dim3 g1((a.ds_nb + 1) / 2, (qrows + 127) / 128, a.heads_q * a.nseq);
+        dim3 g1((a.ds_nb + kSdpKeys / 128 - 1) / (kSdpKeys / 128), (qrows + 127) / 128,
+                a.heads_q * a.nseq);
         if (needs_band(a))
           hipLaunchKernelGGL((bwd_sdp_kernel<DQK, TIn, true>), g1, dim3(512), 0, st, a);
         else
