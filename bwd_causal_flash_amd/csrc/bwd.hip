@@ -25,6 +25,11 @@
 
 namespace cpa {
 
+// Matrix-product steps by which the key kernel's LDS operand reads run
+// ahead of the products that use them (S and dP, dV, dK).  Deeper S/dP
+// read-ahead spills registers.
+constexpr int kSdpAhead = 2, kDvAhead = 2, kDkAhead = 4;
+
 // ---------------------------------------------------------------- pre/post
 
 // One group of DV/8 lanes per (row, head).
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   float* Dl = reinterpret_cast<float*>(smem + L::D_OFF);
   int* Ps = reinterpret_cast<int*>(smem + L::P_OFF);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
   const int kg = wave & 3, qh = wave >> 2;
   CT* Ts = reinterpret_cast<CT*>(smem + L::T_OFF);
@@ -409,7 +414,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
       // S and dP as two interleaved chains; the operands of step i + AHEAD
       // are read before the products of step i.
       {
-        constexpr int NS = KSQ > KSV ? KSQ : KSV, AHEAD = 2;
+        constexpr int NS = KSQ > KSV ? KSQ : KSV, AHEAD = kSdpAhead;
         CT8 qa[NS], kb[NS], oa[NS], vb[NS];
         auto rd = [&](int i) {
           if (i < KSQ) {
@@ -444,13 +449,25 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int v = 8 * vh + e;
-          float p = fast_exp2(__builtin_fmaf(sacc[v], a.scale_log2, -lr[e]));
-          if (need_mask) {
-            const bool vis = key_valid && band_vis<WIN>(a, my_kpos, Ps[rr + e]);
-            p = vis ? p : 0.f;
+          sacc[v] = fast_exp2(__builtin_fmaf(sacc[v], a.scale_log2, -lr[e]));
+        }
+        // need_mask is wave-uniform: one scalar branch around a branch-free
+        // pass (the query positions read as vectors, the conditions combined
+        // without short-circuit, so no per-element exec regions).
+        if (need_mask) {
+          const int4 p0 = *reinterpret_cast<const int4*>(&Ps[rr]);
+          const int4 p1 = *reinterpret_cast<const int4*>(&Ps[rr + 4]);
+          const int pq[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const bool vis = key_valid & band_vis<WIN>(a, my_kpos, pq[e]);
+            sacc[8 * vh + e] = vis ? sacc[8 * vh + e] : 0.f;
           }
-          sacc[v] = p;
-          pacc[v] = p * (pacc[v] - dr[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int v = 8 * vh + e;
+          pacc[v] = sacc[v] * (pacc[v] - dr[e]);
         }
       }
       CT8 wp[2];
@@ -467,7 +484,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
       }
       // dV^T += dO^T P over the wave's 32 query rows, operands 2 steps ahead.
       {
-        constexpr int N = 2 * NDV, AHEAD = 2;
+        constexpr int N = 2 * NDV, AHEAD = kDvAhead;
         CT8 oa[N];
         auto rd = [&](int i) {
           const int tt = i / NDV, db = i % NDV;
@@ -492,15 +509,22 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
     // dK^T column blocks [qh*NDKH, +NDKH) over both query halves; the dS
     // operand (lane = key column, 8 consecutive query rows) is a row read of
     // the half's dS^T block.
+    // Both halves run as one chain of 4*NDKH products whenever either is on,
+    // so the operand reads run kDkAhead steps ahead across the halves.  An
+    // off half adds nothing: its dS block was written as zeros, and Q rows
+    // past the end of the sequence are zero-filled.
+    if (on[0] || on[1]) {
+      CT8 wd[2][2];
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      if (!on[qq]) continue;
-      const CT* Tq = Ts + (kg + 4 * qq) * 32 * TP;
-      const CT8 wd[2] = {lds_row8(Tq, TP, lq, 8 * hh), lds_row8(Tq, TP, lq, 16 + 8 * hh)};
-      constexpr int N = 2 * NDKH, AHEAD = 2;
+      for (int qq = 0; qq < 2; ++qq) {
+        const CT* Tq = Ts + (kg + 4 * qq) * 32 * TP;
+        wd[qq][0] = lds_row8(Tq, TP, lq, 8 * hh);
+        wd[qq][1] = lds_row8(Tq, TP, lq, 16 + 8 * hh);
+      }
+      constexpr int N = 4 * NDKH, AHEAD = kDkAhead;
       CT8 qa[N];
       auto rd = [&](int i) {
-        const int tt = i / NDKH, j = i % NDKH;
+        const int qq = i / (2 * NDKH), tt = (i / NDKH) % 2, j = i % NDKH;
         qa[i] = lds_tr8p(Qs, QP, 32 * qq + 16 * tt + 8 * (grp >> 1),
                         (qh * NDKH + j) * 32 + 16 * (grp & 1), gl);
       };
@@ -509,7 +533,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < N; ++i) {
         if (i + AHEAD < N) rd(i + AHEAD);
-        acck[i % NDKH] = mfma32(qa[i], wd[i / NDKH], acck[i % NDKH]);
+        acck[i % NDKH] = mfma32(qa[i], wd[i / (2 * NDKH)][(i / NDKH) % 2], acck[i % NDKH]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -582,7 +606,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   static_assert(DQK % DC == 0, "whole column chunks");
   __shared__ __attribute__((aligned(16))) CT Ks[BN * KP];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
   const int h = blockIdx.x % a.heads_q;
   const int c0 = (blockIdx.x / a.heads_q) * DC;
@@ -616,14 +640,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   // (waves past the sequence's last tile read that tile and discard it)
   const int nqt = (s.qlen + 63) / 64;
   const int utc = ut < nqt ? ut : nqt - 1;
-  const CT* dsw = static_cast<const CT*>(a.ds) +
-                    ((int64_t)h * a.ds_nu + ds_ubase(a, s, z) + utc) * a.ds_nb * kDsTileElems +
-                    ((int64_t)qb2 * 8 * 64 + lane) * 8;
+  // The tile address is uniform (scalar registers) and the lane's offset in
+  // it fixed, so a step's loads need no per-lane 64-bit address arithmetic
+  // (whose temporaries would otherwise wait on loads still in flight).
+  const CT* dst = static_cast<const CT*>(a.ds) +
+                  ((int64_t)h * a.ds_nu + ds_ubase(a, s, z) + utc) * a.ds_nb * kDsTileElems;
+  const unsigned loff = (unsigned)(qb2 * 8 * 64 + lane) * 8u;
   auto load_frags = [&](int kt, CT8* f) {
-    const CT* p = dsw + (int64_t)(kt - a.kt0) * kDsTileElems;
+    const CT* p = dst + (int64_t)(kt - a.kt0) * kDsTileElems;
 #pragma unroll
     for (int t = 0; t < 8; ++t)   // streamed once: non-temporal, K keeps L2
-      f[t] = __builtin_nontemporal_load(reinterpret_cast<const CT8*>(p + 512 * t));
+      f[t] = __builtin_nontemporal_load(reinterpret_cast<const CT8*>(p + (loff + 512u * t)));
   };
 
   f32x16 acc[NDK];
@@ -637,16 +664,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   // the prefetched loads).  Wide column chunks keep one block ahead so the
   // accumulators fit without spilling.
   constexpr int AHEAD = NDK > 6 ? 1 : 2;
-  TileStage<BN, DC, TIn, NT, true> kst;
+  TileStage<BN, DC, TIn, NT, false> kst;   // dS is exactly zero past the last key
   CT8 fa[8], fb[8], fc[AHEAD == 2 ? 8 : 1];
-  kst.load(K + kbase, a.k_stride[1], kt_begin * BN, s.klen, tid);
+  // Issue order as at the end of a step (K tile, then one block of dS), so
+  // the loop head sees the same loads in flight from both of its entries.
   load_frags(kt_begin, fa);
-  if (AHEAD == 2 && kt_begin + 1 < kt_end) load_frags(kt_begin + 1, fb);
+  kst.load(K + kbase, a.k_stride[1], kt_begin * BN, s.klen, tid);
+  if (AHEAD == 2) load_frags(min(kt_begin + 1, kt_end - 1), fb);
   auto body = [&](int kt, const CT8 (&cur)[8], CT8 (&nn)[8]) {
     __syncthreads();
     kst.store(Ks, KP, tid);
-    if (kt + 1 < kt_end) kst.load(K + kbase, a.k_stride[1], (kt + 1) * BN, s.klen, tid);
-    if (kt + AHEAD < kt_end) load_frags(kt + AHEAD, nn);
+    // Both prefetches are unconditional (clamped to the last block, whose
+    // data is then unused), so every path issues the same loads and the
+    // wait for the K tile above does not also wait for the dS prefetch.
+    kst.load(K + kbase, a.k_stride[1], min(kt + 1, kt_end - 1) * BN, s.klen, tid);
+    load_frags(min(kt + AHEAD, kt_end - 1), nn);
     __syncthreads();
     if (kt >= my_first && kt <= my_last) {
 #pragma unroll
@@ -738,7 +770,7 @@ void bwd_sdp_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) CT Ks[2][BK * LP];
   __shared__ __attribute__((aligned(16))) CT Vs[2][BK * LP];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int hh = lane >> 5, lq = lane & 31;
   const int kg = wave & 3, qh = wave >> 2;   // keys kg*32*NX.., query rows qh*64..
   const int h = blockIdx.z % a.heads_q, z = blockIdx.z / a.heads_q;
@@ -911,7 +943,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   __shared__ __attribute__((aligned(16))) CT Pt[BM * SP];
   __shared__ __attribute__((aligned(16))) CT St[BM * SP];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
   const int kg = wave & 3, dh = wave >> 2;   // keys kg*32.., columns dh*64..
   constexpr int NDT = D / DT;

@@ -69,6 +69,14 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// Index of the calling wave in its workgroup, as a scalar: every value
+// derived from it (tile offsets, per-wave branches) then stays in scalar
+// registers and per-wave conditions become scalar branches rather than
+// exec-mask regions.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
 // Accumulator row of element v for a lane in half `hh` when the A operand's
 // rows were loaded through perm32(): the rows of one half become two runs of
 // 8 consecutive indices, 16*(v/8) + 8*hh + (v%8).
@@ -332,48 +340,39 @@ __device__ __forceinline__ int kpos0(const AttnArgs& a) { return a.thd ? 0 : a.k
 // neighbouring threads read one row's 128 contiguous bytes and every offset
 // is a compile-time immediate.  load() fetches rows [r0, r0+ROWS) of the
 // source (zeros past `limit`), store() writes them to a padded LDS tile.
-// CLAMP selects how a tail tile (rows past `limit`) is loaded: with CLAMP,
-// every thread still issues all its loads (rows past the end read the last
-// row and are zeroed afterwards), so the number of loads in flight does not
-// depend on the lane and later waits can stay exact; without it, those rows
-// are skipped.  CLAMP requires limit >= 1.
-template <int ROWS, int D, typename TIn, int NT = 256, bool CLAMP = false>
+// Every thread issues all its loads on one branch-free path: rows past the
+// end read the last row, and are replaced by zeros only when the tile is
+// stored.  So the number of loads in flight never depends on the tile, no
+// wait follows a load directly, and the compiler's wait counts after a
+// prefetch stay exact (a branch between a full-tile and a tail-tile path
+// makes it merge the two and wait for every load at the join).  Requires
+// limit >= 1.  ZERO = false keeps the repeated last row in the tile: for
+// callers whose products already give those rows zero weight (keys masked
+// out of the scores, dS exactly zero past the last key), which then need
+// no select on the loaded registers at all.
+template <int ROWS, int D, typename TIn, int NT = 256, bool ZERO = true>
 struct TileStage {
   static constexpr int RP = NT / 8;   // rows covered per pass
   static constexpr int RI = ROWS / RP, CJ = D / 64;
   static_assert(ROWS % RP == 0 && D % 64 == 0, "tile shape");
   using CT = ct_t<TIn>;
   vec8<CT> v[RI][CJ];
+  int lim = 0;   // rows of the tile inside the source (limit - r0)
   __device__ __forceinline__ void load(const TIn* base, int64_t row_stride, int r0, int limit,
                                        int tid) {
     const int rg = tid >> 3, cp = (tid & 7) * 8;
-    if (r0 + ROWS <= limit) {   // whole tile in range: no per-row predicate
-#pragma unroll
-      for (int i = 0; i < RI; ++i) {
-        const TIn* p = base + (int64_t)(r0 + rg + RP * i) * row_stride + cp;
-#pragma unroll
-        for (int j = 0; j < CJ; ++j) v[i][j] = Elem<TIn>::load8(p + 64 * j);
-      }
-      return;
-    }
+    lim = limit - r0;
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
       const int r = r0 + rg + RP * i;
-      if constexpr (CLAMP) {
-        const int rc = r < limit ? r : limit - 1;
-        const TIn* p = base + (int64_t)rc * row_stride + cp;
+      const TIn* p = base + (int64_t)(r < limit ? r : limit - 1) * row_stride + cp;
 #pragma unroll
-        for (int j = 0; j < CJ; ++j) {
-          const vec8<CT> x = Elem<TIn>::load8(p + 64 * j);
-          v[i][j] = r < limit ? x : zero8<CT>();
-        }
-      } else {
-        const TIn* p = base + (int64_t)r * row_stride + cp;
-#pragma unroll
-        for (int j = 0; j < CJ; ++j)
-          v[i][j] = r < limit ? Elem<TIn>::load8(p + 64 * j) : zero8<CT>();
-      }
+      for (int j = 0; j < CJ; ++j) v[i][j] = Elem<TIn>::load8(p + 64 * j);
     }
+  }
+  __device__ __forceinline__ vec8<CT> row_val(int i, int j, int rg) const {
+    if constexpr (!ZERO) return v[i][j];
+    return rg + RP * i < lim ? v[i][j] : zero8<CT>();
   }
   // Direct copy with few registers live (at most two chunks in flight).
   static __device__ __forceinline__ void copy(const TIn* base, int64_t row_stride, int r0,
@@ -396,7 +395,7 @@ struct TileStage {
     for (int i = 0; i < RI; ++i)
 #pragma unroll
       for (int j = 0; j < CJ; ++j)
-        *reinterpret_cast<vec8<CT>*>(tile + (rg + RP * i) * pitch + cp + 64 * j) = v[i][j];
+        *reinterpret_cast<vec8<CT>*>(tile + (rg + RP * i) * pitch + cp + 64 * j) = row_val(i, j, rg);
   }
   // The same into a row-permuted tile (row r goes to rperm16(r)).
   __device__ __forceinline__ void store_rperm(CT* tile, int pitch, int tid) const {
@@ -405,7 +404,8 @@ struct TileStage {
     for (int i = 0; i < RI; ++i)
 #pragma unroll
       for (int j = 0; j < CJ; ++j)
-        *reinterpret_cast<vec8<CT>*>(tile + rperm16(rg + RP * i) * pitch + cp + 64 * j) = v[i][j];
+        *reinterpret_cast<vec8<CT>*>(tile + rperm16(rg + RP * i) * pitch + cp + 64 * j) =
+            row_val(i, j, rg);
   }
 };
 

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
   __shared__ __attribute__((aligned(16))) CT Ks[BN * KP];
   __shared__ __attribute__((aligned(16))) CT Vs[BN * VP];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
   const int h = blockIdx.x % a.heads_q;
   const int ch = blockIdx.x / a.heads_q;
@@ -107,9 +107,11 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
   const int kr = perm32(lq);
 
   // K/V tiles go global -> registers -> LDS; tile t+1 is fetched while
-  // tile t is being computed.
-  TileStage<BN, DQK, TIn, 256, true> kst;   // limit = klen >= 1 when ntiles > 0
-  TileStage<BN, DVC, TIn, 256, true> vst;
+  // tile t is being computed.  Rows past the last key repeat the last key
+  // (limit = klen >= 1 when ntiles > 0): their scores are masked to -inf, so
+  // they add nothing to O.
+  TileStage<BN, DQK, TIn, 256, false> kst;
+  TileStage<BN, DVC, TIn, 256, false> vst;
   if (t0 < ntiles) {
     kst.load(Kb, a.k_stride[1], t0 * BN, s.klen, tid);
     vst.load(Vb, a.v_stride[1], t0 * BN, s.klen, tid);
@@ -120,10 +122,10 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
     __syncthreads();
     kst.store(Ks, KP, tid);
     vst.store(Vs, VP, tid);
-    if (t + 1 < ntiles) {
-      kst.load(Kb, a.k_stride[1], j0 + BN, s.klen, tid);
-      vst.load(Vb, a.v_stride[1], j0 + BN, s.klen, tid);
-    }
+    // (the last tile loads itself again: the same loads on every path)
+    const int jn = (t + 1 < ntiles ? t + 1 : t) * BN;
+    kst.load(Kb, a.k_stride[1], jn, s.klen, tid);
+    vst.load(Vb, a.v_stride[1], jn, s.klen, tid);
     __syncthreads();
     if (!wave_active || (a.causal && kp0 + j0 > whi + bd.wr) ||
         (bd.left && kp0 + j0 + BN - 1 < wlo - bd.wl))
