@@ -856,6 +856,9 @@ void bwd_sdp_kernel(const AttnArgs a) {
   for (int c = 0; c < NC; ++c) {
     const int b = c & 1;
     if (c + 1 < NC) load_chunk(c + 1);
+    // Raised issue priority over the burst of products (two workgroups
+    // share each CU; the other one's softmax and staging fill the gaps).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < DC / 16; ++ks) {
       CT8 ka[NX], va[NX], qb[2], ob[2];
@@ -877,6 +880,7 @@ void bwd_sdp_kernel(const AttnArgs a) {
           pacc[x][y] = mfma32(va[x], ob[y], pacc[x][y]);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (c + 1 < NC) store_chunk(b ^ 1);
     __syncthreads();
   }
@@ -1022,6 +1026,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     if (nhg < a.group) fetch(nhg, nut);
     __syncthreads();
     // dV^T += dO^T P, dK^T += Q^T dS over the tile's 64 rows
+    __builtin_amdgcn_s_setprio(1);   // as in the score kernel
 #pragma unroll
     for (int ks = 0; ks < BM / 16; ++ks) {
       const int k0 = ks * 16 + 8 * (grp >> 1);
@@ -1034,6 +1039,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         acck[j] = mfma32(lds_tr8(Qs, TP, k0, m0, gl), sb, acck[j]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     hg = nhg;
     ut = nut;
   }

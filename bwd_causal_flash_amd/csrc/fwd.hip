@@ -136,11 +136,16 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
+    // Raised issue priority over each burst of products: the other
+    // workgroup's wave on the SIMD, when in its softmax, then fills the
+    // cycles the products leave free instead of delaying them.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = mfma32(lds_row8(Ks, KP, kb * 32 + kr, ks * 16 + hh * 8), qreg[ks], sacc[kb]);
+    __builtin_amdgcn_s_setprio(0);
 
     const bool need_mask = (j0 + BN > s.klen) || (a.causal && kp0 + j0 + BN - 1 > wlo + bd.wr) ||
                            (bd.left && kp0 + j0 < whi - bd.wl);
@@ -187,6 +192,7 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
     rs = sum_halves(rs);
     l_run += rs;
 
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int st = 0; st < BN / 16; ++st) {
       CT8 pb;
@@ -197,6 +203,7 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
         oacc[db] = mfma32(lds_tr8(Vs, VP, 16 * st + 8 * (grp >> 1), db * 32 + 16 * (grp & 1), gl),
                           pb, oacc[db]);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   if (!qvalid) return;
