@@ -7,8 +7,10 @@ of a 32768-token causal sequence under CP4 with the dual-chunk balance, so
 the rank holds query chunks 0 and 7 (4096 rows each, global positions kept)
 and all 32768 keys; 32 heads, QK/V head dims 192/128, bf16 inputs drawn from
 N(0, 1).  One step = the whole path on one batch:
-  * 9 forward partials (query chunk x visible 4096-key block) in fp32,
-  * 7 LSE merges (the last one writes the bf16 O),
+  * 9 forward partials (query chunk x visible 4096-key block); each one
+    after a chunk's first block is merged by LSE into the chunk's fp32
+    accumulator in the forward kernel's epilogue (7 merges; the last
+    writes the bf16 O),
   * pack + unpack of O and the fp32 LSE into 4 head-group segments,
   * the backward (D, main kernel, dQ cast) over both chunks and all keys.
 Inputs are resident in HBM before the timed region starts.
@@ -165,7 +167,7 @@ def main():
 
     if args.breakdown:
         phases = {}
-        for name, fn in (("forward(9 partials + 7 merges)", lambda: rs.forward(stream)),
+        for name, fn in (("forward(9 partials, 7 merged in the epilogue)", lambda: rs.forward(stream)),
                          ("pack+unpack", lambda: rs.pack_roundtrip(stream)),
                          ("backward(pre+main+dq+post)", lambda: rs.backward(stream))):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -139,14 +139,16 @@ def workspace_error_flag(ws: torch.Tensor) -> int:
 
 def attn_fwd(q, k, v, o, lse, *, causal=True, scale=None, q_segments=None, k_pos_begin=0,
              varlen: Optional[Varlen] = None, workspace=None, stream=None,
-             window=None) -> torch.Tensor:
+             window=None, acc=None) -> torch.Tensor:
     """Forward into preallocated o (bf16 or fp32) and lse (fp32).
 
     q_segments: BSHD query positions as [(row_begin, pos_begin), ...]
     (default: one segment at 0, top-left causal); k_pos_begin: position of
     key row 0; window: (left, right) sliding window / band, -1 = unbounded
-    on that side (None: no window).  Returns the workspace (its first int32
-    is the THD metadata error flag).
+    on that side (None: no window).  acc = (o_acc, lse_acc): fp32 running
+    accumulator laid out like (o, lse); the result is merged into it by LSE
+    (attn_fwd_accum; o, lse may be o_acc, lse_acc themselves).  Returns the
+    workspace (its first int32 is the THD metadata error flag).
     """
     lib = _lib.load()
     p = _fill_problem(q, k, v, causal=causal, scale=scale, out_dtype=_dtype_code(o),
@@ -158,9 +160,21 @@ def attn_fwd(q, k, v, o, lse, *, causal=True, scale=None, q_segments=None, k_pos
     need = lib.attn_fwd_workspace_size(ctypes.byref(p))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    st = lib.attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                      _ptr(workspace), workspace.numel(), _stream_handle(stream))
-    _lib.check(st, "attn_fwd")
+    if acc is None:
+        st = lib.attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                          _ptr(workspace), workspace.numel(), _stream_handle(stream))
+        _lib.check(st, "attn_fwd")
+    else:
+        o_acc, lse_acc = acc
+        if o_acc.dtype != torch.float32 or lse_acc.dtype != torch.float32:
+            raise ValueError("the accumulator is fp32")
+        if (o_acc.shape != o.shape or o_acc.stride() != o.stride() or
+                lse_acc.shape != lse.shape or lse_acc.stride() != lse.stride()):
+            raise ValueError("the accumulator must have the layout of o and lse")
+        st = lib.attn_fwd_accum(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_acc),
+                                _ptr(lse_acc), _ptr(o), _ptr(lse), _ptr(workspace),
+                                workspace.numel(), _stream_handle(stream))
+        _lib.check(st, "attn_fwd_accum")
     return workspace
 
 

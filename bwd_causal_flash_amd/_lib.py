@@ -111,6 +111,8 @@ EXPORTS = {
     "attn_bwd_workspace_min": (ctypes.c_size_t, [ctypes.POINTER(Problem)]),
     "attn_fwd": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 6 +
                  [ctypes.c_size_t, ctypes.c_void_p]),
+    "attn_fwd_accum": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 8 +
+                       [ctypes.c_size_t, ctypes.c_void_p]),
     "attn_bwd": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 +
                  [ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]),
     "attn_bwd_pre": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 +

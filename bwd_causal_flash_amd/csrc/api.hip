@@ -247,6 +247,60 @@ void set_bwd_ws(AttnArgs& a, const cpa_problem* p, void* ws, size_t ws_bytes) {
   a.ps = keeps_p(p) ? static_cast<char*>(a.ds) + ds_part_bytes(p) * (size_t)a.ds_nb : nullptr;
 }
 
+// attn_fwd, and attn_fwd_accum when o_acc / lse_acc are given.
+cpa_status fwd_common(const cpa_problem* p, const void* q, const void* k, const void* v,
+                      const float* o_acc, const float* lse_acc, void* o, float* lse, void* ws,
+                      size_t ws_bytes, cpa_stream_t stream) {
+  cpa_status st = check_problem(p);
+  if (st != CPA_OK) return st;
+  if (!q || !k || !v || !o || !lse) return CPA_ERR_NULL;
+  if (!strides_ok(p->o_stride, 3)) return CPA_ERR_STRIDE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3))
+    return CPA_ERR_ALIGN;
+  if (!ws || ws_bytes < attn_fwd_workspace_size(p) || !aligned16(ws)) return CPA_ERR_WORKSPACE;
+  const int ib = dtype_bytes(p->in_dtype), ob = dtype_bytes(p->out_dtype);
+  const Span so = qspan(p, o, p->o_stride, p->d_v, ob), sl = lsespan(p, lse);
+  const Span sq = qspan(p, q, p->q_stride, p->d_qk, ib);
+  const Span sk = kspan(p, k, p->k_stride, p->d_qk, ib), sv = kspan(p, v, p->v_stride, p->d_v, ib);
+  const Span sw = {reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + ws_bytes};
+  for (Span out : {so, sl, sw})
+    for (Span in : {sq, sk, sv})
+      if (overlap(out, in)) return CPA_ERR_OVERLAP;
+  if (overlap(so, sl) || overlap(so, sw) || overlap(sl, sw)) return CPA_ERR_OVERLAP;
+  if (o_acc) {
+    // The accumulator is fp32 with O's element strides and LSE's strides.
+    // O may be the accumulator itself (fp32 output, in place) and LSE its
+    // LSE (in place while one workgroup writes a whole row, d_v <= 256);
+    // any other overlap with an output is an error, as is one with the
+    // workspace.
+    if (!aligned16(o_acc) || (reinterpret_cast<uintptr_t>(lse_acc) & 3)) return CPA_ERR_ALIGN;
+    const Span sa = qspan(p, o_acc, p->o_stride, p->d_v, 4), sal = lsespan(p, lse_acc);
+    const bool o_inplace = static_cast<const void*>(o_acc) == o && p->out_dtype == CPA_FP32;
+    const bool l_inplace = lse_acc == lse && p->d_v <= 256;
+    if ((!o_inplace && overlap(sa, so)) || overlap(sa, sl) || overlap(sa, sw)) return CPA_ERR_OVERLAP;
+    if ((!l_inplace && overlap(sal, sl)) || overlap(sal, so) || overlap(sal, sw))
+      return CPA_ERR_OVERLAP;
+  }
+
+  AttnArgs a = make_args(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out_o = o;
+  a.out_lse = lse;
+  a.acc_o = o_acc;
+  a.acc_lse = lse_acc;
+  a.err_flag = static_cast<int*>(ws);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // BSHD has no metadata to check: the forward kernel itself clears the
+  // flag when it runs (rows and sequences present).
+  if ((a.thd || a.seqlen_q == 0 || a.nseq == 0) && launch_meta_check(a, s) != hipSuccess)
+    return CPA_ERR_LAUNCH;
+  if (launch_fwd(a, p->d_qk, p->d_v, p->in_dtype, p->out_dtype, s) != hipSuccess)
+    return CPA_ERR_LAUNCH;
+  return CPA_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -285,36 +339,14 @@ size_t attn_bwd_workspace_min(const cpa_problem* p) {
 
 cpa_status attn_fwd(const cpa_problem* p, const void* q, const void* k, const void* v, void* o,
                     float* lse, void* ws, size_t ws_bytes, cpa_stream_t stream) {
-  cpa_status st = check_problem(p);
-  if (st != CPA_OK) return st;
-  if (!q || !k || !v || !o || !lse) return CPA_ERR_NULL;
-  if (!strides_ok(p->o_stride, 3)) return CPA_ERR_STRIDE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-      (reinterpret_cast<uintptr_t>(lse) & 3))
-    return CPA_ERR_ALIGN;
-  if (!ws || ws_bytes < attn_fwd_workspace_size(p) || !aligned16(ws)) return CPA_ERR_WORKSPACE;
-  const int ib = dtype_bytes(p->in_dtype), ob = dtype_bytes(p->out_dtype);
-  const Span so = qspan(p, o, p->o_stride, p->d_v, ob), sl = lsespan(p, lse);
-  const Span sq = qspan(p, q, p->q_stride, p->d_qk, ib);
-  const Span sk = kspan(p, k, p->k_stride, p->d_qk, ib), sv = kspan(p, v, p->v_stride, p->d_v, ib);
-  const Span sw = {reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + ws_bytes};
-  for (Span out : {so, sl, sw})
-    for (Span in : {sq, sk, sv})
-      if (overlap(out, in)) return CPA_ERR_OVERLAP;
-  if (overlap(so, sl) || overlap(so, sw) || overlap(sl, sw)) return CPA_ERR_OVERLAP;
+  return fwd_common(p, q, k, v, nullptr, nullptr, o, lse, ws, ws_bytes, stream);
+}
 
-  AttnArgs a = make_args(p);
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.out_o = o;
-  a.out_lse = lse;
-  a.err_flag = static_cast<int*>(ws);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (launch_meta_check(a, s) != hipSuccess) return CPA_ERR_LAUNCH;
-  if (launch_fwd(a, p->d_qk, p->d_v, p->in_dtype, p->out_dtype, s) != hipSuccess)
-    return CPA_ERR_LAUNCH;
-  return CPA_OK;
+cpa_status attn_fwd_accum(const cpa_problem* p, const void* q, const void* k, const void* v,
+                          const float* o_acc, const float* lse_acc, void* o, float* lse, void* ws,
+                          size_t ws_bytes, cpa_stream_t stream) {
+  if (!o_acc || !lse_acc) return CPA_ERR_NULL;
+  return fwd_common(p, q, k, v, o_acc, lse_acc, o, lse, ws, ws_bytes, stream);
 }
 
 }  // extern "C"
@@ -386,7 +418,10 @@ cpa_status bwd_run(const cpa_problem* p, const void* q, const void* k, const voi
   auto run = [&](int step) {
     return launch_bwd(a, p->d_qk, p->d_v, p->in_dtype, p->out_dtype, step, s) == hipSuccess;
   };
-  if ((steps & 1) && launch_meta_check(a, s) != hipSuccess) return CPA_ERR_LAUNCH;
+  // (BSHD: the pre kernel clears the flag when it runs)
+  if ((steps & 1) && (a.thd || a.seqlen_q == 0 || a.nseq == 0) &&
+      launch_meta_check(a, s) != hipSuccess)
+    return CPA_ERR_LAUNCH;
   if ((steps & 1) && !run(0)) return CPA_ERR_LAUNCH;
   if (a.ds_nb > 0) {
     const int nb = a.ds_nb;

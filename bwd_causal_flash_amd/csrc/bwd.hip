@@ -37,6 +37,7 @@ template <int DV, int DQK, typename TIn>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a) {
   constexpr int G = DV / 8;            // lanes per (row, head)
   constexpr int PER_BLOCK = 256 / G;
+  if (!a.thd && (blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *a.err_flag = 0;
   const int z = blockIdx.z;
   const Seq s = load_seq(a, z);
   const int gid = threadIdx.x / G, gl = threadIdx.x % G;

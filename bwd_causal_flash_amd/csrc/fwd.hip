@@ -44,6 +44,7 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
+  if (!a.thd && (blockIdx.x | blockIdx.y | blockIdx.z | tid) == 0) *a.err_flag = 0;
   const int h = blockIdx.x % a.heads_q;
   const int ch = blockIdx.x / a.heads_q;
   const int tile = gridDim.y - 1 - blockIdx.y;   // heaviest tiles first
@@ -208,28 +209,59 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
 
   if (!qvalid) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  TOut* orow = O + obase + (int64_t)qi * a.o_stride[1] + (int64_t)h * a.o_stride[2] + ch * DVC;
+  const int64_t ooff = obase + (int64_t)qi * a.o_stride[1] + (int64_t)h * a.o_stride[2] + ch * DVC;
+  TOut* orow = O + ooff;
+  const int64_t lrow = a.thd ? s.q_row0 + qi : (int64_t)qi;
+  const int64_t loff = (a.thd ? 0 : (int64_t)z * a.lse_stride[0]) + (int64_t)h * a.lse_stride[1] + lrow;
+  // This block's normalised O and natural-log LSE (the ring-step partial).
+  float lse = l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -kInf;
+  float wa = 0.f, wp = inv;   // O = wa * O_acc + wp * oacc
+  const float* arow = nullptr;
+  if (a.acc_o) {
+    // Merged into the running accumulator as the LSE merge does it: with
+    // M = max of the two LSEs, weights exp(LSE_x - M) / their sum, and the
+    // new LSE = M + ln(sum); both -inf gives O = 0, LSE = -inf.
+    const float la = a.acc_lse[loff], lp = lse;
+    const float mx = fmaxf(la, lp);
+    float ea = 0.f, ep = 0.f;
+    lse = -kInf;
+    if (mx != -kInf) {
+      ea = la == -kInf ? 0.f : expf(la - mx);
+      ep = lp == -kInf ? 0.f : expf(lp - mx);
+      const float sum = ea + ep;
+      lse = mx + logf(sum);
+      ea /= sum;
+      ep /= sum;
+    }
+    wa = ea;
+    wp = ep * inv;
+    arow = a.acc_o + ooff;
+  }
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
       const int d = db * 32 + 8 * a4 + 4 * hh;
+      float r[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = oacc[db][4 * a4 + e] * wp;
+      if (wa != 0.f) {
+        const float4 x = *reinterpret_cast<const float4*>(arow + d);
+        r[0] += wa * x.x;
+        r[1] += wa * x.y;
+        r[2] += wa * x.z;
+        r[3] += wa * x.w;
+      }
       if constexpr (sizeof(TOut) == 2) {
         vec4<TOut> w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (TOut)(oacc[db][4 * a4 + e] * inv);
+        for (int e = 0; e < 4; ++e) w[e] = (TOut)r[e];
         *reinterpret_cast<vec4<TOut>*>(orow + d) = w;
       } else {
-        float4 w = make_float4(oacc[db][4 * a4 + 0] * inv, oacc[db][4 * a4 + 1] * inv,
-                               oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv);
-        *reinterpret_cast<float4*>(orow + d) = w;
+        *reinterpret_cast<float4*>(orow + d) = make_float4(r[0], r[1], r[2], r[3]);
       }
     }
-  if (hh == 0 && ch == 0) {
-    const int64_t lrow = a.thd ? s.q_row0 + qi : (int64_t)qi;
-    const int64_t loff = (a.thd ? 0 : (int64_t)z * a.lse_stride[0]) + (int64_t)h * a.lse_stride[1] + lrow;
-    a.out_lse[loff] = l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -kInf;
-  }
+  if (hh == 0 && ch == 0) a.out_lse[loff] = lse;
 }
 
 // THD metadata check: writes 0 to the flag, or 1 if any sequence's offsets

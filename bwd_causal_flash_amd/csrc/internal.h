@@ -18,6 +18,8 @@ struct AttnArgs {
   const float* lse;   // bwd: saved LSE
   void* out_o;        // fwd: O
   float* out_lse;     // fwd: LSE
+  const float* acc_o;     // fwd with merge: fp32 accumulator, O's element strides
+  const float* acc_lse;   // fwd with merge: accumulator LSE, LSE's strides
   void* dq;
   void* dk;
   void* dv;

@@ -5,9 +5,12 @@ balanced partition of TransformerEngine PR 3510, "Add head-parallel FA4
 backward for cuDNN CP attention", Changes) and the keys/values of the whole
 sequence, cut into KV blocks the way a P2P ring would deliver them.  The
 forward computes one partial attention per (query chunk, visible KV block)
-in fp32 and folds it into the chunk's accumulator with the LSE merge (the
+and folds it into the chunk's fp32 accumulator with the LSE merge (the
 per-step kernel call plus LSE correction of PR 3527's CP ring commits); the
-last merge of a chunk writes the final O in the output dtype.  The backward
+last merge of a chunk writes the final O in the output dtype.  By default
+the merge runs in the forward kernel's epilogue (attn_fwd_accum); with
+fused_merge=False each partial goes to an fp32 buffer and attn_merge_lse
+folds it in.  The backward
 is one call over all the rank's query rows against all keys, with the
 merged O and LSE.  The saved O and fp32 LSE are then packed into per-head-
 group segments for the head-parallel exchange and unpacked again (PR 3510,
@@ -51,9 +54,11 @@ class RankStep:
     """
 
     def __init__(self, q, k, v, dout, chunks: Sequence[Tuple[int, int, int]], kv_blocks: int,
-                 *, scale=None, pack_groups: int = 4, out_dtype=None):
+                 *, scale=None, pack_groups: int = 4, out_dtype=None,
+                 fused_merge: bool = True):
         self.q, self.k, self.v, self.dout = q, k, v, dout
         self.scale = scale
+        self.fused_merge = fused_merge
         self.chunks = [Chunk(*c) for c in chunks]
         b, sq, hq, _ = q.shape
         sk = k.shape[1]
@@ -94,9 +99,13 @@ class RankStep:
         for ci, c in enumerate(self.chunks):
             blocks = self.visible_blocks(c)
             for n, j in enumerate(blocks):
+                last = n == len(blocks) - 1
+                if self.fused_merge:
+                    plan.append(Call("fwd", ci, j, final=last))
+                    continue
                 plan.append(Call("fwd", ci, j, final=(len(blocks) == 1)))
                 if n > 0:
-                    plan.append(Call("merge", ci, j, final=(n == len(blocks) - 1)))
+                    plan.append(Call("merge", ci, j, final=last))
         return plan
 
     def n_fwd_calls(self) -> int:
@@ -113,9 +122,15 @@ class RankStep:
             c = self.chunks[call.chunk]
             rs = slice(c.row0, c.row0 + c.rows)
             ks = slice(call.block * blk, (call.block + 1) * blk)
-            if call.kind == "fwd":
+            if call.kind == "fwd" and self.fused_merge and call.block != self.visible_blocks(c)[0]:
+                acc = (self.o_acc[:, rs], self.lse_acc[:, :, rs])
+                out = (self.o[:, rs], self.lse[:, :, rs]) if call.final else acc
+                attn_fwd(self.q[:, rs], self.k[:, ks], self.v[:, ks], *out, causal=True,
+                         scale=self.scale, q_segments=[(0, c.pos0)], k_pos_begin=ks.start,
+                         workspace=self.fwd_ws, stream=stream, acc=acc)
+            elif call.kind == "fwd":
                 first = call.block == self.visible_blocks(c)[0]
-                if call.final:
+                if call.final and first:
                     o, lse = self.o[:, rs], self.lse[:, :, rs]
                 elif first:
                     o, lse = self.o_acc[:, rs], self.lse_acc[:, :, rs]

@@ -173,6 +173,27 @@ cpa_status attn_fwd(const cpa_problem* p, const void* q, const void* k,
                     const void* v, void* o, float* lse, void* ws,
                     size_t ws_bytes, cpa_stream_t stream);
 
+/*
+ * Forward of one key block merged into a running accumulator: writes to
+ * (o, lse) what attn_merge_lse would make of (o_acc, lse_acc) and this
+ * block's attn_fwd result (the per-ring-step combine of PR 3527's
+ * context-parallel commits: LSE correction of each step's partial), with
+ * no fp32 partial in memory and no separate merge launch.  Per row:
+ *   M = max(lse_acc, lse_blk);  M = -inf -> O = 0, LSE = -inf;  else
+ *   LSE = M + ln(exp(lse_acc - M) + exp(lse_blk - M)),
+ *   O = exp(lse_acc - LSE) o_acc + exp(lse_blk - LSE) o_blk   (fp32 math).
+ * o_acc: device fp32, 16-byte aligned, laid out with the problem's o
+ * strides (element units); lse_acc: fp32 with the problem's LSE layout.
+ * o may be o_acc itself when out_dtype = CPA_FP32, and lse may be lse_acc
+ * itself when d_v <= 256 (in place); any other overlap of the accumulator
+ * with o, lse or ws is CPA_ERR_OVERLAP; a null accumulator CPA_ERR_NULL.
+ * Everything else (arguments, workspace, determinism) as for attn_fwd.
+ */
+cpa_status attn_fwd_accum(const cpa_problem* p, const void* q, const void* k,
+                          const void* v, const float* o_acc,
+                          const float* lse_acc, void* o, float* lse,
+                          void* ws, size_t ws_bytes, cpa_stream_t stream);
+
 /* Bytes of workspace attn_bwd needs (host, pure) for its fastest schedule:
  * the error flag, D = rowsum(dO*O), an fp32 dQ accumulator, a small table
  * of query positions per 64-row tile and the dS tiles of the whole key

@@ -94,6 +94,26 @@ def main():
     p = good_problem(); p.window = 1; p.window_left = 100; p.window_right = -1
     case("window_valid_reaches_launch", "CPA_ERR_LAUNCH", fwd(p))
 
+    def acc_fwd(p, oa=100, la=120, o=40, l=60, ws=80, wsb=256):
+        a = [None if x is None else ptr(x) for x in (oa, la, o, l, ws)]
+        return lib.attn_fwd_accum(ctypes.byref(p), ptr(1), ptr(2), ptr(3), *a, wsb, None)
+
+    p = good_problem()
+    case("accum_null_o_acc", "CPA_ERR_NULL", acc_fwd(p, oa=None))
+    case("accum_null_lse_acc", "CPA_ERR_NULL", acc_fwd(p, la=None))
+    # o_acc is fp32: the same pointer as a bf16 o is an overlap, not in place
+    case("accum_o_acc_is_bf16_o", "CPA_ERR_OVERLAP", acc_fwd(p, oa=40))
+    case("accum_o_acc_overlaps_workspace", "CPA_ERR_OVERLAP", acc_fwd(p, oa=80))
+    case("accum_lse_acc_overlaps_o", "CPA_ERR_OVERLAP", acc_fwd(p, la=40))
+    case("accum_misaligned_o_acc", "CPA_ERR_ALIGN",
+         lib.attn_fwd_accum(ctypes.byref(p), ptr(1), ptr(2), ptr(3), ctypes.c_void_p(A * 101 + 8),
+                            ptr(120), ptr(40), ptr(60), ptr(80), 256, None))
+    p = good_problem(); p.out_dtype = 1
+    case("accum_in_place_fp32_reaches_launch", "CPA_ERR_LAUNCH", acc_fwd(p, oa=40, la=60))
+    p = good_problem(512, 512); p.out_dtype = 1
+    case("accum_lse_in_place_d512_declined", "CPA_ERR_OVERLAP", acc_fwd(p, oa=40, la=60))
+    case("accum_d512_separate_lse_reaches_launch", "CPA_ERR_LAUNCH", acc_fwd(p, oa=40))
+
     def bwd(p, flags=0, wsb=1 << 30, dq=100, dk=120, dv=140):
         return lib.attn_bwd(ctypes.byref(p), ptr(1), ptr(2), ptr(3), ptr(40), ptr(50), ptr(60),
                             ptr(dq), ptr(dk), ptr(dv), ptr(200), wsb, flags, None)

@@ -88,18 +88,32 @@ def test_dense8k_heads():
 
 
 def test_cp4_rank_pipeline():
-    """Nine (chunk, KV block) forward partials in fp32, seven LSE merges, the
-    backward over both chunks, and the pack/unpack round trip, exactly as the
-    benchmark runs them; compared with the unsplit oracle on one head."""
+    """Nine (chunk, KV block) forward partials, seven of them merged by LSE
+    into their chunk's accumulator in the forward epilogue, the backward over
+    both chunks, and the pack/unpack round trip, exactly as the benchmark
+    runs them; the merged forward agrees with partials + separate merges to
+    one bf16 ulp, and the step matches the unsplit oracle on one head."""
     w = workloads.CONFIGS["cp4_rank"]
     x = workloads.draw_inputs(w)
     d = dev()
     qi, ki, vi, doi = (x[n].to(BF).to(d) for n in ("q", "k", "v", "do"))
     chunks = cp_chunks(w.seqlen_k, w.cp, w.cp_rank)
+    ru = RankStep(qi, ki, vi, doi, chunks, w.kv_blocks, scale=w.scale, pack_groups=w.cp,
+                  fused_merge=False)
+    assert ru.n_fwd_calls() == 9 and ru.n_merges() == 7
+    say("cp4_rank forward partials + separate merges")
+    ru.forward()
     rs = RankStep(qi, ki, vi, doi, chunks, w.kv_blocks, scale=w.scale, pack_groups=w.cp)
-    assert rs.n_fwd_calls() == 9 and rs.n_merges() == 7
-    say("cp4_rank forward partials + merges")
+    assert rs.n_fwd_calls() == 9 and rs.n_merges() == 0
+    say("cp4_rank forward partials merged in the epilogue")
     rs.forward()
+    torch.cuda.synchronize()
+    lf, lu = rs.lse.cpu().numpy(), ru.lse.cpu().numpy()
+    assert float(np.max(np.abs(lf - lu))) <= 2e-6
+    of, ou = rs.o.float().cpu().numpy(), ru.o.float().cpu().numpy()
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ou), 2.0 ** -126))) - 7)
+    assert np.all(np.abs(of - ou) <= ulp + 2e-6)   # one bf16 ulp + fp32 reordering
+    del ru
     say("cp4_rank pack/unpack")
     rs.pack_roundtrip()
     say("cp4_rank backward")
