@@ -412,52 +412,67 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
       f32x16 sacc, pacc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
-      // S and dP as two interleaved chains; the operands of step i + AHEAD
-      // are read before the products of step i.
+      // This lane's 16 rows are two runs of 8: qh*32 + 16*(v/8) + 8*hh + v%8.
+      const int rr0 = qh * 32 + 8 * hh;
+      // S = Q K^T as one chain; the operands of step i + AHEAD are read
+      // before the product of step i.
       {
-        constexpr int NS = KSQ > KSV ? KSQ : KSV, AHEAD = kSdpAhead;
-        CT8 qa[NS], kb[NS], oa[NS], vb[NS];
+        constexpr int AHEAD = kSdpAhead;
+        CT8 qa[KSQ], kb[KSQ];
         auto rd = [&](int i) {
-          if (i < KSQ) {
-            qa[i] = lds_row8(Qs, QP, rperm16(qh * 32 + pr), i * 16 + hh * 8);
-            kb[i] = lds_row8(Ks, KP, kg * 32 + lq, i * 16 + hh * 8);
-          }
-          if (i < KSV) {
-            oa[i] = lds_row8(dOs, OP, rperm16(qh * 32 + pr), i * 16 + hh * 8);
-            vb[i] = lds_row8(Vs, VP, kg * 32 + lq, i * 16 + hh * 8);
-          }
+          qa[i] = lds_row8(Qs, QP, rperm16(qh * 32 + pr), i * 16 + hh * 8);
+          kb[i] = lds_row8(Ks, KP, kg * 32 + lq, i * 16 + hh * 8);
         };
 #pragma unroll
         for (int i = 0; i < AHEAD; ++i) rd(i);
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          if (i + AHEAD < NS) rd(i + AHEAD);
-          if (i < KSQ) sacc = mfma32(qa[i], kb[i], sacc);
-          if (i < KSV) pacc = mfma32(oa[i], vb[i], pacc);
+        for (int i = 0; i < KSQ; ++i) {
+          if (i + AHEAD < KSQ) rd(i + AHEAD);
+          sacc = mfma32(qa[i], kb[i], sacc);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // This lane's 16 rows are two runs of 8: qh*32 + 16*vh + 8*hh + e.
+      // dP = dO V^T as a second chain; P = exp2(S s log2e - LSE log2e) of the
+      // finished scores is computed between its products, so the exponentials
+      // run while the matrix core works on dP.
+      {
+        float lr[16];
 #pragma unroll
-      for (int vh = 0; vh < 2; ++vh) {
-        const int rr = qh * 32 + 16 * vh + 8 * hh;
-        const float4 l0 = *reinterpret_cast<const float4*>(&Ls[rr]);
-        const float4 l1 = *reinterpret_cast<const float4*>(&Ls[rr + 4]);
-        const float4 d0 = *reinterpret_cast<const float4*>(&Dl[rr]);
-        const float4 d1 = *reinterpret_cast<const float4*>(&Dl[rr + 4]);
-        const float lr[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        const float dr[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int v = 8 * vh + e;
-          sacc[v] = fast_exp2(__builtin_fmaf(sacc[v], a.scale_log2, -lr[e]));
+        for (int vh = 0; vh < 2; ++vh) {
+          const float4 l0 = *reinterpret_cast<const float4*>(&Ls[rr0 + 16 * vh]);
+          const float4 l1 = *reinterpret_cast<const float4*>(&Ls[rr0 + 16 * vh + 4]);
+          lr[8 * vh + 0] = l0.x; lr[8 * vh + 1] = l0.y; lr[8 * vh + 2] = l0.z; lr[8 * vh + 3] = l0.w;
+          lr[8 * vh + 4] = l1.x; lr[8 * vh + 5] = l1.y; lr[8 * vh + 6] = l1.z; lr[8 * vh + 7] = l1.w;
         }
-        // need_mask is wave-uniform: one scalar branch around a branch-free
-        // pass (the query positions read as vectors, the conditions combined
-        // without short-circuit, so no per-element exec regions).
-        if (need_mask) {
-          const int4 p0 = *reinterpret_cast<const int4*>(&Ps[rr]);
-          const int4 p1 = *reinterpret_cast<const int4*>(&Ps[rr + 4]);
+        constexpr int AHEAD = kSdpAhead, PER = 16 / KSV;
+        static_assert(16 % KSV == 0, "exponentials per dP product");
+        CT8 oa[KSV], vb[KSV];
+        auto rd = [&](int i) {
+          oa[i] = lds_row8(dOs, OP, rperm16(qh * 32 + pr), i * 16 + hh * 8);
+          vb[i] = lds_row8(Vs, VP, kg * 32 + lq, i * 16 + hh * 8);
+        };
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i) rd(i);
+#pragma unroll
+        for (int i = 0; i < KSV; ++i) {
+          if (i + AHEAD < KSV) rd(i + AHEAD);
+          pacc = mfma32(oa[i], vb[i], pacc);
+#pragma unroll
+          for (int e = 0; e < PER; ++e) {
+            const int v = PER * i + e;
+            sacc[v] = fast_exp2(__builtin_fmaf(sacc[v], a.scale_log2, -lr[v]));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // need_mask is wave-uniform: one scalar branch around a branch-free
+      // pass (the query positions read as vectors, the conditions combined
+      // without short-circuit, so no per-element exec regions).
+      if (need_mask) {
+#pragma unroll
+        for (int vh = 0; vh < 2; ++vh) {
+          const int4 p0 = *reinterpret_cast<const int4*>(&Ps[rr0 + 16 * vh]);
+          const int4 p1 = *reinterpret_cast<const int4*>(&Ps[rr0 + 16 * vh + 4]);
           const int pq[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -465,27 +480,25 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
             sacc[8 * vh + e] = vis ? sacc[8 * vh + e] : 0.f;
           }
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int v = 8 * vh + e;
-          pacc[v] = sacc[v] * (pacc[v] - dr[e]);
-        }
       }
       CT8 wp[2];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        CT8 wd;
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          wp[tt][e] = (CT)sacc[8 * tt + e];
-          wd[e] = (CT)pacc[8 * tt + e];
-        }
-        // dS^T block of this wave: row = key, column = query row (natural order)
-        *reinterpret_cast<CT8*>(&Tw[lq * TP + 16 * tt + 8 * hh]) = wd;
-      }
-      // dV^T += dO^T P over the wave's 32 query rows, operands 2 steps ahead.
+        for (int e = 0; e < 8; ++e) wp[tt][e] = (CT)sacc[8 * tt + e];
+      // dV^T += dO^T P over the wave's 32 query rows, operands AHEAD steps
+      // ahead; dS = P (dP - D) is computed between its products.
       {
-        constexpr int N = 2 * NDV, AHEAD = kDvAhead;
+        float dr[16];
+#pragma unroll
+        for (int vh = 0; vh < 2; ++vh) {
+          const float4 d0 = *reinterpret_cast<const float4*>(&Dl[rr0 + 16 * vh]);
+          const float4 d1 = *reinterpret_cast<const float4*>(&Dl[rr0 + 16 * vh + 4]);
+          dr[8 * vh + 0] = d0.x; dr[8 * vh + 1] = d0.y; dr[8 * vh + 2] = d0.z; dr[8 * vh + 3] = d0.w;
+          dr[8 * vh + 4] = d1.x; dr[8 * vh + 5] = d1.y; dr[8 * vh + 6] = d1.z; dr[8 * vh + 7] = d1.w;
+        }
+        constexpr int N = 2 * NDV, AHEAD = kDvAhead, PER = 16 / N;
+        static_assert(16 % N == 0, "dS elements per dV product");
         CT8 oa[N];
         auto rd = [&](int i) {
           const int tt = i / NDV, db = i % NDV;
@@ -497,8 +510,21 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
         for (int i = 0; i < N; ++i) {
           if (i + AHEAD < N) rd(i + AHEAD);
           accv[i % NDV] = mfma32(oa[i], wp[i / NDV], accv[i % NDV]);
+#pragma unroll
+          for (int e = 0; e < PER; ++e) {
+            const int v = PER * i + e;
+            pacc[v] = sacc[v] * (pacc[v] - dr[v]);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        CT8 wd;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wd[e] = (CT)pacc[8 * tt + e];
+        // dS^T block of this wave: row = key, column = query row (natural order)
+        *reinterpret_cast<CT8*>(&Tw[lq * TP + 16 * tt + 8 * hh]) = wd;
       }
     } else {
 #pragma unroll
