@@ -631,7 +631,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   using CT8 = vec8<CT>;
   constexpr int KP = tr_pitch(DC);   // K is read only through transpose reads
   static_assert(DQK % DC == 0, "whole column chunks");
-  __shared__ __attribute__((aligned(16))) CT Ks[BN * KP];
+  __shared__ __attribute__((aligned(16))) CT Ks[2 * BN * KP];   // K tiles of consecutive blocks alternate
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
@@ -697,22 +697,27 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   // the loop head sees the same loads in flight from both of its entries.
   load_frags(kt_begin, fa);
   kst.load(K + kbase, a.k_stride[1], kt_begin * BN, s.klen, tid);
+  kst.store(Ks + (kt_begin & 1) * BN * KP, KP, tid);
+  kst.load(K + kbase, a.k_stride[1], min(kt_begin + 1, kt_end - 1) * BN, s.klen, tid);
   if (AHEAD == 2) load_frags(min(kt_begin + 1, kt_end - 1), fb);
+  // One barrier per block: block kt's K tile sits in buffer kt & 1 (stored
+  // during the previous step), and the step stores block kt + 1's tile into
+  // the other buffer, which every wave finished reading before the barrier.
   auto body = [&](int kt, const CT8 (&cur)[8], CT8 (&nn)[8]) {
     __syncthreads();
-    kst.store(Ks, KP, tid);
+    kst.store(Ks + ((kt + 1) & 1) * BN * KP, KP, tid);
     // Both prefetches are unconditional (clamped to the last block, whose
     // data is then unused), so every path issues the same loads and the
     // wait for the K tile above does not also wait for the dS prefetch.
-    kst.load(K + kbase, a.k_stride[1], min(kt + 1, kt_end - 1) * BN, s.klen, tid);
+    kst.load(K + kbase, a.k_stride[1], min(kt + 2, kt_end - 1) * BN, s.klen, tid);
     load_frags(min(kt + AHEAD, kt_end - 1), nn);
-    __syncthreads();
+    const CT* Kc = Ks + (kt & 1) * BN * KP;
     if (kt >= my_first && kt <= my_last) {
 #pragma unroll
       for (int t = 0; t < 8; ++t)
 #pragma unroll
         for (int db = 0; db < NDK; ++db)
-          acc[db] = mfma32(cur[t], lds_tr8(Ks, KP, 16 * t + 8 * (grp >> 1),
+          acc[db] = mfma32(cur[t], lds_tr8(Kc, KP, 16 * t + 8 * (grp >> 1),
                                            db * 32 + 16 * (grp & 1), gl), acc[db]);
     }
   };
