@@ -1,7 +1,8 @@
 // Causal attention forward with online softmax on gfx950.
 //
-// One workgroup = 4 waves = 128 query rows of one head (32 rows per wave);
-// KV tiles of 64 keys are staged row-major in LDS.  Each wave computes
+// One workgroup = 8 waves = 256 query rows of one head (32 rows per wave;
+// 4 waves = 128 rows for head dims 256 and 512); KV tiles of 64 keys are
+// staged row-major in LDS.  Each wave computes
 // S^T = K Q^T with the 32x32x16 bf16 matrix-core product, so that every lane
 // owns one query row: a row's max and sum need only an in-lane reduction
 // plus one swap with lane l^32.  The K rows are fed in a permuted order
@@ -24,23 +25,26 @@
 
 namespace cpa {
 
-// Two workgroups per CU where the registers allow it (<= 256 per lane): the
-// second workgroup's waves fill the gaps of the first (their barriers are
-// independent), which the measured kernel time shows to be worth more than
-// the accumulator registers a single workgroup could use.
+// Waves per workgroup, one workgroup per CU.  Where a wave's state fits 256
+// registers per lane (head dims up to 192/128): 8 waves over 256 query rows,
+// with the K/V tiles double-buffered in LDS so a tile costs one barrier, and
+// each K/V tile read from L2 serves twice the rows of a 4-wave workgroup
+// (measured faster than two independent 4-wave workgroups per CU with two
+// barriers per tile).  Head dims 256 and 512: 4 waves with 512 registers.
 template <int DSUM>
-constexpr int fwd_blocks_per_cu() { return DSUM <= 320 ? 2 : 1; }
+constexpr int fwd_waves() { return DSUM <= 320 ? 8 : 4; }
 
 template <int DQK, int DVC, int NCH, typename TIn, typename TOut, bool WIN>
-__global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kernel(const AttnArgs a) {
-  constexpr int BM = 128, BN = 64;
+__global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(const AttnArgs a) {
+  constexpr int NW = fwd_waves<DQK + DVC>(), NT = 64 * NW, BM = 32 * NW, BN = 64;
+  constexpr int NBUF = NW == 8 ? 2 : 1;
   using CT = ct_t<TIn>;   // matrix-core operand type
   using CT8 = vec8<CT>;
   constexpr int KP = lds_pitch(DQK), VP = tr_pitch(DVC);   // V: transpose reads only
   constexpr int KS = DQK / 16;
   constexpr int NDB = DVC / 32;
-  __shared__ __attribute__((aligned(16))) CT Ks[BN * KP];
-  __shared__ __attribute__((aligned(16))) CT Vs[BN * VP];
+  __shared__ __attribute__((aligned(16))) CT Ksb[NBUF * BN * KP];
+  __shared__ __attribute__((aligned(16))) CT Vsb[NBUF * BN * VP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
@@ -111,23 +115,42 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
   // tile t is being computed.  Rows past the last key repeat the last key
   // (limit = klen >= 1 when ntiles > 0): their scores are masked to -inf, so
   // they add nothing to O.
-  TileStage<BN, DQK, TIn, 256, false> kst;
-  TileStage<BN, DVC, TIn, 256, false> vst;
+  TileStage<BN, DQK, TIn, NT, false> kst;
+  TileStage<BN, DVC, TIn, NT, false> vst;
   if (t0 < ntiles) {
     kst.load(Kb, a.k_stride[1], t0 * BN, s.klen, tid);
     vst.load(Vb, a.v_stride[1], t0 * BN, s.klen, tid);
+    if constexpr (NBUF == 2) {
+      // tile t sits in buffer t & 1, stored one step ahead
+      kst.store(Ksb + (t0 & 1) * BN * KP, KP, tid);
+      vst.store(Vsb + (t0 & 1) * BN * VP, VP, tid);
+      const int jn = (t0 + 1 < ntiles ? t0 + 1 : t0) * BN;
+      kst.load(Kb, a.k_stride[1], jn, s.klen, tid);
+      vst.load(Vb, a.v_stride[1], jn, s.klen, tid);
+    }
   }
 
   for (int t = t0; t < ntiles; ++t) {
     const int j0 = t * BN;
+    const CT* Ks = Ksb + (NBUF == 2 ? (t & 1) : 0) * BN * KP;
+    const CT* Vs = Vsb + (NBUF == 2 ? (t & 1) : 0) * BN * VP;
     __syncthreads();
-    kst.store(Ks, KP, tid);
-    vst.store(Vs, VP, tid);
-    // (the last tile loads itself again: the same loads on every path)
-    const int jn = (t + 1 < ntiles ? t + 1 : t) * BN;
-    kst.load(Kb, a.k_stride[1], jn, s.klen, tid);
-    vst.load(Vb, a.v_stride[1], jn, s.klen, tid);
-    __syncthreads();
+    if constexpr (NBUF == 2) {
+      // the other buffer was last read in the previous step, before the barrier
+      kst.store(Ksb + ((t + 1) & 1) * BN * KP, KP, tid);
+      vst.store(Vsb + ((t + 1) & 1) * BN * VP, VP, tid);
+      const int jn = (t + 2 < ntiles ? t + 2 : ntiles - 1) * BN;
+      kst.load(Kb, a.k_stride[1], jn, s.klen, tid);
+      vst.load(Vb, a.v_stride[1], jn, s.klen, tid);
+    } else {
+      kst.store(Ksb, KP, tid);
+      vst.store(Vsb, VP, tid);
+      // (the last tile loads itself again: the same loads on every path)
+      const int jn = (t + 1 < ntiles ? t + 1 : t) * BN;
+      kst.load(Kb, a.k_stride[1], jn, s.klen, tid);
+      vst.load(Vb, a.v_stride[1], jn, s.klen, tid);
+      __syncthreads();
+    }
     if (!wave_active || (a.causal && kp0 + j0 > whi + bd.wr) ||
         (bd.left && kp0 + j0 + BN - 1 < wlo - bd.wl))
       continue;
@@ -137,9 +160,9 @@ __global__ __launch_bounds__(256, fwd_blocks_per_cu<DQK + DVC>()) void fwd_kerne
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
-    // Raised issue priority over each burst of products: the other
-    // workgroup's wave on the SIMD, when in its softmax, then fills the
-    // cycles the products leave free instead of delaying them.
+    // Raised issue priority over each burst of products: the SIMD's other
+    // wave, when in its softmax, then fills the cycles the products leave
+    // free instead of delaying them.
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -289,13 +312,14 @@ static hipError_t fwd_variant(const AttnArgs& a, hipStream_t st) {
   constexpr int DVC = DV > 256 ? 256 : DV;
   constexpr int NCH = DV / DVC;
   const int qrows = a.thd ? a.max_q : (int)a.seqlen_q;
-  const int ntile = (qrows + 127) / 128;
+  constexpr int NT = 64 * fwd_waves<DQK + DVC>(), BM = NT / 2;
+  const int ntile = (qrows + BM - 1) / BM;
   if (ntile == 0 || a.nseq == 0) return hipSuccess;
   dim3 grid(a.heads_q * NCH, ntile, a.nseq);
   if (needs_band(a))
-    hipLaunchKernelGGL((fwd_kernel<DQK, DVC, NCH, TIn, TOut, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<DQK, DVC, NCH, TIn, TOut, true>), grid, dim3(NT), 0, st, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<DQK, DVC, NCH, TIn, TOut, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<DQK, DVC, NCH, TIn, TOut, false>), grid, dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
