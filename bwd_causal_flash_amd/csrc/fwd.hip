@@ -36,7 +36,10 @@ constexpr int fwd_waves() { return DSUM <= 320 ? 8 : 4; }
 
 template <int DQK, int DVC, int NCH, typename TIn, typename TOut, bool WIN>
 __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(const AttnArgs a) {
-  constexpr int NW = fwd_waves<DQK + DVC>(), NT = 64 * NW, BM = 32 * NW, BN = 64;
+  constexpr int NW = fwd_waves<DQK + DVC>(), NT = 64 * NW, BM = 32 * NW;
+  // Keys per tile: 32 for head dim 512, whose 128-register Q operand and
+  // 128 accumulator registers per lane leave no room to stage 64-key tiles.
+  constexpr int BN = DQK > 256 ? 32 : 64, NKB = BN / 32;
   constexpr int NBUF = NW == 8 ? 2 : 1;
   using CT = ct_t<TIn>;   // matrix-core operand type
   using CT8 = vec8<CT>;
@@ -155,9 +158,9 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
         (bd.left && kp0 + j0 + BN - 1 < wlo - bd.wl))
       continue;
 
-    f32x16 sacc[2];
+    f32x16 sacc[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
     // Raised issue priority over each burst of products: the SIMD's other
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
         sacc[kb] = mfma32(lds_row8(Ks, KP, kb * 32 + kr, ks * 16 + hh * 8), qreg[ks], sacc[kb]);
     __builtin_amdgcn_s_setprio(0);
 
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
                            (bd.left && kp0 + j0 < whi - bd.wl);
     if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int j = j0 + kb * 32 + acc_row_perm(v, hh);
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
     // Row max of the raw scores (the scale is positive), in log2 units.
     float mx = -kInf;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
     mx = max_halves(mx) * a.scale_log2;
@@ -204,10 +207,10 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
         for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
     }
     const float base = m_run == -kInf ? 0.f : m_run;
-    float x[2][16];
+    float x[NKB][16];
     float rs = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         x[kb][v] = fast_exp2(__builtin_fmaf(sacc[kb][v], a.scale_log2, -base));
