@@ -405,9 +405,10 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
     const bool wave_on = on[qh];
     const bool need_mask = (jw + 32 > s.klen) || (a.causal && wlo + bd.wr < wkpos_hi) ||
                            (bd.left && whi - bd.wl > wkpos_lo);
-    // Next tile's Q/dO into registers (outside the per-wave branch, so the
-    // compiler sees one set of loads).
-    if (nhg < a.group) fetch(nhg, nut);
+    // Next tile's Q/dO into registers: between the first score products on
+    // waves with work (the address arithmetic then runs beside the matrix
+    // core), else at once; the same loads in the same order on both paths.
+    if (!wave_on && nhg < a.group) fetch(nhg, nut);
     if (wave_on) {
       f32x16 sacc, pacc;
 #pragma unroll
@@ -429,6 +430,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
         for (int i = 0; i < KSQ; ++i) {
           if (i + AHEAD < KSQ) rd(i + AHEAD);
           sacc = mfma32(qa[i], kb[i], sacc);
+          if (i == 0 && nhg < a.group) fetch(nhg, nut);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
