@@ -328,8 +328,11 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
     }
   };
 
-  TileStage<BM, DQK, TIn, NT> qst;
-  TileStage<BM, DV, TIn, NT> dost;
+  // Rows past the end of the sequence repeat its last row (finite): their
+  // LSE is staged as +inf and D as 0, so their P and dS are exactly 0 and
+  // the repeated values add nothing to dK or dV.
+  TileStage<BM, DQK, TIn, NT, false> qst;
+  TileStage<BM, DV, TIn, NT, false> dost;
   float pre_l = 0.f, pre_d = 0.f;
   int pre_p = 0;
   const int64_t qseq = a.thd ? s.q_row0 * a.q_stride[1] : (int64_t)z * a.q_stride[0];
