@@ -543,8 +543,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
     // the half's dS^T block.
     // Both halves run as one chain of 4*NDKH products whenever either is on,
     // so the operand reads run kDkAhead steps ahead across the halves.  An
-    // off half adds nothing: its dS block was written as zeros, and Q rows
-    // past the end of the sequence are zero-filled.
+    // off half adds nothing: its dS block was written as zeros; the Q rows
+    // past the end of the sequence (repeats of its last row) meet dS = 0.
     if (on[0] || on[1]) {
       CT8 wd[2][2];
 #pragma unroll
