@@ -35,6 +35,9 @@ CASES = [
     ("d192_kv_block_partial_fp32out", 1, 200, 256, 2, 2, 192, 128, "bf16", "fp32", True,
      [(0, 700)], 512),
     ("d64_fp32_in_bf16_out", 1, 190, 190, 2, 1, 64, 64, "fp32", "bf16", True, None, 0),
+    # all keys in one partial key tile (64 keys; 32 at head dim 512)
+    ("d192_128_one_key_tile", 1, 70, 40, 2, 2, 192, 128, "bf16", "bf16", True, None, 0),
+    ("d512_one_key_tile", 1, 33, 20, 2, 1, 512, 512, "bf16", "bf16", True, None, 0),
 ]
 
 DT = {"bf16": torch.bfloat16, "fp32": torch.float32}
