@@ -27,10 +27,9 @@ namespace cpa {
 
 // Waves per workgroup, one workgroup per CU.  Where a wave's state fits 256
 // registers per lane (head dims up to 192/128): 8 waves over 256 query rows,
-// with the K/V tiles double-buffered in LDS so a tile costs one barrier, and
-// each K/V tile read from L2 serves twice the rows of a 4-wave workgroup
-// (measured faster than two independent 4-wave workgroups per CU with two
-// barriers per tile).  Head dims 256 and 512: 4 waves with 512 registers.
+// each K/V tile read from L2 then serving twice the rows of a 4-wave
+// workgroup (measured faster than two independent 4-wave workgroups per CU).
+// Head dims 256 and 512: 4 waves with 512 registers.
 template <int DSUM>
 constexpr int fwd_waves() { return DSUM <= 320 ? 8 : 4; }
 
@@ -40,12 +39,16 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
   // Keys per tile: 32 for head dim 512, whose 128-register Q operand and
   // 128 accumulator registers per lane leave no room to stage 64-key tiles.
   constexpr int BN = DQK > 256 ? 32 : 64, NKB = BN / 32;
-  constexpr int NBUF = NW == 8 ? 2 : 1;
+  // K/V tiles double-buffered in LDS at every head dim (92 KB at 192/128,
+  // 142 KB at 256, 103 KB at 512 with its 32-key tiles), so a tile costs one
+  // barrier.
+  constexpr int NBUF = 2;
   using CT = ct_t<TIn>;   // matrix-core operand type
   using CT8 = vec8<CT>;
   constexpr int KP = lds_pitch(DQK), VP = tr_pitch(DVC);   // V: transpose reads only
   constexpr int KS = DQK / 16;
   constexpr int NDB = DVC / 32;
+  static_assert(NBUF * BN * (KP + VP) * (int)sizeof(CT) <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) CT Ksb[NBUF * BN * KP];
   __shared__ __attribute__((aligned(16))) CT Vsb[NBUF * BN * VP];
 
@@ -114,46 +117,35 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
   float m_run = -kInf, l_run = 0.f;
   const int kr = perm32(lq);
 
-  // K/V tiles go global -> registers -> LDS; tile t+1 is fetched while
-  // tile t is being computed.  Rows past the last key repeat the last key
-  // (limit = klen >= 1 when ntiles > 0): their scores are masked to -inf, so
-  // they add nothing to O.
+  // K/V tiles go global -> registers -> LDS, double-buffered: tile t sits
+  // in buffer t & 1, stored during the step before, and tile t+2 is fetched
+  // into registers while tile t is being computed.  Rows past the last key
+  // repeat the last key (limit = klen >= 1 when ntiles > 0): their scores
+  // are masked to -inf, so they add nothing to O.  (Fetches past the last
+  // tile load the last tile again: the same loads on every path.)
   TileStage<BN, DQK, TIn, NT, false> kst;
   TileStage<BN, DVC, TIn, NT, false> vst;
   if (t0 < ntiles) {
     kst.load(Kb, a.k_stride[1], t0 * BN, s.klen, tid);
     vst.load(Vb, a.v_stride[1], t0 * BN, s.klen, tid);
-    if constexpr (NBUF == 2) {
-      // tile t sits in buffer t & 1, stored one step ahead
-      kst.store(Ksb + (t0 & 1) * BN * KP, KP, tid);
-      vst.store(Vsb + (t0 & 1) * BN * VP, VP, tid);
-      const int jn = (t0 + 1 < ntiles ? t0 + 1 : t0) * BN;
-      kst.load(Kb, a.k_stride[1], jn, s.klen, tid);
-      vst.load(Vb, a.v_stride[1], jn, s.klen, tid);
-    }
+    kst.store(Ksb + (t0 & 1) * BN * KP, KP, tid);
+    vst.store(Vsb + (t0 & 1) * BN * VP, VP, tid);
+    const int jn = (t0 + 1 < ntiles ? t0 + 1 : t0) * BN;
+    kst.load(Kb, a.k_stride[1], jn, s.klen, tid);
+    vst.load(Vb, a.v_stride[1], jn, s.klen, tid);
   }
 
   for (int t = t0; t < ntiles; ++t) {
     const int j0 = t * BN;
-    const CT* Ks = Ksb + (NBUF == 2 ? (t & 1) : 0) * BN * KP;
-    const CT* Vs = Vsb + (NBUF == 2 ? (t & 1) : 0) * BN * VP;
+    const CT* Ks = Ksb + (t & 1) * BN * KP;
+    const CT* Vs = Vsb + (t & 1) * BN * VP;
     __syncthreads();
-    if constexpr (NBUF == 2) {
-      // the other buffer was last read in the previous step, before the barrier
-      kst.store(Ksb + ((t + 1) & 1) * BN * KP, KP, tid);
-      vst.store(Vsb + ((t + 1) & 1) * BN * VP, VP, tid);
-      const int jn = (t + 2 < ntiles ? t + 2 : ntiles - 1) * BN;
-      kst.load(Kb, a.k_stride[1], jn, s.klen, tid);
-      vst.load(Vb, a.v_stride[1], jn, s.klen, tid);
-    } else {
-      kst.store(Ksb, KP, tid);
-      vst.store(Vsb, VP, tid);
-      // (the last tile loads itself again: the same loads on every path)
-      const int jn = (t + 1 < ntiles ? t + 1 : t) * BN;
-      kst.load(Kb, a.k_stride[1], jn, s.klen, tid);
-      vst.load(Vb, a.v_stride[1], jn, s.klen, tid);
-      __syncthreads();
-    }
+    // the other buffer was last read in the previous step, before the barrier
+    kst.store(Ksb + ((t + 1) & 1) * BN * KP, KP, tid);
+    vst.store(Vsb + ((t + 1) & 1) * BN * VP, VP, tid);
+    const int jn = (t + 2 < ntiles ? t + 2 : ntiles - 1) * BN;
+    kst.load(Kb, a.k_stride[1], jn, s.klen, tid);
+    vst.load(Vb, a.v_stride[1], jn, s.klen, tid);
     if (!wave_active || (a.causal && kp0 + j0 > whi + bd.wr) ||
         (bd.left && kp0 + j0 + BN - 1 < wlo - bd.wl))
       continue;
