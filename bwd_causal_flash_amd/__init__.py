@@ -81,12 +81,89 @@ def _strides3(t: torch.Tensor, thd: bool):
     return (0, st[0], st[1]) if thd else (st[0], st[1], st[2])
 
 
+# ------------------------------------------------------------- validation
+#
+# The C ABI sees pointers and sizes only, so it cannot tell a tensor of the
+# wrong shape or dtype, or a host pointer, from a good one.  Every entry point
+# below checks its tensors against the problem before calling the library
+# (the pages' validation of dtypes, shapes and LSE before dispatch: PR 3527
+# "cuDNN FROST attention backend for head_dim in (256, 512]", commit notes on
+# input validation).  Shapes and dtypes are checked first, devices last.
+
+def _need(cond, msg, exc=ValueError):
+    if not cond:
+        raise exc(msg)
+
+
+def _shape(t, name, shape):
+    _need(isinstance(t, torch.Tensor), f"{name}: expected a tensor", TypeError)
+    _need(tuple(t.shape) == tuple(int(x) for x in shape),
+          f"{name}: shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+
+
+def _dtype(t, name, dtypes):
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    _need(t.dtype in dtypes, f"{name}: dtype {t.dtype}, expected {' or '.join(map(str, dtypes))}",
+          TypeError)
+
+
+def _same_device(named, ref):
+    """Every tensor on ``ref``'s device, which must be a GPU."""
+    _need(ref.is_cuda, f"tensors must be on a GPU (got {ref.device})")
+    for name, t in named:
+        if t is not None:
+            _need(t.is_cuda and t.device == ref.device,
+                  f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _check_qkv(q, k, v, varlen):
+    thd = q.dim() == 3
+    _need(q.dim() in (3, 4), "q must be [B, S, H, D] or [T, H, D]")
+    _dtype(q, "q", (torch.bfloat16, torch.float16, torch.float32))
+    _need(k.dim() == q.dim() and v.dim() == q.dim(), "q, k, v must have the same layout")
+    _dtype(k, "k", q.dtype)
+    _dtype(v, "v", q.dtype)
+    if thd:
+        _shape(v, "v", (k.shape[0], k.shape[1], v.shape[-1]))
+        _shape(k, "k", (k.shape[0], k.shape[1], q.shape[-1]))
+    else:
+        _shape(k, "k", (q.shape[0], k.shape[1], k.shape[2], q.shape[-1]))
+        _shape(v, "v", (q.shape[0], k.shape[1], k.shape[2], v.shape[-1]))
+    if varlen is not None:
+        n = varlen.seqused_q.numel()
+        for name in ("cu_seqlens_q", "cu_seqlens_k", "seqused_q", "seqused_k"):
+            t = getattr(varlen, name)
+            _dtype(t, f"varlen.{name}", torch.int32)
+            _need(t.dim() == 1 and t.is_contiguous(), f"varlen.{name} must be 1-D contiguous")
+        _shape(varlen.seqused_k, "varlen.seqused_k", (n,))
+        _shape(varlen.cu_seqlens_q, "varlen.cu_seqlens_q", (n + 1,))
+        _shape(varlen.cu_seqlens_k, "varlen.cu_seqlens_k", (n + 1,))
+
+
+def _varlen_tensors(varlen):
+    if varlen is None:
+        return []
+    return [(f"varlen.{n}", getattr(varlen, n))
+            for n in ("cu_seqlens_q", "cu_seqlens_k", "seqused_q", "seqused_k")]
+
+
+def _lse_expected(q, thd):
+    return (q.shape[1], q.shape[0]) if thd else (q.shape[0], q.shape[2], q.shape[1])
+
+
+def _check_workspace(ws, q):
+    if ws is not None:
+        _dtype(ws, "workspace", torch.uint8)
+        _need(ws.dim() == 1 and ws.is_contiguous(), "workspace must be 1-D contiguous")
+
+
 def _fill_problem(q, k, v, *, causal, scale, out_dtype, q_segments, k_pos_begin,
                   varlen: Optional[Varlen], window=None) -> Problem:
     p = Problem()
     thd = q.dim() == 3
     if thd != (varlen is not None):
         raise ValueError("3-D (THD) tensors need varlen metadata, 4-D (BSHD) must not have it")
+    _check_qkv(q, k, v, varlen)
     p.layout = 1 if thd else 0
     p.in_dtype = _dtype_code(q)
     p.out_dtype = out_dtype
@@ -150,11 +227,21 @@ def attn_fwd(q, k, v, o, lse, *, causal=True, scale=None, q_segments=None, k_pos
     (attn_fwd_accum; o, lse may be o_acc, lse_acc themselves).  Returns the
     workspace (its first int32 is the THD metadata error flag).
     """
-    lib = _lib.load()
     p = _fill_problem(q, k, v, causal=causal, scale=scale, out_dtype=_dtype_code(o),
                       q_segments=q_segments, k_pos_begin=k_pos_begin, varlen=varlen,
                       window=window)
     thd = p.layout == 1
+    _shape(o, "o", (*q.shape[:-1], v.shape[-1]))
+    _shape(lse, "lse", _lse_expected(q, thd))
+    _dtype(lse, "lse", torch.float32)
+    _check_workspace(workspace, q)
+    if acc is not None:
+        _need(len(acc) == 2, "acc = (o_acc, lse_acc)")
+        _shape(acc[0], "o_acc", o.shape)
+        _shape(acc[1], "lse_acc", lse.shape)
+    _same_device([("k", k), ("v", v), ("o", o), ("lse", lse), ("workspace", workspace),
+                  *(("acc", t) for t in (acc or ())), *_varlen_tensors(varlen)], q)
+    lib = _lib.load()
     p.o_stride = _strides3(o, thd)
     p.lse_stride = _lse_strides(lse, thd)
     need = lib.attn_fwd_workspace_size(ctypes.byref(p))
@@ -189,11 +276,25 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, *, causal=True, scale=None, q_se
         raise ValueError(step)
     if o.dtype != q.dtype or dout.dtype != q.dtype:
         raise TypeError("o and dout must have q's dtype")
-    lib = _lib.load()
     p = _fill_problem(q, k, v, causal=causal, scale=scale, out_dtype=_dtype_code(dq),
                       q_segments=q_segments, k_pos_begin=k_pos_begin, varlen=varlen,
                       window=window)
     thd = p.layout == 1
+    ov = (*q.shape[:-1], v.shape[-1])
+    _shape(o, "o", ov)
+    _shape(dout, "dout", ov)
+    _shape(lse, "lse", _lse_expected(q, thd))
+    _dtype(lse, "lse", torch.float32)
+    _shape(dq, "dq", q.shape)
+    _shape(dk, "dk", k.shape)
+    _shape(dv, "dv", v.shape)
+    _dtype(dk, "dk", dq.dtype)
+    _dtype(dv, "dv", dq.dtype)
+    _check_workspace(workspace, q)
+    _same_device([("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse), ("dq", dq),
+                  ("dk", dk), ("dv", dv), ("workspace", workspace),
+                  *_varlen_tensors(varlen)], q)
+    lib = _lib.load()
     p.o_stride = _strides3(o, thd)
     p.do_stride = _strides3(dout, thd)
     p.dq_stride = _strides3(dq, thd)
@@ -232,11 +333,20 @@ def attn_merge_lse(o_acc, lse_acc, o_part, lse_part, o_out=None, lse_out=None, *
     """(o_out, lse_out) = LSE merge of (o_acc, lse_acc) and (o_part,
     lse_part).  Defaults to in place on the accumulator.  O tensors are
     [B, S, H, D] or [S, H, D]; LSE [B, H, S] or [H, S]."""
-    lib = _lib.load()
     if o_out is None:
         o_out = o_acc
     if lse_out is None:
         lse_out = lse_acc
+    _need(o_acc.dim() in (3, 4), "O tensors are [B, S, H, D] or [S, H, D]")
+    for name, t in (("o_part", o_part), ("o_out", o_out)):
+        _shape(t, name, o_acc.shape)
+    lshape = (o_acc.shape[:-3] + (o_acc.shape[-2], o_acc.shape[-3]))
+    for name, t in (("lse_acc", lse_acc), ("lse_part", lse_part), ("lse_out", lse_out)):
+        _shape(t, name, lshape)
+        _dtype(t, name, torch.float32)
+    _same_device([("lse_acc", lse_acc), ("o_part", o_part), ("lse_part", lse_part),
+                  ("o_out", o_out), ("lse_out", lse_out)], o_acc)
+    lib = _lib.load()
     a4, la = _as4(o_acc, lse_acc)
     p4, lp = _as4(o_part, lse_part)
     o4, lo = _as4(o_out, lse_out)
@@ -258,6 +368,9 @@ def attn_merge_lse(o_acc, lse_acc, o_part, lse_part, o_out=None, lse_out=None, *
 
 
 def _pack_desc(o, lse, groups, force_int64):
+    _need(o.dim() in (3, 4), "o is [B, S, H, D] or [S, H, D]")
+    _shape(lse, "lse", o.shape[:-3] + (o.shape[-2], o.shape[-3]))
+    _dtype(lse, "lse", torch.float32)
     o4, l3 = _as4(o, lse)
     d = PackDesc()
     d.batch, d.seqlen, d.heads, d.d_v = o4.shape
@@ -279,8 +392,12 @@ def pack_saved_size(o, lse, groups) -> int:
 def pack_saved(o, lse, groups, buf=None, *, force_int64=False, stream=None) -> torch.Tensor:
     """Pack O and the raw fp32 LSE into per-head-group segments; returns the
     uint8 buffer."""
-    lib = _lib.load()
     d, o4, l3 = _pack_desc(o, lse, groups, force_int64)
+    if buf is not None:
+        _dtype(buf, "buf", torch.uint8)
+        _need(buf.dim() == 1 and buf.is_contiguous(), "buf must be 1-D contiguous")
+    _same_device([("lse", lse), ("buf", buf)], o)
+    lib = _lib.load()
     need = lib.pack_saved_size(ctypes.byref(d))
     if buf is None:
         buf = torch.empty(need, dtype=torch.uint8, device=o.device)
@@ -292,8 +409,11 @@ def pack_saved(o, lse, groups, buf=None, *, force_int64=False, stream=None) -> t
 
 def unpack_saved(buf, o, lse, groups, *, force_int64=False, stream=None):
     """Inverse of pack_saved, into preallocated o and lse."""
-    lib = _lib.load()
     d, o4, l3 = _pack_desc(o, lse, groups, force_int64)
+    _dtype(buf, "buf", torch.uint8)
+    _need(buf.dim() == 1 and buf.is_contiguous(), "buf must be 1-D contiguous")
+    _same_device([("lse", lse), ("buf", buf)], o)
+    lib = _lib.load()
     st = lib.unpack_saved(ctypes.byref(d), _ptr(buf), buf.numel(), _ptr(o4), _ptr(l3),
                           _stream_handle(stream))
     _lib.check(st, "unpack_saved")
@@ -360,8 +480,13 @@ def _ptr_array(tensors):
 
 def xchg_pack(tensors, *, groups, ranges, split, buf=None, stream=None) -> torch.Tensor:
     """Pack every segment of ``tensors`` into one uint8 buffer (returned)."""
-    lib = _lib.load()
     d = xchg_desc(tensors, groups=groups, ranges=ranges, split=split)
+    if buf is not None:
+        _dtype(buf, "buf", torch.uint8)
+        _need(buf.dim() == 1 and buf.is_contiguous(), "buf must be 1-D contiguous")
+    _same_device([(f"tensors[{i}]", t) for i, t in enumerate(tensors)] + [("buf", buf)],
+                 tensors[0])
+    lib = _lib.load()
     need = xchg_offsets(d)[-1]
     if buf is None:
         buf = torch.empty(need, dtype=torch.uint8, device=tensors[0].device)
@@ -373,8 +498,12 @@ def xchg_pack(tensors, *, groups, ranges, split, buf=None, stream=None) -> torch
 
 def xchg_unpack(buf, tensors, *, groups, ranges, split, stream=None):
     """Unpack a (received) buffer into ``tensors`` in place."""
-    lib = _lib.load()
     d = xchg_desc(tensors, groups=groups, ranges=ranges, split=split)
+    _dtype(buf, "buf", torch.uint8)
+    _need(buf.dim() == 1 and buf.is_contiguous(), "buf must be 1-D contiguous")
+    _same_device([(f"tensors[{i}]", t) for i, t in enumerate(tensors)] + [("buf", buf)],
+                 tensors[0])
+    lib = _lib.load()
     st = lib.xchg_unpack(ctypes.byref(d), _ptr(buf), buf.numel(), _ptr_array(tensors),
                          _stream_handle(stream))
     _lib.check(st, "xchg_unpack")

@@ -69,6 +69,44 @@ Dims dims_of(const cpa_problem* p) {
   return d;
 }
 
+// Launch grids: at most 65535 workgroups along y and z, at most 2^32 - 1
+// work-items along x.  Checked with the other arguments, so a problem whose
+// grids would not launch is declined before anything is enqueued.
+constexpr int64_t kGridYZ = 65535;
+constexpr int64_t kGridX = (1ll << 32) - 1;
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+struct GridRows {
+  int64_t qrows, krows, nseq;   // rows per sequence as the grids count them
+};
+GridRows grid_rows(const cpa_problem* p) {
+  const bool thd = p->layout == CPA_LAYOUT_THD;
+  return {thd ? p->max_seqlen_q : p->seqlen_q, thd ? p->max_seqlen_k : p->seqlen_k,
+          thd ? p->num_seqs : p->batch};
+}
+bool fwd_grids_ok(const cpa_problem* p) {
+  const GridRows g = grid_rows(p);
+  const bool big = p->d_qk + p->d_v > 320;
+  const int64_t bm = big ? 128 : 256, nch = p->d_v > 256 ? 2 : 1;
+  return cdiv(g.qrows, bm) <= kGridYZ && (int64_t)p->heads_q * nch * (2 * bm) <= kGridX;
+}
+int64_t pow2_at_least(int64_t x) { return x <= 8 ? 8 : x <= 16 ? 16 : x <= 32 ? 32 : 64; }
+bool bwd_grids_ok(const cpa_problem* p) {
+  const GridRows g = grid_rows(p);
+  const int64_t hq = p->heads_q, hkv = p->heads_kv;
+  const int64_t kblocks = cdiv(g.krows, 128), qtiles = cdiv(g.qrows, 64);
+  const bool big = p->d_qk + p->d_v > 320;
+  const int64_t dq_chunks = p->d_qk > 256 ? p->d_qk / 256 : 1;
+  if (g.qrows * hq * (p->d_v / 8) + 256 > kGridX) return false;               // pre
+  if (g.qrows * hq * pow2_at_least(p->d_qk / 8) + 256 > kGridX) return false;  // post
+  if (cdiv(qtiles, 64) * 64 > kGridX) return false;                            // tile table
+  if (kblocks > kGridYZ || cdiv(qtiles, 4) > kGridYZ) return false;            // main, dq
+  if (hq * dq_chunks * 512 > kGridX || hkv * 512 * (big ? p->d_qk / 128 : 1) > kGridX)
+    return false;
+  if (big && (cdiv(g.qrows, 128) > kGridYZ || hq * g.nseq > kGridYZ || kblocks * 512 > kGridX))
+    return false;                                                              // sdp
+  return true;
+}
+
 cpa_status check_problem(const cpa_problem* p) {
   if (!p) return CPA_ERR_NULL;
   if (p->layout != CPA_LAYOUT_BSHD && p->layout != CPA_LAYOUT_THD) return CPA_ERR_SHAPE;
@@ -116,6 +154,7 @@ cpa_status check_problem(const cpa_problem* p) {
   if (!strides_ok(p->q_stride, 3) || !strides_ok(p->k_stride, 3) || !strides_ok(p->v_stride, 3))
     return CPA_ERR_STRIDE;
   if (p->lse_stride[0] < 0 || p->lse_stride[1] < 0) return CPA_ERR_STRIDE;
+  if (!fwd_grids_ok(p)) return CPA_ERR_UNSUPPORTED;
   return CPA_OK;
 }
 
@@ -370,6 +409,7 @@ cpa_status bwd_prepare(const cpa_problem* p, const void* q, const void* k, const
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       (reinterpret_cast<uintptr_t>(lse) & 3))
     return CPA_ERR_ALIGN;
+  if (!bwd_grids_ok(p)) return CPA_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < attn_bwd_workspace_min(p) || !aligned16(ws)) return CPA_ERR_WORKSPACE;
   const int ib = dtype_bytes(p->in_dtype), ob = dtype_bytes(p->out_dtype);
   const Span ins[] = {qspan(p, q, p->q_stride, p->d_qk, ib),

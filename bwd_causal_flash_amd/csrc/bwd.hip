@@ -1126,7 +1126,7 @@ static hipError_t bwd_variant(const AttnArgs& a, int step, hipStream_t st) {
         hipLaunchKernelGGL((bwd_kv_kernel<DQK, DV, TIn, TOut, false>), g, dim3(512), 0, st, a);
     } else {
       static_assert(DQK == DV, "materialised path: symmetric head dims");
-      if ((int64_t)a.heads_q * a.nseq > 65535) return hipErrorInvalidValue;   // grid z
+      // (heads_q * nseq <= 65535, the grid's z limit, is checked on the host)
       if (qrows > 0) {
         dim3 g1((a.ds_nb + kSdpKeys / 128 - 1) / (kSdpKeys / 128), (qrows + 127) / 128,
                 a.heads_q * a.nseq);

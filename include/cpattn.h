@@ -67,7 +67,15 @@
  * GPU check of lengths and origins on every execution).
  *
  * Unsupported configurations are refused with CPA_ERR_UNSUPPORTED rather
- * than approximated (PR 3527, commit adding frost_attention.py).
+ * than approximated (PR 3527, commit adding frost_attention.py).  Among them
+ * are problems whose launch grids would exceed the device's limits (65535
+ * workgroups along a grid's y or z axis): more than 16,776,960 query rows
+ * per sequence in the forward (8,388,480 for head dims 256 and 512); in the
+ * backward more than 8,388,480 key rows or 16,776,960 query rows per
+ * sequence (8,388,480 query rows for head dims 256 and 512, where also at
+ * most 65535 (query head, sequence) pairs are accepted).  Rows per sequence are seqlen_* for BSHD and max_seqlen_*
+ * for THD.  These are declined by the host check, before anything is
+ * enqueued.
  */
 #ifndef CPATTN_H
 #define CPATTN_H

@@ -135,6 +135,19 @@ def main():
     case("bwd_dq_step_needs_full_workspace", "CPA_ERR_WORKSPACE", step(lib.attn_bwd_dq, need - 1))
     case("bwd_outputs_overlap", "CPA_ERR_OVERLAP", bwd(p, dk=100))
     case("bwd_output_overlaps_input", "CPA_ERR_OVERLAP", bwd(p, dq=2))
+    # launch grids past the device limits are declined by the host check
+    p = good_problem(d_qk=256, d_v=256); p.batch = 20000
+    case("bwd_d256_grid_z_declined", "CPA_ERR_UNSUPPORTED", bwd(p))
+    far = lambda i: ctypes.c_void_p((i + 1) << 40)   # disjoint fakes for huge tensors
+    fwd_far = lambda p: lib.attn_fwd(ctypes.byref(p), far(0), far(1), far(2), far(3), far(4),
+                                     far(5), 256, None)
+    case("fwd_d256_same_problem_reaches_launch", "CPA_ERR_LAUNCH", fwd_far(p))
+    p = good_problem(); p.seqlen_q = 1 << 24
+    case("fwd_grid_y_declined", "CPA_ERR_UNSUPPORTED", fwd(p))
+    p = good_problem(); p.seqlen_k = 65536 * 128
+    case("bwd_grid_y_key_blocks_declined", "CPA_ERR_UNSUPPORTED", bwd(p))
+    case("fwd_long_keys_reaches_launch", "CPA_ERR_LAUNCH", fwd_far(p))
+    p = good_problem()
     out["bwd_workspace_bytes"] = ["int", int(need)]
     out["bwd_workspace_min_bytes"] = ["int", int(least)]
     p = good_problem(d_qk=512, d_v=512)
