@@ -2,27 +2,32 @@
 """Benchmark: causal attention forward + backward of one context-parallel
 rank on one MI355X.
 
-Workload (the metric's configuration, workloads.CONFIGS["cp4_rank"]): rank 0
-of a 32768-token causal sequence under CP4 with the dual-chunk balance, so
-the rank holds query chunks 0 and 7 (4096 rows each, global positions kept)
-and all 32768 keys; 32 heads, QK/V head dims 192/128, bf16 inputs drawn from
-N(0, 1).  One step = the whole path on one batch:
+Default workload (the metric's configuration, workloads.CONFIGS["cp4_rank"]):
+rank 0 of a 32768-token causal sequence under CP4 with the dual-chunk
+balance, so the rank holds query chunks 0 and 7 (4096 rows each, global
+positions kept) and all 32768 keys; 32 heads, QK/V head dims 192/128, bf16
+inputs drawn from N(0, 1).  One step = the whole path on one batch:
   * 9 forward partials (query chunk x visible 4096-key block); each one
     after a chunk's first block is merged by LSE into the chunk's fp32
     accumulator in the forward kernel's epilogue (7 merges; the last
     writes the bf16 O),
   * pack + unpack of O and the fp32 LSE into 4 head-group segments,
-  * the backward (D, main kernel, dQ cast) over both chunks and all keys.
+  * the backward (D, main kernel, dQ, dQ cast) over both chunks and all keys.
 Inputs are resident in HBM before the timed region starts.
+
+--workload dense8k | thd_gqa | d512 times the other full-size configurations
+(B1 H32 S8192 D128; packed THD 32768 tokens Hq32/Hkv8 D128; B1 S16384
+Hq16/Hkv4 D512): one step = attn_fwd + attn_bwd on the whole problem.
 
 Prints ONE JSON line.  value = algorithmic TFLOP/s of the whole step:
 fwd 2*N_vis*(D_qk+D_v)*H + bwd 2*N_vis*(3*D_qk+2*D_v)*H, N_vis = visible
 (query, key) pairs per head (masked work and skipped tiles not counted).
-roofline = the dominant kernel (the backward's key-outer kernel, which forms
-S, dP, dS and accumulates dK, dV: 2*N_vis*(2*D_qk + 2*D_v)*H algorithmic
-FLOPs), those FLOPs per launch over its average launch time from HIP events
-on its own stream.  (dQ = dS K runs in a separate query-outer kernel.)
-cpu_baseline = the fp64 oracle on one head of the same workload.
+ms_per_step is the timed region over the step count; the per-step times
+(HIP events between consecutive steps) give median, p10 and p90.
+roofline = the dominant kernel, the backward's key-outer main step (S, dP,
+dS, dK, dV: 2*N_vis*(2*D_qk + 2*D_v)*H algorithmic FLOPs), those FLOPs per
+launch over its average launch time from HIP events on its own stream.
+cpu_baseline = the fp64 oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -38,10 +43,15 @@ if ROOT not in sys.path:
 
 METRIC = "causal attn fwd+bwd ms & TFLOP/s (BF16, % MFMA peak), 32K-seq CP4 rank shape"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_kv_kernel_cp4_rank_traffic.md")
 KERNEL_SOURCES = ("bwd_causal_flash_amd/csrc/bwd.hip", "bwd_causal_flash_amd/csrc/device_common.h",
                   "bwd_causal_flash_amd/csrc/internal.h")
 COPY_BYTES = 512 << 20        # calibration copy: reads and writes this many bytes
+WORKLOADS = ("cp4_rank", "dense8k", "thd_gqa", "d512")
+MAIN_KERNEL = {"cp4_rank": "bwd_kv_kernel<192,128>", "dense8k": "bwd_kv_kernel<128,128>",
+               "thd_gqa": "bwd_kv_kernel<128,128>",
+               "d512": "bwd_sdp_kernel<512> + bwd_dkv_kernel<512>"}
 
 
 def visible_pairs(q_positions, n_keys):
@@ -87,27 +97,177 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(w, x, qpos):
-    """Time the oracle (fp64 numpy, as it stands) on one head, fwd + bwd."""
-    import numpy as np
-    import oracle
+def cpu_info():
+    """CPU model (from /proc/cpuinfo) and the cores this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, x):
+    """Time the oracle (fp64 numpy, as it stands) on one head of the
+    workload, forward + backward; d512 on the last 2048 query rows of one
+    head (they see the most keys).  Returns the contract's object."""
+    import numpy as np
+    import oracle
     h = 0
-    a = [x[n][0, :, h:h + 1].double().numpy() for n in ("q", "k", "v", "do")]
     t0 = time.perf_counter()
-    oracle.forward(a[0], a[1], a[2], w.scale, qpos)
-    oracle.backward(*a, w.scale, qpos)
+    if w.layout == "thd":
+        used, cu = x["seqused"], x["cu_seqlens"]
+        kvh = h // (w.heads_q // w.heads_kv)
+        a = [x[n][:, sl].double().numpy() for n, sl in
+             (("q", slice(h, h + 1)), ("k", slice(kvh, kvh + 1)), ("v", slice(kvh, kvh + 1)),
+              ("do", slice(h, h + 1)))]
+        oracle.thd_forward(a[0], a[1], a[2], w.scale, cu, cu, used, used)
+        oracle.thd_backward(*a, w.scale, cu, cu, used, used)
+        nvis = int(sum(int(n) * (int(n) + 1) // 2 for n in used))
+        sample = f"q-head 0 of thd_gqa over all {len(used)} documents"
+    else:
+        kvh = h // (w.heads_q // w.heads_kv)
+        a = [x[n][0, :, sl].double().numpy() for n, sl in
+             (("q", slice(h, h + 1)), ("k", slice(kvh, kvh + 1)), ("v", slice(kvh, kvh + 1)),
+              ("do", slice(h, h + 1)))]
+        if w.name == "cp4_rank":
+            from bwd_causal_flash_amd.pipeline import cp_chunks
+            qpos = np.concatenate([np.arange(c[2], c[2] + c[1])
+                                   for c in cp_chunks(w.seqlen_k, w.cp, w.cp_rank)])
+            sample = (f"1 of {w.heads_q} heads of cp4_rank (8192 query rows x 32768 keys, "
+                      f"D 192/128)")
+        elif w.name == "d512":
+            rows = np.arange(w.seqlen_q - 2048, w.seqlen_q)
+            a[0], a[3] = a[0][rows], a[3][rows]
+            qpos = rows
+            sample = f"1 of {w.heads_q} heads of d512, last 2048 query rows x {w.seqlen_k} keys"
+        else:
+            qpos = np.arange(w.seqlen_q)
+            sample = f"1 of {w.heads_q} heads of {w.name} ({w.seqlen_q} rows, D {w.d_qk})"
+        oracle.forward(a[0], a[1], a[2], w.scale, qpos)
+        oracle.backward(*a, w.scale, qpos)
+        nvis = visible_pairs(qpos, w.seqlen_k)
     dt = time.perf_counter() - t0
-    nvis = visible_pairs(qpos, w.seqlen_k)
     f, b = flops(nvis, 1, w.d_qk, w.d_v)
-    return {"value": round((f + b) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"1 of {w.heads_q} heads of cp4_rank (8192 query rows x 32768 keys, "
-                      f"D 192/128), fwd+bwd in fp64 numpy: {dt:.2f} s"}
+    model, aff = cpu_info()
+    return {"value": round((f + b) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads()),
+            "kind": "oracle", "sample": f"{sample}, fwd+bwd in fp64 numpy: {dt:.2f} s",
+            "cpu_model": model, "affinity_cores": aff}
+
+
+class SimpleStep:
+    """attn_fwd + attn_bwd over a whole problem (dense BSHD or packed THD),
+    every buffer and workspace allocated once."""
+
+    def __init__(self, w, x, dev):
+        import torch
+        import bwd_causal_flash_amd as cpa
+        self.cpa = cpa
+        bf = torch.bfloat16
+        self.q, self.k, self.v, self.dout = (x[n].to(bf).to(dev) for n in ("q", "k", "v", "do"))
+        self.scale = w.scale
+        self.varlen = None
+        if w.layout == "thd":
+            used, cu = x["seqused"], x["cu_seqlens"]
+            tcu, tused = torch.tensor(cu, device=dev), torch.tensor(used, device=dev)
+            self.varlen = cpa.Varlen(tcu, tcu, tused, tused, int(used.max()), int(used.max()))
+            self.lse = torch.empty(w.heads_q, w.seqlen_q, dtype=torch.float32, device=dev)
+        else:
+            self.lse = torch.empty(w.batch, w.heads_q, w.seqlen_q, dtype=torch.float32, device=dev)
+        self.o = torch.empty(*self.q.shape[:-1], w.d_v, dtype=bf, device=dev)
+        self.dq, self.dk, self.dv = (torch.empty_like(t) for t in (self.q, self.k, self.v))
+        self.fwd_ws = torch.empty(256, dtype=torch.uint8, device=dev)
+        n = cpa.bwd_workspace_bytes(self.q, self.k, self.v, varlen=self.varlen)
+        self.bwd_ws = torch.empty(n, dtype=torch.uint8, device=dev)
+
+    def step(self, stream, main_events=None):
+        cpa = self.cpa
+        cpa.attn_fwd(self.q, self.k, self.v, self.o, self.lse, scale=self.scale, varlen=self.varlen,
+                     workspace=self.fwd_ws, stream=stream)
+        kw = dict(scale=self.scale, varlen=self.varlen, workspace=self.bwd_ws, stream=stream)
+        args = (self.q, self.k, self.v, self.o, self.dout, self.lse, self.dq, self.dk, self.dv)
+        cpa.attn_bwd(*args, step="attn_bwd_pre", **kw)
+        if main_events:
+            main_events[0].record(stream)
+        cpa.attn_bwd(*args, step="attn_bwd_main", **kw)
+        if main_events:
+            main_events[1].record(stream)
+        cpa.attn_bwd(*args, step="attn_bwd_dq", **kw)
+        cpa.attn_bwd(*args, step="attn_bwd_post", **kw)
+
+
+def time_fn(fn, stream, reps):
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def breakdown_cp4(rs, w, x, chunks, stream, dev):
+    """Per-phase times of the cp4_rank step and the memory-bound kernels
+    alone, with algorithmic GB/s against the HBM peak."""
+    import torch
+    import bwd_causal_flash_amd as cpa
+    out = {}
+    out["forward_ms"] = time_fn(lambda: rs.forward(stream), stream, 5)
+    out["pack_unpack_ms"] = time_fn(lambda: rs.pack_roundtrip(stream), stream, 10)
+    out["backward_ms"] = time_fn(lambda: rs.backward(stream), stream, 5)
+    kw = dict(causal=True, scale=rs.scale, q_segments=rs.segments, k_pos_begin=0,
+              workspace=rs.bwd_ws, stream=stream)
+    args = (rs.q, rs.k, rs.v, rs.o, rs.dout, rs.lse, rs.dq, rs.dk, rs.dv)
+    rows_heads = w.seqlen_q * w.heads_q
+
+    def hbm(name, ms, nbytes):
+        out[name] = {"ms": round(ms, 4), "bytes": int(nbytes),
+                     "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+
+    # D = rowsum(dO*O) + zeroed dQ accumulator (+ the tiny tile table): per
+    # (row, head) reads 2*D_v*2 B, writes 4 B + D_qk*4 B
+    hbm("bwd_pre", time_fn(lambda: cpa.attn_bwd(*args, step="attn_bwd_pre", **kw), stream, 20),
+        rows_heads * (2 * w.d_v * 2 + 4 + w.d_qk * 4))
+    # dQ = s*acc: reads D_qk*4 B, writes D_qk*2 B per (row, head)
+    hbm("bwd_post", time_fn(lambda: cpa.attn_bwd(*args, step="attn_bwd_post", **kw), stream, 20),
+        rows_heads * (w.d_qk * 4 + w.d_qk * 2))
+    # pack and unpack: O (bf16) + LSE, read and written once each way
+    nb = rows_heads * (w.d_v * 2 + 4)
+    hbm("pack_saved", time_fn(lambda: cpa.pack_saved(rs.o, rs.lse, rs.pack_groups, rs.pack_buf,
+                                                     stream=stream), stream, 20), 2 * nb)
+    hbm("unpack_saved", time_fn(lambda: cpa.unpack_saved(rs.pack_buf, rs.o_recv, rs.lse_recv,
+                                                         rs.pack_groups, stream=stream),
+                                stream, 20), 2 * nb)
+    # a ring step's LSE merge alone at this shape: one 4096-row chunk, fp32
+    # accumulator and fp32 partial, in place (reads 2 x (D_v*4 + 4) B, writes
+    # D_v*4 + 4 B per (row, head))
+    c = chunks[1]
+    n = c[1]
+    g = torch.Generator(device=dev).manual_seed(5)
+    o_acc = torch.randn(1, n, w.heads_q, w.d_v, device=dev, generator=g)
+    o_part = torch.randn(1, n, w.heads_q, w.d_v, device=dev, generator=g)
+    l_acc = torch.randn(1, w.heads_q, n, device=dev, generator=g)
+    l_part = torch.randn(1, w.heads_q, n, device=dev, generator=g)
+    hbm("attn_merge_lse", time_fn(lambda: cpa.attn_merge_lse(o_acc, l_acc, o_part, l_part,
+                                                             stream=stream), stream, 20),
+        n * w.heads_q * 3 * (w.d_v * 4 + 4))
+    for k_ in ("forward_ms", "pack_unpack_ms", "backward_ms"):
+        out[k_] = round(out[k_], 4)
+    return out
 
 
 def main():
@@ -115,9 +275,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=WORKLOADS, default="cp4_rank")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true",
-                    help="also print per-phase times (stderr)")
+                    help="cp4_rank: also time each phase and the memory-bound kernels alone "
+                         "(added to the JSON line as 'breakdown')")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain elementwise copy of a known size "
                          "(for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -130,80 +292,59 @@ def main():
     import numpy as np
     import torch
     import workloads
-    from bwd_causal_flash_amd.pipeline import RankStep, cp_chunks
-    import oracle  # noqa: F401  (cpu baseline only)
 
-    w = workloads.CONFIGS["cp4_rank"]
+    w = workloads.CONFIGS[args.workload]
     x = workloads.draw_inputs(w)
     dev = torch.device("cuda:0")
-    q, k, v, do = (x[n].to(torch.bfloat16).to(dev) for n in ("q", "k", "v", "do"))
-    chunks = cp_chunks(w.seqlen_k, w.cp, w.cp_rank)
-    rs = RankStep(q, k, v, do, chunks, w.kv_blocks, scale=w.scale, pack_groups=w.cp)
-    qpos = np.concatenate([np.arange(c[2], c[2] + c[1]) for c in chunks])
-    nvis = visible_pairs(qpos, w.seqlen_k)
+    chunks = None
+    if w.name == "cp4_rank":
+        from bwd_causal_flash_amd.pipeline import RankStep, cp_chunks
+        q, k, v, do = (x[n].to(torch.bfloat16).to(dev) for n in ("q", "k", "v", "do"))
+        chunks = cp_chunks(w.seqlen_k, w.cp, w.cp_rank)
+        runner = RankStep(q, k, v, do, chunks, w.kv_blocks, scale=w.scale, pack_groups=w.cp)
+        qpos = np.concatenate([np.arange(c[2], c[2] + c[1]) for c in chunks])
+        nvis = visible_pairs(qpos, w.seqlen_k)
+        config = {"workload": "cp4_rank", "seq_len": w.seqlen_k, "cp": w.cp, "rank": w.cp_rank,
+                  "q_rows": w.seqlen_q, "kv_blocks": w.kv_blocks, "heads": w.heads_q,
+                  "d_qk": w.d_qk, "d_v": w.d_v, "batch": w.batch}
+    else:
+        runner = SimpleStep(w, x, dev)
+        if w.layout == "thd":
+            nvis = int(sum(int(n) * (int(n) + 1) // 2 for n in x["seqused"]))
+        else:
+            nvis = w.batch * w.seqlen_q * (w.seqlen_q + 1) // 2
+        config = {"workload": w.name, "layout": w.layout, "batch": w.batch,
+                  "seq_len": w.seqlen_q, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+                  "d_qk": w.d_qk, "d_v": w.d_v}
+        if w.layout == "thd":
+            config["documents"] = int(len(x["seqused"]))
     f_fwd, f_bwd = flops(nvis, w.heads_q, w.d_qk, w.d_v)
     f_kv = kv_kernel_flops(nvis, w.heads_q, w.d_qk, w.d_v)
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        rs.step(stream)
+        runner.step(stream)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    E = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    ev = [(E(), E()) for _ in range(args.steps)]
+    marks = [E() for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record(stream)
     for i in range(args.steps):
-        rs.step(stream, main_events=ev[i])
-    t_end.record(stream)
+        marks[i].record(stream)
+        runner.step(stream, main_events=ev[i])
+    marks[-1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    ms_step = marks[0].elapsed_time(marks[-1]) / args.steps
     main_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
     achieved = f_kv / (main_ms * 1e-3) / 1e12
 
-    if args.breakdown:
-        phases = {}
-        for name, fn in (("forward(9 partials, 7 merged in the epilogue)", lambda: rs.forward(stream)),
-                         ("pack+unpack", lambda: rs.pack_roundtrip(stream)),
-                         ("backward(pre+main+dq+post)", lambda: rs.backward(stream))):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(5):
-                fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            phases[name] = round(a.elapsed_time(b) / 5, 4)
-        # head-parallel exchange buffer: this rank's Q, K, V, O, dO rows and LSE
-        # packed seq -> heads into 4 head-group segments (and unpacked back)
-        import bwd_causal_flash_amd as cpa
-        rows = torch.cat([torch.arange(c[0], c[0] + c[1]) for c in chunks]).to(dev)
-        kpos = torch.cat([torch.arange(c[2], c[2] + c[1]) for c in chunks]).to(dev)
-        fields = [rs.q, k[:, kpos].contiguous(), v[:, kpos].contiguous(), rs.o, rs.dout,
-                  rs.lse]
-        every = [[(0, int(rows.numel()))]] * w.cp
-        xbuf = cpa.xchg_pack(fields, groups=w.cp, ranges=every, split=True, stream=stream)
-        outs = [torch.empty_like(f) for f in fields]
-        for name, fn in (("xchg_pack", lambda: cpa.xchg_pack(fields, groups=w.cp, ranges=every,
-                                                             split=True, buf=xbuf, stream=stream)),
-                         ("xchg_unpack", lambda: cpa.xchg_unpack(xbuf, outs, groups=w.cp,
-                                                                 ranges=every, split=True,
-                                                                 stream=stream))):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(10):
-                fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            ms = a.elapsed_time(b) / 10
-            phases[name] = round(ms, 4)
-            phases[name + "_GBps(read+write)"] = round(2 * xbuf.numel() / (ms * 1e-3) / 1e9, 1)
-        print(json.dumps({"phase_ms": phases, "main_ms": round(main_ms, 4),
-                          "fwd_tflops": round(f_fwd / 1e12, 4),
-                          "bwd_tflops": round(f_bwd / 1e12, 4)}), file=sys.stderr)
+    extra = {}
+    if args.breakdown and w.name == "cp4_rank":
+        extra["breakdown"] = breakdown_cp4(runner, w, x, chunks, stream, dev)
 
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -212,9 +353,16 @@ def main():
             torch.mul(src, 1.0, out=dst)    # one elementwise kernel: reads and writes COPY_BYTES
         torch.cuda.synchronize()
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, x, qpos)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, x)
+    config.update({"frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+                   "ms_median": round(float(np.median(step_ms)), 4),
+                   "ms_p10": round(float(np.percentile(step_ms, 10)), 4),
+                   "ms_p90": round(float(np.percentile(step_ms, 90)), 4),
+                   "fwd_tflop": round(f_fwd / 1e12, 4), "bwd_tflop": round(f_bwd / 1e12, 4),
+                   "wall_s_timed": round(wall, 3)})
     out = {
-        "metric": METRIC,
+        "metric": METRIC if w.name == "cp4_rank" else
+        f"causal attn fwd+bwd ms & TFLOP/s (BF16, % MFMA peak), {w.description}",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -226,16 +374,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "cp4_rank", "seq_len": w.seqlen_k, "cp": w.cp,
-                   "rank": w.cp_rank, "q_rows": w.seqlen_q, "kv_blocks": w.kv_blocks,
-                   "heads": w.heads_q, "d_qk": w.d_qk, "d_v": w.d_v, "batch": w.batch,
-                   "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
-                   "wall_s_timed": round(wall, 3)},
-        "roofline": {"bound": "mfma", "kernel": "bwd_kv_kernel<192,128>",
+        "config": config,
+        "roofline": {"bound": "mfma", "kernel": MAIN_KERNEL[w.name],
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "avg_launch_ms": round(main_ms, 4), "traffic": measured_traffic()},
+                     "avg_launch_ms": round(main_ms, 4),
+                     "traffic": measured_traffic() if w.name == "cp4_rank" else None},
         "cpu_baseline": cpu,
+        **extra,
     }
     print(json.dumps(out))
 

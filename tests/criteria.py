@@ -20,7 +20,14 @@ naive reference is reported too ("ratio_in"), as a diagnostic.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
+
+# Every passing check() of the session, for the one-line margin summary the
+# test session prints at its end (tests/conftest.py): test id, output name,
+# err / (2 floor), err / (2 unrounded floor), rel-L2.
+RECORDS = []
 
 
 def as64(x):
@@ -92,14 +99,35 @@ def passes(r):
     return r["pass_floor"] and r.get("pass_l2", True)
 
 
+def _record(name, r):
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0].split("::", 1)[-1]
+    RECORDS.append((test, name, r["ratio"], r["ratio_in"], r.get("rel_l2")))
+
+
 def check(name, gpu, true, naive, *, mask=None, grad=False, log=None, out_bf16=False):
     r = evaluate(gpu, true, naive, mask=mask, grad=grad, out_bf16=out_bf16)
     if log is not None:
         log[name] = r
+    _record(name, r)
     assert r["pass_floor"], f"{name}: err {r['err']:.3e} > 2 x floor {r['floor']:.3e}"
     if grad:
         assert r["pass_l2"], f"{name}: rel L2 {r['rel_l2']:.4f} >= 0.008"
     return r
+
+
+def summary():
+    """Worst margins per test and output: {test: {output: [ratio, ratio_in,
+    rel_l2]}} (ratio = err / (2 floor); a check passes at ratio <= 1)."""
+    out = {}
+    for test, name, ratio, ratio_in, l2 in RECORDS:
+        cur = out.setdefault(test, {}).get(name)
+        new = [round(ratio, 3), round(ratio_in, 3), None if l2 is None else round(l2, 5)]
+        if cur is None:
+            out[test][name] = new
+        else:
+            out[test][name] = [max(cur[0], new[0]), max(cur[1], new[1]),
+                               None if l2 is None else max(cur[2] or 0, new[2])]
+    return out
 
 
 def check_lse(name, gpu, true, naive, *, mask=None, log=None):

@@ -153,3 +153,40 @@ def test_pack_strided_source_and_reused_allocation():
     # bytes outside the views are untouched
     assert (recv[:, :100].float() == 7).all() and (recv[..., 128:].float() == 7).all()
     assert (lrecv[..., :10] == 3).all() and (lrecv[..., 310:] == 3).all()
+
+
+def test_pack_beyond_2gib_takes_the_wide_path():
+    """A 2.7 GB O (bf16 [1, 81920, 64, 256]) in 4 head groups: segment 3
+    lies past byte 2^31 of the buffer, so pack_saved must take its 64-bit
+    offset path on its own (PR 3510, Validation: both index widths, with a
+    real large-stride case).  The buffer equals the oracle's byte layout and
+    the round trip is exact."""
+    b, s, h, d, groups = 1, 81920, 64, 256, 4
+    g = dev()
+    gen = torch.Generator(device=g).manual_seed(77)
+    o_d = torch.randint(-32768, 32767, (b, s, h, d), generator=gen, device=g,
+                        dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    l_d = torch.randint(-2**31, 2**31 - 1, (b, h, s), generator=gen, device=g,
+                        dtype=torch.int64).to(torch.int32).view(torch.float32)
+    seg, obytes, loff = oracle.pack_layout(b, s, h, d, 2, groups)
+    assert groups * seg > 2**31 and 3 * seg < 2**31 < 3 * seg + obytes
+    say("pack > 2 GiB")
+    buf = cpa.pack_saved(o_d, l_d, groups)
+    torch.cuda.synchronize()
+    ref = oracle.pack_saved(o_d.view(torch.int16).cpu().numpy().view(np.uint16),
+                            l_d.cpu().numpy(), groups)
+    got = buf.cpu().numpy()
+    assert got.size == ref.size
+    n = h // groups * s * 4
+    for sg in range(groups):
+        a = sg * seg
+        assert np.array_equal(got[a:a + obytes], ref[a:a + obytes]), sg
+        assert np.array_equal(got[a + loff:a + loff + n], ref[a + loff:a + loff + n]), sg
+    del ref, got
+    o2 = torch.empty_like(o_d)
+    l2 = torch.empty_like(l_d)
+    say("unpack > 2 GiB")
+    cpa.unpack_saved(buf, o2, l2, groups)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.view(torch.int16), o_d.view(torch.int16))
+    assert torch.equal(l2.view(torch.int32), l_d.view(torch.int32))

@@ -46,8 +46,10 @@ def _pad_rows(cu, used):
     return np.asarray(rows, np.int64)
 
 
-@pytest.mark.parametrize("bottom_right", [False, True])
-def test_thd_parity_and_padding_untouched(bottom_right):
+def _thd_case(bottom_right, scale_mult=1.0):
+    """Seven documents (one empty, one of one row) at a 64-row pitch, padding
+    inputs NaN, padding outputs sentinel-filled; returns the GPU outputs, the
+    oracle's true and naive results and the real-row masks."""
     used_q = np.array([37, 0, 130, 1, 200, 64, 5], np.int32)
     used_k = used_q.copy() if not bottom_right else np.array([50, 3, 100, 70, 200, 64, 0], np.int32)
     pitch = 64
@@ -73,20 +75,20 @@ def test_thd_parity_and_padding_untouched(bottom_right):
                     int(used_q.max()), int(used_k.max()), bottom_right)
     o = _sentinel((T, hq, d), torch.bfloat16, dv_)
     lse = _sentinel((hq, T), torch.float32, dv_)
-    say(f"thd fwd br={bottom_right}")
-    ws = cpa.attn_fwd(qi, ki, vi, o, lse, varlen=vl)
+    scale = 1 / math.sqrt(d)
+    say(f"thd fwd br={bottom_right} scale x{scale_mult}")
+    ws = cpa.attn_fwd(qi, ki, vi, o, lse, varlen=vl, scale=scale * scale_mult)
     dq = _sentinel((T, hq, d), torch.bfloat16, dv_)
     dk = _sentinel((T, hkv, d), torch.bfloat16, dv_)
     dvv = _sentinel((T, hkv, d), torch.bfloat16, dv_)
-    say(f"thd bwd br={bottom_right}")
-    ws2 = cpa.attn_bwd(qi, ki, vi, o, doi, lse, dq, dk, dvv, varlen=vl)
+    say(f"thd bwd br={bottom_right} scale x{scale_mult}")
+    ws2 = cpa.attn_bwd(qi, ki, vi, o, doi, lse, dq, dk, dvv, varlen=vl, scale=scale * scale_mult)
     torch.cuda.synchronize()
     assert cpa.workspace_error_flag(ws) == 0 and cpa.workspace_error_flag(ws2) == 0
     for t, rows in ((o, pad_q), (dq, pad_q), (dk, pad_k), (dvv, pad_k)):
         assert (bits(t)[rows] == np.int16(SENT_BF16)).all()
     assert (bits(lse)[:, pad_q] == np.int32(SENT_F32)).all()
 
-    scale = 1 / math.sqrt(d)
     ref = {}
     for kind, f in (("true", true64), ("naive", naive64)):
         oo, ll = oracle.thd_forward(f(q), f(k), f(v), scale, cu_q, cu_k, used_q, used_k, True,
@@ -96,16 +98,42 @@ def test_thd_parity_and_padding_untouched(bottom_right):
         ref[kind] = dict(o=oo, lse=ll, dq=a, dk=b_, dv=c)
     real_q = np.ones(T, bool); real_q[pad_q] = False
     real_k = np.ones(T, bool); real_k[pad_k] = False
-    mq = np.broadcast_to(real_q[:, None, None], (T, hq, d))
-    mk = np.broadcast_to(real_k[:, None, None], (T, hkv, d))
+    masks = dict(o=np.broadcast_to(real_q[:, None, None], (T, hq, d)),
+                 dq=np.broadcast_to(real_q[:, None, None], (T, hq, d)),
+                 dk=np.broadcast_to(real_k[:, None, None], (T, hkv, d)),
+                 dv=np.broadcast_to(real_k[:, None, None], (T, hkv, d)),
+                 lse=np.broadcast_to(real_q[None], (hq, T)))
+    return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dvv), ref, masks
+
+
+@pytest.mark.parametrize("bottom_right", [False, True])
+def test_thd_parity_and_padding_untouched(bottom_right):
+    out, ref, masks = _thd_case(bottom_right)
     log = {}
-    criteria.check("O", o, ref["true"]["o"], ref["naive"]["o"], mask=mq, log=log, out_bf16=True)
-    criteria.check_lse("LSE", lse, ref["true"]["lse"], ref["naive"]["lse"],
-                       mask=np.broadcast_to(real_q[None], (hq, T)), log=log)
-    criteria.check("dq", dq, ref["true"]["dq"], ref["naive"]["dq"], mask=mq, grad=True, log=log, out_bf16=True)
-    criteria.check("dk", dk, ref["true"]["dk"], ref["naive"]["dk"], mask=mk, grad=True, log=log, out_bf16=True)
-    criteria.check("dv", dvv, ref["true"]["dv"], ref["naive"]["dv"], mask=mk, grad=True, log=log, out_bf16=True)
+    criteria.check("O", out["o"], ref["true"]["o"], ref["naive"]["o"], mask=masks["o"], log=log,
+                   out_bf16=True)
+    criteria.check_lse("LSE", out["lse"], ref["true"]["lse"], ref["naive"]["lse"],
+                       mask=masks["lse"], log=log)
+    for g in ("dq", "dk", "dv"):
+        criteria.check(g, out[g], ref["true"][g], ref["naive"][g], mask=masks[g], grad=True,
+                       log=log, out_bf16=True)
     print(log)
+
+
+def test_thd_one_percent_scale_error_is_rejected():
+    """The same THD case with the softmax scale 1% off must fail the
+    criterion (PR 3527, Verification: the bound has to catch a 1% error)."""
+    out, ref, masks = _thd_case(False, scale_mult=1.01)
+    fails = {}
+    for g in ("o", "dq", "dk", "dv"):
+        r = criteria.evaluate(out[g], ref["true"][g], ref["naive"][g], mask=masks[g],
+                              grad=(g != "o"), out_bf16=True)
+        fails[g] = not criteria.passes(r)
+    fin = masks["lse"] & np.isfinite(ref["naive"]["lse"])
+    fails["lse"] = criteria.max_err(out["lse"], ref["naive"]["lse"], fin) > 1e-4
+    print("thd 1% scale error caught by:", fails)
+    assert fails["lse"]
+    assert fails["o"] or fails["dq"] or fails["dk"] or fails["dv"], fails
 
 
 def test_thd_malformed_metadata_sets_flag_and_skips_sequence():

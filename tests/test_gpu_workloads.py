@@ -187,19 +187,16 @@ def test_thd_gqa_full():
                masks={"o": m, "dq": m})
     criteria.check_lse("lse", lse[:1], ref["true"]["lse"], ref["naive"]["lse"],
                        mask=np.broadcast_to(real[None], (1, T)), log=log)
-    # kv-head 1 (q heads 4..7) on the four shortest documents: dK, dV
-    docs = sorted(range(len(used)), key=lambda n: used[n])[:4]
-    for n in docs:
-        a0, L = int(cu[n]), int(used[n])
-        r = slice(a0, a0 + L)
-        refk = {}
-        for kind, f in (("true", true64), ("naive", naive64)):
-            a = [f(x[nm][r]) for nm in ("q", "k", "v", "do")]
-            _, gk, gv = oracle.backward(a[0][:, 4:8], a[1][:, 1:2], a[2][:, 1:2], a[3][:, 4:8],
-                                        w.scale)
-            refk[kind] = dict(dk=gk, dv=gv)
-        gk = dict(dk=dk[r, 1:2], dv=dv[r, 1:2])
-        _check_all(log, gk, refk["true"], refk["naive"], out_bf16=True, names=("dk", "dv"))
+    # kv-head 1 (q heads 4..7) over every document: dK, dV
+    refk = {}
+    for kind, f in (("true", true64), ("naive", naive64)):
+        a = [f(x[nm][:, sl]) for nm, sl in (("q", slice(4, 8)), ("k", slice(1, 2)),
+                                            ("v", slice(1, 2)), ("do", slice(4, 8)))]
+        _, gk, gv = oracle.thd_backward(*a, w.scale, cu, cu, used, used)
+        refk[kind] = dict(dk=gk, dv=gv)
+    gk = dict(dk=dk[:, 1:2], dv=dv[:, 1:2])
+    _check_all(log, gk, refk["true"], refk["naive"], out_bf16=True, names=("dk", "dv"),
+               masks={"dk": m, "dv": m})
     _report("thd_gqa", log)
 
 
@@ -218,13 +215,25 @@ def test_d512_sampled():
     for kind, f in (("true", true64), ("naive", naive64)):
         a = [f(x[n][0]) for n in ("q", "k", "v", "do")]
         oo, ll = oracle.forward_rows(a[0], a[1], a[2], w.scale, rows)
-        gq, gk, gv = oracle.backward(a[0][rows], a[1], a[2], a[3][rows], w.scale, q_pos=rows)
-        # only rows >= S-64 see keys >= S-64, so these dK/dV are exact
-        ref[kind] = dict(o=oo, lse=ll, dq=gq, dk=gk[S - 64:], dv=gv[S - 64:])
-    g = dict(o=o[0, rows], dq=dq[0, rows], dk=dk[0, S - 64:], dv=dv[0, S - 64:])
+        gq, _, _ = oracle.backward(a[0][rows], a[1], a[2], a[3][rows], w.scale, q_pos=rows)
+        ref[kind] = dict(o=oo, lse=ll, dq=gq)
+    g = dict(o=o[0, rows], dq=dq[0, rows])
     log = {}
-    _check_all(log, g, ref["true"], ref["naive"], out_bf16=True)
+    _check_all(log, g, ref["true"], ref["naive"], out_bf16=True, names=("o", "dq"))
     criteria.check_lse("lse", lse[0][:, rows], ref["true"]["lse"], ref["naive"]["lse"], log=log)
+    # dK, dV of the last 2048 keys of kv head 2 (query heads 8..11): only
+    # rows >= S-2048 see them, so the oracle over those rows gives them
+    # exactly; they span 16 key blocks and 32 query tiles of the dK/dV kernel
+    n = 2048
+    r = np.arange(S - n, S)
+    refk = {}
+    for kind, f in (("true", true64), ("naive", naive64)):
+        a = [f(x[nm][0][:, sl]) for nm, sl in (("q", slice(8, 12)), ("k", slice(2, 3)),
+                                               ("v", slice(2, 3)), ("do", slice(8, 12)))]
+        _, gk, gv = oracle.backward(a[0][r], a[1], a[2], a[3][r], w.scale, q_pos=r)
+        refk[kind] = dict(dk=gk[S - n:], dv=gv[S - n:])
+    gk = dict(dk=dk[0, S - n:, 2:3], dv=dv[0, S - n:, 2:3])
+    _check_all(log, gk, refk["true"], refk["naive"], out_bf16=True, names=("dk", "dv"))
     # identities at full size: sum_j dK_j = 0; sum_j dV_j = sum_i dO_i per group
     dk64 = dk[0].double()
     dv64 = dv[0].double()
