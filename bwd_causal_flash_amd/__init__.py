@@ -30,7 +30,7 @@ from ._lib import (CPA_BF16, CPA_FP16, CPA_FP32, CPA_FLAG_DETERMINISTIC, CpaErro
                    MergeDesc, PackDesc, Problem, STATUS_CODE)
 
 __all__ = [
-    "attn_fwd", "attn_bwd", "bwd_workspace_bytes", "attn_merge_lse", "pack_saved", "unpack_saved",
+    "attn_fwd", "attn_bwd", "attn_bwd_static", "bwd_workspace_bytes", "attn_merge_lse", "pack_saved", "unpack_saved",
     "pack_saved_size", "Varlen", "CpaError", "forward", "backward",
     "workspace_error_flag", "library",
 ]
@@ -310,6 +310,47 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, *, causal=True, scale=None, q_se
             _stream_handle(stream))
     _lib.check(st, step)
     return workspace
+
+
+def attn_bwd_static(q, k, v, o, dout, lse, dq, dk, dv, *, err_flag=None, causal=True,
+                    scale=None, q_segments=None, k_pos_begin=0,
+                    varlen: Optional[Varlen] = None, flags=0, stream=None, window=None):
+    """Backward into preallocated dq, dk, dv with the library's fixed
+    per-GPU workspace (attn_bwd_static): no allocation.  ``err_flag``: a
+    device int32 tensor of one element for the THD metadata flag (required
+    for THD)."""
+    if o.dtype != q.dtype or dout.dtype != q.dtype:
+        raise TypeError("o and dout must have q's dtype")
+    p = _fill_problem(q, k, v, causal=causal, scale=scale, out_dtype=_dtype_code(dq),
+                      q_segments=q_segments, k_pos_begin=k_pos_begin, varlen=varlen,
+                      window=window)
+    thd = p.layout == 1
+    ov = (*q.shape[:-1], v.shape[-1])
+    _shape(o, "o", ov)
+    _shape(dout, "dout", ov)
+    _shape(lse, "lse", _lse_expected(q, thd))
+    _dtype(lse, "lse", torch.float32)
+    _shape(dq, "dq", q.shape)
+    _shape(dk, "dk", k.shape)
+    _shape(dv, "dv", v.shape)
+    _dtype(dk, "dk", dq.dtype)
+    _dtype(dv, "dv", dq.dtype)
+    if err_flag is not None:
+        _dtype(err_flag, "err_flag", torch.int32)
+        _need(err_flag.numel() >= 1, "err_flag needs one element")
+    _same_device([("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse), ("dq", dq),
+                  ("dk", dk), ("dv", dv), ("err_flag", err_flag), *_varlen_tensors(varlen)], q)
+    lib = _lib.load()
+    p.o_stride = _strides3(o, thd)
+    p.do_stride = _strides3(dout, thd)
+    p.dq_stride = _strides3(dq, thd)
+    p.dk_stride = _strides3(dk, thd)
+    p.dv_stride = _strides3(dv, thd)
+    p.lse_stride = _lse_strides(lse, thd)
+    st = lib.attn_bwd_static(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                             _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(err_flag), int(flags),
+                             _stream_handle(stream))
+    _lib.check(st, "attn_bwd_static")
 
 
 def bwd_workspace_bytes(q, k, v, *, varlen=None, minimum=False, **kw) -> int:

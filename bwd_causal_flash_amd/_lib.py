@@ -16,6 +16,7 @@ CPA_BF16, CPA_FP32, CPA_FP16 = 0, 1, 2
 CPA_LAYOUT_BSHD, CPA_LAYOUT_THD = 0, 1
 CPA_MAX_SEGMENTS = 8
 CPA_FLAG_DETERMINISTIC = 1
+CPA_BWD_STATIC_WORKSPACE_BYTES = 256 << 20
 
 STATUS = {
     0: "CPA_OK", 1: "CPA_ERR_NULL", 2: "CPA_ERR_SHAPE", 3: "CPA_ERR_DTYPE",
@@ -123,6 +124,8 @@ EXPORTS = {
                       [ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]),
     "attn_bwd_post": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 +
                       [ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]),
+    "attn_bwd_static": (ctypes.c_int, [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 +
+                        [ctypes.c_uint32, ctypes.c_void_p]),
     "attn_merge_lse": (ctypes.c_int, [ctypes.POINTER(MergeDesc)] + [ctypes.c_void_p] * 7),
     "pack_saved_size": (ctypes.c_size_t, [ctypes.POINTER(PackDesc)]),
     "pack_saved": (ctypes.c_int, [ctypes.POINTER(PackDesc), ctypes.c_void_p, ctypes.c_void_p,

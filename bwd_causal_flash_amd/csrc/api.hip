@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 using namespace cpa;
@@ -446,12 +448,32 @@ cpa_status bwd_prepare(const cpa_problem* p, const void* q, const void* k, const
 // bit 3 = post.  The whole backward runs main and dq band by band when the
 // workspace holds fewer dS key blocks than the key range; the single steps
 // need room for the whole range.
+// flag: where the metadata error flag goes instead of the workspace's first
+// word (nullptr: the workspace).
 cpa_status bwd_run(const cpa_problem* p, const void* q, const void* k, const void* v,
                    const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                   void* ws, size_t ws_bytes, uint32_t flags, cpa_stream_t stream, int steps) {
+                   void* ws, size_t ws_bytes, uint32_t flags, cpa_stream_t stream, int steps,
+                   int32_t* flag = nullptr) {
   AttnArgs a;
   const cpa_status st = bwd_prepare(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, flags, a);
   if (st != CPA_OK) return st;
+  if (flag) {
+    const int ib = dtype_bytes(p->in_dtype), ob = dtype_bytes(p->out_dtype);
+    const Span sf = {reinterpret_cast<uintptr_t>(flag), reinterpret_cast<uintptr_t>(flag) + 4};
+    const Span all[] = {qspan(p, q, p->q_stride, p->d_qk, ib),
+                        kspan(p, k, p->k_stride, p->d_qk, ib),
+                        kspan(p, v, p->v_stride, p->d_v, ib),
+                        qspan(p, o, p->o_stride, p->d_v, ib),
+                        qspan(p, dout, p->do_stride, p->d_v, ib),
+                        lsespan(p, lse),
+                        qspan(p, dq, p->dq_stride, p->d_qk, ob),
+                        kspan(p, dk, p->dk_stride, p->d_qk, ob),
+                        kspan(p, dv, p->dv_stride, p->d_v, ob),
+                        {reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + ws_bytes}};
+    for (const Span& x : all)
+      if (overlap(sf, x)) return CPA_ERR_OVERLAP;
+    a.err_flag = flag;
+  }
   const int64_t nkb = ds_key_blocks(p);
   if (steps != 15 && (steps & 6) && a.ds_nb < nkb) return CPA_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -657,6 +679,66 @@ cpa_status unpack_saved(const cpa_pack_desc* d, const void* buf, size_t buf_byte
                         float* lse, cpa_stream_t stream) {
   return run_pack(d, nullptr, nullptr, buf, nullptr, buf_bytes, o, lse, true,
                   reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ------------------------------------------- backward without allocation
+//
+// attn_bwd_static: the backward with its workspace in a fixed device array
+// instead of a caller-provided buffer, for callers that cannot allocate.
+// Each GPU holds its own copy of the array from the first call on it until
+// the process ends; its address is looked up once per device.
+constexpr size_t kStaticWsBytes = CPA_BWD_STATIC_WORKSPACE_BYTES;
+static __device__ __align__(256) char scratch[kStaticWsBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The array's device address on the current device (which must be the
+// stream's device), looked up on the first call there.
+cpa_status static_workspace(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CPA_ERR_LAUNCH;
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return CPA_ERR_LAUNCH;
+    if (sdev != dev) return CPA_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return CPA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return CPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cpa_status attn_bwd_static(const cpa_problem* p, const void* q, const void* k, const void* v,
+                           const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                           void* dv, int32_t* err_flag, uint32_t flags, cpa_stream_t stream) {
+  // Host checks that need no device come first.
+  const cpa_status st = check_problem(p);
+  if (st != CPA_OK) return st;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return CPA_ERR_NULL;
+  if (p->layout == CPA_LAYOUT_THD && !err_flag) return CPA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(err_flag) & 3) return CPA_ERR_ALIGN;
+  if (attn_bwd_workspace_min(p) > kStaticWsBytes) return CPA_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  const cpa_status sw = static_workspace(s, &ws);
+  if (sw != CPA_OK) return sw;
+  return bwd_run(p, q, k, v, o, dout, lse, dq, dk, dv, ws, kStaticWsBytes, flags, stream, 15,
+                 err_flag);
 }
 
 }  // extern "C"

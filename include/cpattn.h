@@ -279,6 +279,37 @@ cpa_status attn_bwd_post(const cpa_problem* p, const void* q, const void* k,
                          cpa_stream_t stream);
 
 /*
+ * The backward (as attn_bwd) with no workspace argument and no allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Its
+ * workspace is a device array of CPA_BWD_STATIC_WORKSPACE_BYTES (256 MiB)
+ * inside the library; each GPU the library runs on holds its own copy until
+ * the process ends, and its address is looked up once per device on the
+ * first call there (the calling thread's current device, which must be the
+ * stream's device, else CPA_ERR_UNSUPPORTED).  Problems whose smallest
+ * workspace (attn_bwd_workspace_min) exceeds the array are refused with
+ * CPA_ERR_WORKSPACE; others run with the keys in bands of as many 128-key
+ * blocks as fit, exactly as attn_bwd with a workspace of that size (so dK
+ * and dV are bitwise those of attn_bwd; dQ equals attn_bwd's with a 256 MiB
+ * workspace bit for bit).  Every call on one GPU uses the same array and
+ * the kernels rewrite every byte of it they later read, so nothing needs
+ * clearing between calls; calls that overlap in time on one GPU (different
+ * streams, or host threads) race on the array and must be serialised by
+ * the caller.
+ * err_flag: device int32 (4-byte aligned) that receives the THD metadata
+ * flag (0 or nonzero, as the workspace's first word for attn_bwd); required
+ * for THD (CPA_ERR_NULL), may be NULL for BSHD; must not overlap any
+ * tensor.  Other arguments, flags and errors as attn_bwd.  With no usable
+ * device the call returns CPA_ERR_LAUNCH.
+ */
+enum { CPA_BWD_STATIC_WORKSPACE_BYTES = 256 << 20 };
+cpa_status attn_bwd_static(const cpa_problem* p, const void* q, const void* k,
+                           const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv,
+                           int32_t* err_flag, uint32_t flags,
+                           cpa_stream_t stream);
+
+/*
  * LSE merge of two partial attentions over disjoint key sets (the per-ring-
  * step combine of PR 3527's context-parallel commits: per-step kernel calls
  * interleaved with KV exchange and LSE correction).  Per (b, s, h):

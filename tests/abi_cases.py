@@ -147,6 +147,20 @@ def main():
     p = good_problem(); p.seqlen_k = 65536 * 128
     case("bwd_grid_y_key_blocks_declined", "CPA_ERR_UNSUPPORTED", bwd(p))
     case("fwd_long_keys_reaches_launch", "CPA_ERR_LAUNCH", fwd_far(p))
+    # the backward with the library's own workspace array
+    def bstatic(p, flag=300):
+        f = None if flag is None else ctypes.c_void_p(A * flag if flag > 0 else -flag)
+        return lib.attn_bwd_static(ctypes.byref(p), ptr(1), ptr(2), ptr(3), ptr(40), ptr(50),
+                                   ptr(60), ptr(100), ptr(120), ptr(140), f, 0, None)
+    p = good_problem()
+    case("static_valid_reaches_device_lookup", "CPA_ERR_LAUNCH", bstatic(p))
+    case("static_bshd_without_flag_accepted", "CPA_ERR_LAUNCH", bstatic(p, None))
+    case("static_misaligned_flag", "CPA_ERR_ALIGN", bstatic(p, -(A * 300 + 2)))
+    p = good_problem(); p.seqlen_q = p.seqlen_k = 1 << 16; p.heads_q = 64; p.heads_kv = 8
+    case("static_too_large", "CPA_ERR_WORKSPACE", bstatic(p))
+    p = good_problem(); p.layout = 1; p.num_seqs = 1
+    p.cu_seqlens_q = p.cu_seqlens_k = p.seqused_q = p.seqused_k = A * 400
+    case("static_thd_needs_flag", "CPA_ERR_NULL", bstatic(p, None))
     p = good_problem()
     out["bwd_workspace_bytes"] = ["int", int(need)]
     out["bwd_workspace_min_bytes"] = ["int", int(least)]
