@@ -265,6 +265,16 @@ def breakdown_cp4(rs, w, x, chunks, stream, dev):
     hbm("attn_merge_lse", time_fn(lambda: cpa.attn_merge_lse(o_acc, l_acc, o_part, l_part,
                                                              stream=stream), stream, 20),
         n * w.heads_q * 3 * (w.d_v * 4 + 4))
+    # the backward with smaller workspaces: the keys in bands of 128-key
+    # blocks (attn_bwd_workspace_min = one block per band, and a ~2 GiB band)
+    full = rs.bwd_ws.numel()
+    least = cpa.bwd_workspace_bytes(rs.q, rs.k, rs.v, minimum=True)
+    for name, nbytes in (("backward_ws_min", least), ("backward_ws_2GiB", min(full, 2 << 30))):
+        ws = rs.bwd_ws[:nbytes]
+        kwb = dict(kw, workspace=ws)
+        out[name] = {"workspace_bytes": int(nbytes),
+                     "ms": round(time_fn(lambda: cpa.attn_bwd(*args, **kwb), stream, 3), 4)}
+    out["backward_ws_full"] = {"workspace_bytes": int(full), "ms": round(out["backward_ms"], 4)}
     for k_ in ("forward_ms", "pack_unpack_ms", "backward_ms"):
         out[k_] = round(out[k_], 4)
     return out
@@ -342,7 +352,10 @@ def main():
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
     achieved = f_kv / (main_ms * 1e-3) / 1e12
 
-    extra = {}
+    # device memory the step holds: inputs, outputs, partial/accumulator
+    # buffers, pack buffers and the backward workspace (the library itself
+    # allocates nothing)
+    extra = {"peak_device_bytes": int(torch.cuda.max_memory_allocated(dev))}
     if args.breakdown and w.name == "cp4_rank":
         extra["breakdown"] = breakdown_cp4(runner, w, x, chunks, stream, dev)
 
