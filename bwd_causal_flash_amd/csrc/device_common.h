@@ -242,6 +242,53 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
 
+// Keep loop-carried matrix-core accumulators in the accumulator registers
+// (for kernels at one wave per SIMD, whose products write their results
+// there): without this hint the compiler moved them through the vector
+// registers at every loop iteration.
+template <int N>
+__device__ __forceinline__ void pin_acc(f32x16 (&acc)[N]) {
+#pragma unroll
+  for (int d = 0; d < N; ++d) asm volatile("" : "+a"(acc[d]));
+}
+
+// Workgroup barrier after which the LDS writes of this wave's direct
+// global-to-LDS copies are complete as well: those copies count as vector
+// memory operations (vmcnt), which the compiler does not track for LDS.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Direct global-to-LDS copy of a [ROWS x D] tile of 2-byte elements into an
+// LDS tile of pitch P elements (logical row r at row rperm16(r) when PERM):
+// gfx950's 16-byte global_load_lds, with no staging registers.  Each wave
+// instruction fills 64 consecutive 16-byte LDS slots (lane l the slot at
+// the wave's base + l), so each lane loads the global chunk that belongs
+// in its slot; slots of the row padding load the row's first chunk (never
+// read).  Source rows past `limit` repeat the last row (limit >= 1).
+// NTH = threads of the workgroup; w, lane = the caller's wave and lane.
+template <int ROWS, int D, int P, int NTH, bool PERM, typename T>
+__device__ __forceinline__ void dma_tile(const T* base, int64_t row_stride, int r0, int limit,
+                                         T* tile, int w, int lane) {
+  static_assert(sizeof(T) == 2 && P % 8 == 0 && D % 8 == 0 && P >= D, "16-byte slots");
+  constexpr int S = P / 8, DS = D / 8, TOT = ROWS * S;
+#pragma unroll
+  for (int r = 0; r * NTH < TOT; ++r) {
+    const int s0 = r * NTH + w * 64;   // this wave's first slot (uniform)
+    if (s0 < TOT) {
+      const int sl = s0 + lane;
+      const int prow = sl / S, cs = sl % S;
+      const int lrow = PERM ? rperm16(prow) : prow;
+      const int grow = min(r0 + lrow, limit - 1);
+      const T* g = base + (int64_t)grow * row_stride + (cs < DS ? cs : 0) * 8;
+      if (sl < TOT)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(uintptr_t)g,
+            (__attribute__((address_space(3))) void*)(tile + s0 * 8), 16, 0, 0);
+    }
+  }
+}
+
 // ---------------------------------------------------------- sequences
 
 // One sequence (BSHD batch entry or THD document) as the kernels see it.

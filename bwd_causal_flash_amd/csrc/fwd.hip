@@ -29,7 +29,8 @@ namespace cpa {
 // registers per lane (head dims up to 192/128): 8 waves over 256 query rows,
 // each K/V tile read from L2 then serving twice the rows of a 4-wave
 // workgroup (measured faster than two independent 4-wave workgroups per CU).
-// Head dims 256 and 512: 4 waves with 512 registers.
+// Head dims 256 and 512: 4 waves with 512 registers (at 512 a wave holds
+// the whole 512-wide output of its 32 rows in the accumulator registers).
 template <int DSUM>
 constexpr int fwd_waves() { return DSUM <= 320 ? 8 : 4; }
 
@@ -114,6 +115,7 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
+  if constexpr (NW == 4 && DVC > 256) pin_acc(oacc);
   float m_run = -kInf, l_run = 0.f;
   const int kr = perm32(lq);
 
@@ -125,7 +127,21 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
   // tile load the last tile again: the same loads on every path.)
   TileStage<BN, DQK, TIn, NT, false> kst;
   TileStage<BN, DVC, TIn, NT, false> vst;
-  if (t0 < ntiles) {
+  // Where a wave holds a 512-wide output (256 accumulator registers beside
+  // a 128-register Q operand), the K/V tiles go straight from global memory
+  // into LDS, with no staging registers: tile t+1 is copied while tile t is
+  // computed, and the barrier at the top of each step waits for it.
+  constexpr bool DMA = sizeof(TIn) == 2 && DVC > 256;
+  auto dma_kv = [&](int t, int b) {
+    if constexpr (DMA) {
+      dma_tile<BN, DQK, KP, NT, false>(Kb, a.k_stride[1], t * BN, s.klen, Ksb + b * BN * KP, wave,
+                                       lane);
+      dma_tile<BN, DVC, VP, NT, false>(Vb, a.v_stride[1], t * BN, s.klen, Vsb + b * BN * VP, wave,
+                                       lane);
+    }
+  };
+  if (DMA && t0 < ntiles) dma_kv(t0, t0 & 1);
+  if (!DMA && t0 < ntiles) {
     kst.load(Kb, a.k_stride[1], t0 * BN, s.klen, tid);
     vst.load(Vb, a.v_stride[1], t0 * BN, s.klen, tid);
     kst.store(Ksb + (t0 & 1) * BN * KP, KP, tid);
@@ -139,13 +155,21 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
     const int j0 = t * BN;
     const CT* Ks = Ksb + (t & 1) * BN * KP;
     const CT* Vs = Vsb + (t & 1) * BN * VP;
-    __syncthreads();
-    // the other buffer was last read in the previous step, before the barrier
-    kst.store(Ksb + ((t + 1) & 1) * BN * KP, KP, tid);
-    vst.store(Vsb + ((t + 1) & 1) * BN * VP, VP, tid);
-    const int jn = (t + 2 < ntiles ? t + 2 : ntiles - 1) * BN;
-    kst.load(Kb, a.k_stride[1], jn, s.klen, tid);
-    vst.load(Vb, a.v_stride[1], jn, s.klen, tid);
+    if constexpr (DMA) {
+      // this wave's copies of tile t have landed, and every wave is past
+      // step t-1, whose buffer takes tile t+1 now
+      dma_barrier();
+      if (t + 1 < ntiles) dma_kv(t + 1, (t + 1) & 1);
+      pin_acc(oacc);
+    } else {
+      __syncthreads();
+      // the other buffer was last read in the previous step, before the barrier
+      kst.store(Ksb + ((t + 1) & 1) * BN * KP, KP, tid);
+      vst.store(Vsb + ((t + 1) & 1) * BN * VP, VP, tid);
+      const int jn = (t + 2 < ntiles ? t + 2 : ntiles - 1) * BN;
+      kst.load(Kb, a.k_stride[1], jn, s.klen, tid);
+      vst.load(Vb, a.v_stride[1], jn, s.klen, tid);
+    }
     if (!wave_active || (a.causal && kp0 + j0 > whi + bd.wr) ||
         (bd.left && kp0 + j0 + BN - 1 < wlo - bd.wl))
       continue;
@@ -194,9 +218,24 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
       if (move) m_run = mx;
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db) {
+        if constexpr (NW == 4 && DVC > 256) {
+          // 256 accumulators in the accumulator registers and no vector
+          // registers to spare: scale them one register at a time (written
+          // as plain multiplies, the compiler spilled ~380 registers here)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+          for (int v = 0; v < 16; ++v) {
+            float tmp;
+            asm volatile(
+                "v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %2, %1\n\tv_accvgpr_write_b32 %0, %1"
+                : "+a"(oacc[db][v]), "=&v"(tmp)
+                : "v"(alpha));
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+        }
+      }
     }
     const float base = m_run == -kInf ? 0.f : m_run;
     float x[NKB][16];
@@ -304,7 +343,11 @@ __global__ __launch_bounds__(256) void meta_check_kernel(const AttnArgs a) {
 
 template <int DQK, int DV, typename TIn, typename TOut>
 static hipError_t fwd_variant(const AttnArgs& a, hipStream_t st) {
-  constexpr int DVC = DV > 256 ? 256 : DV;
+  // Head dim 512 with 2-byte inputs: one workgroup forms the whole 512-wide
+  // output (K/V copied straight into LDS), so the scores of a row tile are
+  // computed once.  fp32 inputs, which are rounded on the way through
+  // registers, keep two 256-wide column chunks (one workgroup each).
+  constexpr int DVC = (DV > 256 && sizeof(TIn) != 2) ? 256 : DV;
   constexpr int NCH = DV / DVC;
   const int qrows = a.thd ? a.max_q : (int)a.seqlen_q;
   constexpr int NT = 64 * fwd_waves<DQK + DVC>(), BM = NT / 2;
