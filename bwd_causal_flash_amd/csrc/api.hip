@@ -102,7 +102,7 @@ bool bwd_grids_ok(const cpa_problem* p) {
   if (g.qrows * hq * pow2_at_least(p->d_qk / 8) + 256 > kGridX) return false;  // post
   if (cdiv(qtiles, 64) * 64 > kGridX) return false;                            // tile table
   if (kblocks > kGridYZ || cdiv(qtiles, 4) > kGridYZ) return false;            // main, dq
-  if (hq * dq_chunks * 512 > kGridX || hkv * 512 * (big ? p->d_qk / 128 : 1) > kGridX)
+  if (hq * dq_chunks * 512 > kGridX || hkv * 512 * (big ? 2 : 1) > kGridX)
     return false;
   if (big && (cdiv(g.qrows, 128) > kGridYZ || hq * g.nseq > kGridYZ || kblocks * 512 > kGridX))
     return false;                                                              // sdp

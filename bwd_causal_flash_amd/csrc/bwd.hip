@@ -773,9 +773,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
 //        the dq kernel's chunk layout (K rows are read in perm32 order, so
 //        the accumulators already are that layout: lane = query row, 8
 //        consecutive keys per half);
-//   dkv  per (kv head, 128 keys, 128 columns): dV^T += dO^T P and
-//        dK^T += Q^T dS over the query tiles that see the keys, for every
-//        query head of the group, P and dS read back through LDS;
+//   dkv  per (kv head, 128 keys, dV or dK): dV^T += dO^T P or
+//        dK^T += Q^T dS over the whole head dim, from the query tiles that
+//        see the keys, for every query head of the group, P or dS read
+//        back (once) through LDS;
 //   dq   dQ += dS K as for the other head dims.
 // Tiles a key block does not see are neither written nor read (the same
 // block ranges as the dq kernel).
@@ -972,23 +973,35 @@ void bwd_sdp_kernel(const AttnArgs a) {
   }
 }
 
-// dK^T and dV^T of 128 keys x 128 columns from the stored P and dS tiles.
+// dK or dV of 128 keys over the whole head dim from the stored P or dS
+// tiles: blockIdx.x = 2 * kv head + which, which = 0 forms dV^T = dO^T P,
+// which = 1 forms dK^T = Q^T dS (times the softmax scale).  Splitting the
+// two products (rather than the head dim into column chunks) leaves each
+// P or dS tile read once: the accumulators of 128 keys x D columns (128 per
+// lane at D = 512) fill half of a CU's registers.  Wave (kh, cq) owns keys
+// kh*64 .. +63 and columns cq*D/4 .. +D/4 - 1.  Work items are 32-row halves
+// of the 64-row query tiles that see the key block, for every query head
+// of the group, walked from the last tile down: the workgroups of one kv
+// head and product (on one XCD when 2 * heads_kv is a multiple of 8) all
+// start at the same rows and keep moving through them together, so their
+// Q or dO rows are shared in that XCD's L2.
 template <int D, typename TIn, typename TOut>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void bwd_dkv_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(const AttnArgs a) {
   using CT = ct_t<TIn>;
   using CT8 = vec8<CT>;
-  constexpr int BN = 128, DT = 128, BM = 64, NT = 512;
-  constexpr int TP = tr_pitch(DT), SP = tr_pitch(BN);   // transpose-read-only tiles
-  __shared__ __attribute__((aligned(16))) CT Qs[BM * TP];
-  __shared__ __attribute__((aligned(16))) CT Os[BM * TP];
-  __shared__ __attribute__((aligned(16))) CT Pt[BM * SP];
-  __shared__ __attribute__((aligned(16))) CT St[BM * SP];
+  constexpr int BN = 128, BR = 32, NT = 512;
+  constexpr int NCW = D / 128, NKW = 2;          // 32-column and 32-key blocks per wave
+  constexpr int YP = tr_pitch(D), XP = tr_pitch(BN);   // transpose-read-only tiles
+  constexpr int YPR = D / 8;                     // 16-byte pieces per row
+  constexpr int NY = BR * YPR / NT;              // pieces of a row tile per thread
+  static_assert(NY * NT == BR * YPR && BR * BN / 8 == NT, "staging shape");
+  __shared__ __attribute__((aligned(16))) CT Ys[2][BR * YP];
+  __shared__ __attribute__((aligned(16))) CT Xs[2][BR * XP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
-  const int kg = wave & 3, dh = wave >> 2;   // keys kg*32.., columns dh*64..
-  constexpr int NDT = D / DT;
-  const int kvh = blockIdx.x / NDT, c0 = (blockIdx.x % NDT) * DT;
+  const int kh = wave >> 2, cq = wave & 3;
+  const int kvh = blockIdx.x >> 1, which = blockIdx.x & 1;
   const int kt = a.kt0 + blockIdx.y;
   const int z = blockIdx.z;
   const Seq s = load_seq(a, z);
@@ -996,98 +1009,143 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   if (j0 >= s.klen) return;
   const int kp0 = kpos0(a);
   const int nkb = (s.klen + BN - 1) / BN;
-  const int nqt = (s.qlen + BM - 1) / BM;
-  const int my_key = j0 + kg * 32 + lq;
-  const bool key_valid = my_key < s.klen;
+  const int nqt = (s.qlen + 63) / 64;
   const int64_t ubase = ds_ubase(a, s, z);
-  const CT* const ds = static_cast<const CT*>(a.ds);
-  const CT* const ps = static_cast<const CT*>(a.ps);
+  const CT* const xsrc = static_cast<const CT*>(which ? a.ds : a.ps);
+  const TIn* const ysrc = static_cast<const TIn*>(which ? a.q : a.dout);
+  const int64_t* const yst = which ? a.q_stride : a.do_stride;
+  const TIn* const ybase = ysrc + (a.thd ? s.q_row0 * yst[1] : (int64_t)z * yst[0]);
 
-  f32x16 acck[2], accv[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) { acck[j][v] = 0.f; accv[j][v] = 0.f; }
-
-  // Work items: (query head of the group, query tile that sees the block).
-  auto seek = [&](int& hg, int& ut) {
-    while (hg < a.group) {
-      while (ut < nqt && !tile_sees_block(a, s, ut, kt, nkb, kp0)) ++ut;
-      if (ut < nqt) return;
-      ++hg;
-      ut = 0;
-    }
+  // Item = (query tile ut, half qb2, head hg of the group); ut < 0 ends.
+  struct Item {
+    int ut, qb2, hg;
   };
-  TileStage<BM, DT, TIn, NT> qst, ost;
-  CT8 pst[2], sst[2];   // this thread's 16-byte pieces of the P and dS tiles
-  auto fetch = [&](int hg, int ut) {
-    const int h = kvh * a.group + hg;
-    const TIn* Q = static_cast<const TIn*>(a.q) +
-                   (a.thd ? s.q_row0 * a.q_stride[1] : (int64_t)z * a.q_stride[0]) +
-                   (int64_t)h * a.q_stride[2] + c0;
-    const TIn* dO = static_cast<const TIn*>(a.dout) +
-                    (a.thd ? s.q_row0 * a.do_stride[1] : (int64_t)z * a.do_stride[0]) +
-                    (int64_t)h * a.do_stride[2] + c0;
-    qst.load(Q, a.q_stride[1], ut * BM, s.qlen, tid);
-    ost.load(dO, a.do_stride[1], ut * BM, s.qlen, tid);
-    const int64_t tile = ((int64_t)h * a.ds_nu + ubase + ut) * a.ds_nb + (kt - a.kt0);
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int64_t e = tile * kDsTileElems + (int64_t)(tid + NT * r) * 8;
-      pst[r] = __builtin_nontemporal_load(reinterpret_cast<const CT8*>(ps + e));
-      sst[r] = __builtin_nontemporal_load(reinterpret_cast<const CT8*>(ds + e));
-    }
+  auto seek_down = [&](int u) {
+    while (u >= 0 && !tile_sees_block(a, s, u, kt, nkb, kp0)) --u;
+    return u;
   };
-  // Piece n (= tid + 512 r) of a tile is lane n%64 of chunk n/64 = (qb2, t):
-  // rows 32*qb2 + lane%32, keys 16*t + 8*(lane/32) .. +7.
-  auto store_pieces = [&]() {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int n = tid + NT * r, ch = n >> 6, ln = n & 63;
-      const int row = 32 * (ch >> 3) + (ln & 31), col = 16 * (ch & 7) + 8 * (ln >> 5);
-      *reinterpret_cast<CT8*>(&Pt[row * SP + col]) = pst[r];
-      *reinterpret_cast<CT8*>(&St[row * SP + col]) = sst[r];
-    }
+  auto first_item = [&]() {
+    Item it{seek_down(nqt - 1), 1, 0};
+    if (it.ut >= 0 && it.ut * 64 + 32 >= s.qlen) it.qb2 = 0;   // empty top half
+    return it;
+  };
+  auto next_item = [&](Item it) {
+    if (it.ut < 0) return it;
+    if (++it.hg < a.group) return it;
+    it.hg = 0;
+    if (--it.qb2 >= 0) return it;
+    it.qb2 = 1;   // tiles below the last one are full
+    it.ut = seek_down(it.ut - 1);
+    return it;
   };
 
-  int hg = 0, ut = 0;
-  seek(hg, ut);
-  if (hg < a.group) fetch(hg, ut);
-  while (hg < a.group) {
-    __syncthreads();
-    qst.store(Qs, TP, tid);
-    ost.store(Os, TP, tid);
-    store_pieces();
-    int nhg = hg, nut = ut + 1;
-    seek(nhg, nut);
-    if (nhg < a.group) fetch(nhg, nut);
-    __syncthreads();
-    // dV^T += dO^T P, dK^T += Q^T dS over the tile's 64 rows
-    __builtin_amdgcn_s_setprio(1);   // as in the score kernel
+  // Staging through registers.  Row tile: piece p = tid + NT*i is row
+  // p / YPR, columns (p % YPR)*8 .. +7, so a wave reads whole rows.  P/dS
+  // half tile: the 8 KB half is contiguous; piece tid is lane tid%64 of
+  // 16-key chunk tid/64: row tid%32, keys 16*(tid/64) + 8*((tid/32)&1).
+  auto load_y = [&](const Item& it, CT8 (&r)[NY]) {
+    const int h = kvh * a.group + it.hg;
+    const TIn* yb = ybase + (int64_t)h * yst[2];
+    const int r0 = it.ut * 64 + it.qb2 * 32;
 #pragma unroll
-    for (int ks = 0; ks < BM / 16; ++ks) {
+    for (int i = 0; i < NY; ++i) {
+      const int p = tid + NT * i;
+      const int row = min(r0 + p / YPR, s.qlen - 1);   // rows past the end: P, dS are zero
+      r[i] = Elem<TIn>::load8(yb + (int64_t)row * yst[1] + (p % YPR) * 8);
+    }
+  };
+  auto store_y = [&](int b, const CT8 (&r)[NY]) {
+#pragma unroll
+    for (int i = 0; i < NY; ++i) {
+      const int p = tid + NT * i;
+      *reinterpret_cast<CT8*>(&Ys[b][(p / YPR) * YP + (p % YPR) * 8]) = r[i];
+    }
+  };
+  auto load_x = [&](const Item& it) {
+    const int h = kvh * a.group + it.hg;
+    const int64_t tile = ((int64_t)h * a.ds_nu + ubase + it.ut) * a.ds_nb + (kt - a.kt0);
+    return __builtin_nontemporal_load(reinterpret_cast<const CT8*>(
+        xsrc + tile * kDsTileElems + it.qb2 * (kDsTileElems / 2) + tid * 8));
+  };
+  const int xoff = (lane & 31) * XP + 16 * (tid >> 6) + 8 * ((tid >> 5) & 1);
+  auto store_x = [&](int b, const CT8& r) { *reinterpret_cast<CT8*>(&Xs[b][xoff]) = r; };
+
+  f32x16 acc[NKW][NCW];
+#pragma unroll
+  for (int x = 0; x < NKW; ++x)
+#pragma unroll
+    for (int c = 0; c < NCW; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[x][c][v] = 0.f;
+
+  auto compute = [&](int b) {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ks = 0; ks < BR / 16; ++ks) {
       const int k0 = ks * 16 + 8 * (grp >> 1);
-      const CT8 pb = lds_tr8(Pt, SP, k0, kg * 32 + 16 * (grp & 1), gl);
-      const CT8 sb = lds_tr8(St, SP, k0, kg * 32 + 16 * (grp & 1), gl);
+      CT8 xb[NKW], ya[NCW];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int m0 = dh * 64 + j * 32 + 16 * (grp & 1);
-        accv[j] = mfma32(lds_tr8(Os, TP, k0, m0, gl), pb, accv[j]);
-        acck[j] = mfma32(lds_tr8(Qs, TP, k0, m0, gl), sb, acck[j]);
-      }
+      for (int x = 0; x < NKW; ++x) xb[x] = lds_tr8(Xs[b], XP, k0, kh * 64 + x * 32 + 16 * (grp & 1), gl);
+#pragma unroll
+      for (int c = 0; c < NCW; ++c)
+        ya[c] = lds_tr8(Ys[b], YP, k0, cq * (D / 4) + c * 32 + 16 * (grp & 1), gl);
+#pragma unroll
+      for (int x = 0; x < NKW; ++x)
+#pragma unroll
+        for (int c = 0; c < NCW; ++c) acc[x][c] = mfma32(ya[c], xb[x], acc[x][c]);
     }
     __builtin_amdgcn_s_setprio(0);
-    hg = nhg;
-    ut = nut;
-  }
-  if (!key_valid) return;
-  auto key_row = [&](void* outp, const int64_t* st) -> TOut* {
-    return static_cast<TOut*>(outp) +
-           (a.thd ? (s.k_row0 + my_key) * st[1] : (int64_t)z * st[0] + (int64_t)my_key * st[1]) +
-           (int64_t)kvh * st[2] + c0 + dh * 64;
   };
-  store_key_acc(acck, key_row(a.dk, a.dk_stride), hh, a.scale);
-  store_key_acc(accv, key_row(a.dv, a.dv_stride), hh, 1.f);
+
+  // Pipeline: item n computes from buffer n & 1 while item n+1's registers
+  // go to the other buffer (read in step n-1, before this step's barrier),
+  // item n+2's rows and item n+3's P/dS piece are fetched.  P/dS pieces
+  // come from HBM once, so they are fetched further ahead, in three
+  // register sets used in turn.  Fetches for items past the end repeat
+  // the current item (same loads on every path; never stored or read).
+  Item c = first_item();
+  if (c.ut >= 0) {
+    Item n1 = next_item(c), n2 = next_item(n1);
+    CT8 yr[NY], xr0, xr1, xr2;
+    load_y(c, yr);
+    xr0 = load_x(c);
+    store_y(0, yr);
+    store_x(0, xr0);
+    load_y(n1.ut >= 0 ? n1 : c, yr);
+    xr1 = load_x(n1.ut >= 0 ? n1 : c);
+    xr2 = load_x(n2.ut >= 0 ? n2 : c);
+    int b = 0;
+    // Item i's piece sits in set i % 3: step n stores set (n+1) % 3 and
+    // refills set n % 3 (stored in the step before) with item n+3's.
+    auto step = [&](const CT8& xs, CT8& xl) {
+      __syncthreads();
+      store_y(b ^ 1, yr);
+      store_x(b ^ 1, xs);
+      const Item n3 = next_item(n2);
+      load_y(n2.ut >= 0 ? n2 : c, yr);
+      xl = load_x(n3.ut >= 0 ? n3 : c);
+      compute(b);
+      b ^= 1;
+      c = n1;
+      n1 = n2;
+      n2 = n3;
+      return c.ut >= 0;
+    };
+    while (step(xr1, xr0) && step(xr2, xr1) && step(xr0, xr2)) {
+    }
+  }
+
+  const int64_t* kst = which ? a.dk_stride : a.dv_stride;
+  TOut* const out = static_cast<TOut*>(which ? a.dk : a.dv);
+  const float mul = which ? a.scale : 1.f;
+#pragma unroll
+  for (int x = 0; x < NKW; ++x) {
+    const int key = j0 + kh * 64 + x * 32 + lq;
+    if (key >= s.klen) continue;
+    TOut* row = out + (a.thd ? (s.k_row0 + key) * kst[1] : (int64_t)z * kst[0] + (int64_t)key * kst[1]) +
+                (int64_t)kvh * kst[2] + cq * (D / 4);
+    store_key_acc(acc[x], row, hh, mul);
+  }
 }
 
 // ---------------------------------------------------------------- launch
@@ -1135,7 +1193,7 @@ static hipError_t bwd_variant(const AttnArgs& a, int step, hipStream_t st) {
         else
           hipLaunchKernelGGL((bwd_sdp_kernel<DQK, TIn, false>), g1, dim3(512), 0, st, a);
       }
-      dim3 g2(a.heads_kv * (DQK / 128), a.ds_nb, a.nseq);
+      dim3 g2(a.heads_kv * 2, a.ds_nb, a.nseq);
       hipLaunchKernelGGL((bwd_dkv_kernel<DQK, TIn, TOut>), g2, dim3(512), 0, st, a);
     }
   }
