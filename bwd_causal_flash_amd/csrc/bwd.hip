@@ -645,7 +645,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   const int kvh = h / a.group;
   const int z = blockIdx.z;
   const Seq s = load_seq(a, z);
-  const int ut0 = 4 * (int)blockIdx.y;
+  // Heaviest tiles first (the last query tiles see the most key blocks):
+  // workgroups dispatched together then walk the K blocks from the first
+  // one at the same pace and share them in L2.
+  const int ut0 = 4 * (int)(gridDim.y - 1 - blockIdx.y);
   const int ut = ut0 + (wave >> 1);
   const int qb2 = wave & 1;
   const int nkb = (s.klen + BN - 1) / BN;
@@ -680,9 +683,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   const unsigned loff = (unsigned)(qb2 * 8 * 64 + lane) * 8u;
   auto load_frags = [&](int kt, CT8* f) {
     const CT* p = dst + (int64_t)(kt - a.kt0) * kDsTileElems;
+    // With one column chunk the tiles are streamed once: non-temporal, so
+    // K keeps the L2.  With two (head dim 512) the other chunk's workgroup
+    // (blockIdx.x + heads_q: the same XCD when 8 | heads_q, dispatched
+    // alongside) reads the same tiles right after: plain loads leave them
+    // in L2 for it.
 #pragma unroll
-    for (int t = 0; t < 8; ++t)   // streamed once: non-temporal, K keeps L2
-      f[t] = __builtin_nontemporal_load(reinterpret_cast<const CT8*>(p + (loff + 512u * t)));
+    for (int t = 0; t < 8; ++t) {
+      const CT8* q = reinterpret_cast<const CT8*>(p + (loff + 512u * t));
+      f[t] = DC == DQK ? __builtin_nontemporal_load(q) : *q;
+    }
   };
 
   f32x16 acc[NDK];
@@ -814,8 +824,28 @@ void bwd_sdp_kernel(const AttnArgs a) {
   const int h = blockIdx.z % a.heads_q, z = blockIdx.z / a.heads_q;
   const int kvh = h / a.group;
   const Seq s = load_seq(a, z);
-  const int i0 = blockIdx.y * BQ;
-  const int kb0 = a.kt0 + NX * (int)blockIdx.x;   // first 128-key block
+  // Workgroups are dealt to the 8 XCDs in turn (XCD = linear id % 8), and
+  // each XCD has its own L2.  With 8 | gridDim.x the (key block, query
+  // tile) plane of a head is re-dealt so that XCD c takes the key blocks
+  // c, c+8, ... and walks them in 8 x 8 squares (8 of its key blocks x 8
+  // query tiles, key blocks fastest): the 64 workgroups it runs at a time
+  // then share 2 MB of K/V and 2 MB of Q/dO in its L2, where the launch
+  // order kept 16 key blocks (the whole L2) and re-fetched them per query
+  // tile.  A bijection of the plane: partial squares at the edges.
+  int bx = blockIdx.x, by = blockIdx.y;
+  if ((gridDim.x & 7) == 0) {
+    const int nj = gridDim.x >> 3, gy = gridDim.y;
+    const int pl = blockIdx.x + gridDim.x * blockIdx.y;
+    const int c = pl & 7, i = pl >> 3;
+    const int sy = i / (nj * 8), rem = i - sy * nj * 8;
+    const int ty = min(8, gy - sy * 8);
+    const int sj = rem / (8 * ty), rr = rem - sj * 8 * ty;
+    const int tj = min(8, nj - sj * 8);
+    by = sy * 8 + rr / tj;
+    bx = 8 * (sj * 8 + rr % tj) + c;
+  }
+  const int i0 = by * BQ;
+  const int kb0 = a.kt0 + NX * bx;   // first 128-key block
   const int j0 = kb0 * 128;
   if (i0 >= s.qlen || j0 >= s.klen) return;
   const int kp0 = kpos0(a);
