@@ -255,8 +255,13 @@ __device__ __forceinline__ void pin_acc(f32x16 (&acc)[N]) {
 // Workgroup barrier after which the LDS writes of this wave's direct
 // global-to-LDS copies are complete as well: those copies count as vector
 // memory operations (vmcnt), which the compiler does not track for LDS.
+// (Written with the builtins, so the compiler's own wait bookkeeping sees
+// the wait and knows those copies are done afterwards.)  s_waitcnt's
+// immediate on gfx9: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8;
+// 0x70 = vmcnt(0) lgkmcnt(0), expcnt left alone.
 __device__ __forceinline__ void dma_barrier() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x70);
+  __builtin_amdgcn_s_barrier();
 }
 
 // Direct global-to-LDS copy of a [ROWS x D] tile of 2-byte elements into an

@@ -50,8 +50,10 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
   constexpr int KS = DQK / 16;
   constexpr int NDB = DVC / 32;
   static_assert(NBUF * BN * (KP + VP) * (int)sizeof(CT) <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(16))) CT Ksb[NBUF * BN * KP];
-  __shared__ __attribute__((aligned(16))) CT Vsb[NBUF * BN * VP];
+  __shared__ __attribute__((aligned(16))) CT Kx0[BN * KP];
+  __shared__ __attribute__((aligned(16))) CT Kx1[BN * KP];
+  __shared__ __attribute__((aligned(16))) CT Vx0[BN * VP];
+  __shared__ __attribute__((aligned(16))) CT Vx1[BN * VP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
@@ -134,45 +136,29 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
   constexpr bool DMA = sizeof(TIn) == 2 && DVC > 256;
   auto dma_kv = [&](int t, int b) {
     if constexpr (DMA) {
-      dma_tile<BN, DQK, KP, NT, false>(Kb, a.k_stride[1], t * BN, s.klen, Ksb + b * BN * KP, wave,
+      dma_tile<BN, DQK, KP, NT, false>(Kb, a.k_stride[1], t * BN, s.klen, b ? Kx1 : Kx0, wave,
                                        lane);
-      dma_tile<BN, DVC, VP, NT, false>(Vb, a.v_stride[1], t * BN, s.klen, Vsb + b * BN * VP, wave,
+      dma_tile<BN, DVC, VP, NT, false>(Vb, a.v_stride[1], t * BN, s.klen, b ? Vx1 : Vx0, wave,
                                        lane);
     }
   };
-  if (DMA && t0 < ntiles) dma_kv(t0, t0 & 1);
+  if (DMA && t0 < ntiles) dma_kv(t0, 0);
   if (!DMA && t0 < ntiles) {
     kst.load(Kb, a.k_stride[1], t0 * BN, s.klen, tid);
     vst.load(Vb, a.v_stride[1], t0 * BN, s.klen, tid);
-    kst.store(Ksb + (t0 & 1) * BN * KP, KP, tid);
-    vst.store(Vsb + (t0 & 1) * BN * VP, VP, tid);
+    kst.store((t0 & 1) ? Kx1 : Kx0, KP, tid);
+    vst.store((t0 & 1) ? Vx1 : Vx0, VP, tid);
     const int jn = (t0 + 1 < ntiles ? t0 + 1 : t0) * BN;
     kst.load(Kb, a.k_stride[1], jn, s.klen, tid);
     vst.load(Vb, a.v_stride[1], jn, s.klen, tid);
   }
 
-  for (int t = t0; t < ntiles; ++t) {
+  // One step of the online softmax over K/V tile t, read from Ks, Vs.
+  auto tile_step = [&](int t, const CT* Ks, const CT* Vs) {
     const int j0 = t * BN;
-    const CT* Ks = Ksb + (t & 1) * BN * KP;
-    const CT* Vs = Vsb + (t & 1) * BN * VP;
-    if constexpr (DMA) {
-      // this wave's copies of tile t have landed, and every wave is past
-      // step t-1, whose buffer takes tile t+1 now
-      dma_barrier();
-      if (t + 1 < ntiles) dma_kv(t + 1, (t + 1) & 1);
-      pin_acc(oacc);
-    } else {
-      __syncthreads();
-      // the other buffer was last read in the previous step, before the barrier
-      kst.store(Ksb + ((t + 1) & 1) * BN * KP, KP, tid);
-      vst.store(Vsb + ((t + 1) & 1) * BN * VP, VP, tid);
-      const int jn = (t + 2 < ntiles ? t + 2 : ntiles - 1) * BN;
-      kst.load(Kb, a.k_stride[1], jn, s.klen, tid);
-      vst.load(Vb, a.v_stride[1], jn, s.klen, tid);
-    }
     if (!wave_active || (a.causal && kp0 + j0 > whi + bd.wr) ||
         (bd.left && kp0 + j0 + BN - 1 < wlo - bd.wl))
-      continue;
+      return;
 
     f32x16 sacc[NKB];
 #pragma unroll
@@ -183,11 +169,30 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
     // wave, when in its softmax, then fills the cycles the products leave
     // free instead of delaying them.
     __builtin_amdgcn_s_setprio(1);
+    if constexpr (NW == 4 && DVC > 256) {
+      // One wave per SIMD and one 32-key block: a single chain of KS
+      // products.  Its K operands are read RA steps ahead in a ring (the
+      // compiler, short of registers, otherwise waits on each read right
+      // before its product).
+      static_assert(NKB == 1, "one key block");
+      constexpr int RA = 6;
+      CT8 kf[RA];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+      for (int i = 0; i < RA; ++i) kf[i] = lds_row8(Ks, KP, kr, i * 16 + hh * 8);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        sacc[kb] = mfma32(lds_row8(Ks, KP, kb * 32 + kr, ks * 16 + hh * 8), qreg[ks], sacc[kb]);
+      for (int ks = 0; ks < KS; ++ks) {
+        sacc[0] = mfma32(kf[ks % RA], qreg[ks], sacc[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + RA < KS) kf[ks % RA] = lds_row8(Ks, KP, kr, (ks + RA) * 16 + hh * 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          sacc[kb] = mfma32(lds_row8(Ks, KP, kb * 32 + kr, ks * 16 + hh * 8), qreg[ks], sacc[kb]);
+    }
     __builtin_amdgcn_s_setprio(0);
 
     const bool need_mask = (j0 + BN > s.klen) || (a.causal && kp0 + j0 + BN - 1 > wlo + bd.wr) ||
@@ -251,17 +256,77 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
     l_run += rs;
 
     __builtin_amdgcn_s_setprio(1);
+    if constexpr (NW == 4 && DVC > 256) {
+      // As for S: the V operands of the BN/16 x NDB products are read RB
+      // products ahead in a ring.
+      constexpr int NPV = (BN / 16) * NDB, RB = 4;
+      CT8 pb[BN / 16];
 #pragma unroll
-    for (int st = 0; st < BN / 16; ++st) {
-      CT8 pb;
+      for (int st = 0; st < BN / 16; ++st)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (CT)x[st >> 1][8 * (st & 1) + e];
+        for (int e = 0; e < 8; ++e) pb[st][e] = (CT)x[st >> 1][8 * (st & 1) + e];
+      auto vread = [&](int i) {
+        const int st = i / NDB, db = i % NDB;
+        return lds_tr8(Vs, VP, 16 * st + 8 * (grp >> 1), db * 32 + 16 * (grp & 1), gl);
+      };
+      CT8 vf[RB];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        oacc[db] = mfma32(lds_tr8(Vs, VP, 16 * st + 8 * (grp >> 1), db * 32 + 16 * (grp & 1), gl),
-                          pb, oacc[db]);
+      for (int i = 0; i < RB; ++i) vf[i] = vread(i);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        oacc[i % NDB] = mfma32(vf[i % RB], pb[i / NDB], oacc[i % NDB]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + RB < NPV) vf[i % RB] = vread(i + RB);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < BN / 16; ++st) {
+        CT8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (CT)x[st >> 1][8 * (st & 1) + e];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          oacc[db] = mfma32(lds_tr8(Vs, VP, 16 * st + 8 * (grp >> 1), db * 32 + 16 * (grp & 1), gl),
+                            pb, oacc[db]);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
+  };
+
+  if constexpr (DMA) {
+    // The two buffers are distinct arrays, used in a fixed order (step t0
+    // + 2i reads buffer 0, t0 + 2i + 1 buffer 1), so the compiler can tell
+    // the LDS reads of one buffer from the copies into the other and does
+    // not wait for those copies before the reads (with one array indexed by
+    // parity it waits for every copy in flight, and nothing overlaps).
+    for (int t = t0; t < ntiles; t += 2) {
+      // this wave's copies of tile t have landed, and every wave is past
+      // step t-1, whose buffer takes tile t+1 now
+      dma_barrier();
+      if (t + 1 < ntiles) dma_kv(t + 1, 1);
+      asm volatile("" ::: "memory");   // the copies stay ahead of this step's LDS reads
+      pin_acc(oacc);
+      tile_step(t, Kx0, Vx0);
+      if (t + 1 < ntiles) {
+        dma_barrier();
+        if (t + 2 < ntiles) dma_kv(t + 2, 0);
+        asm volatile("" ::: "memory");
+        pin_acc(oacc);
+        tile_step(t + 1, Kx1, Vx1);
+      }
+    }
+  } else {
+    for (int t = t0; t < ntiles; ++t) {
+      __syncthreads();
+      // the other buffer was last read in the previous step, before the barrier
+      kst.store((t & 1) ? Kx0 : Kx1, KP, tid);
+      vst.store((t & 1) ? Vx0 : Vx1, VP, tid);
+      const int jn = (t + 2 < ntiles ? t + 2 : ntiles - 1) * BN;
+      kst.load(Kb, a.k_stride[1], jn, s.klen, tid);
+      vst.load(Vb, a.v_stride[1], jn, s.klen, tid);
+      tile_step(t, (t & 1) ? Kx1 : Kx0, (t & 1) ? Vx1 : Vx0);
+    }
   }
 
   if (!qvalid) return;
