@@ -810,9 +810,14 @@ void bwd_sdp_kernel(const AttnArgs a) {
   using CT8 = vec8<CT>;
   constexpr int BQ = 128, BK = kSdpKeys, DC = 32, NC = D / DC;
   constexpr int NX = BK / 128;   // 32-key sub-blocks per wave (and 128-key blocks per workgroup)
-  // Row pitch 80 bytes = 5 x 16: the 16-byte row reads of 16 consecutive
-  // rows (the only reads of these tiles) fall on 16 distinct bank groups.
-  constexpr int LP = DC + 8;
+  // Rows of 64 bytes, unpadded, with the four 16-byte pieces of row r
+  // stored in the order piece ^ ((r / 4) % 4): the 16-byte reads of one
+  // piece from 16 consecutive rows (the operand reads) and the stores of 4
+  // whole rows by 16 lanes both fall on 16 distinct bank groups of 256 bytes
+  // (an 80-byte pitch keeps the reads apart but not the stores).
+  constexpr int LP = DC;
+  static_assert(DC == 32, "four 16-byte pieces per row");
+  auto sw = [](int r, int piece) { return r * LP + 8 * (piece ^ ((r >> 2) & 3)); };
   __shared__ __attribute__((aligned(16))) CT Qs[2][BQ * LP];
   __shared__ __attribute__((aligned(16))) CT Os[2][BQ * LP];
   __shared__ __attribute__((aligned(16))) CT Ks[2][BK * LP];
@@ -879,33 +884,32 @@ void bwd_sdp_kernel(const AttnArgs a) {
                  (a.thd ? s.k_row0 * a.v_stride[1] : (int64_t)z * a.v_stride[0]) +
                  (int64_t)kvh * a.v_stride[2];
 
-  // Staging of one 32-column chunk: 128 Q and dO rows, 256 K and V rows,
-  // 4 x 16 bytes per row; thread t owns row t/4 (+128) and chunk t%4.
-  const int sr = tid >> 2, sc = (tid & 3) * 8;
+  // Staging of one 32-column chunk: 128 Q and dO rows, 128*NX K and V
+  // rows, 4 x 16 bytes per row; thread t owns row t/4 (+128) and piece t%4.
+  // Rows past the ends repeat the last row, on one branch-free path: their
+  // products only reach P entries that are zero (LSE = -inf rows, masked
+  // keys), so their values never matter.
+  const int sr = tid >> 2, sp = tid & 3, sc = sp * 8;
   CT8 stq, sto, stk[NX], stv[NX];
   auto load_chunk = [&](int c) {
     const int col = c * DC + sc;
-    const int qi = i0 + sr;
-    const bool qok = qi < s.qlen;
-    const int qr = qok ? qi : 0;
-    stq = qok ? Elem<TIn>::load8(Q + (int64_t)qr * a.q_stride[1] + col) : zero8<CT>();
-    sto = qok ? Elem<TIn>::load8(dO + (int64_t)qr * a.do_stride[1] + col) : zero8<CT>();
+    const int qr = min(i0 + sr, s.qlen - 1);
+    stq = Elem<TIn>::load8(Q + (int64_t)qr * a.q_stride[1] + col);
+    sto = Elem<TIn>::load8(dO + (int64_t)qr * a.do_stride[1] + col);
 #pragma unroll
     for (int r = 0; r < NX; ++r) {
-      const int kj = j0 + sr + 128 * r;
-      const bool kok = kj < s.klen;
-      const int kr = kok ? kj : 0;
-      stk[r] = kok ? Elem<TIn>::load8(K + (int64_t)kr * a.k_stride[1] + col) : zero8<CT>();
-      stv[r] = kok ? Elem<TIn>::load8(V + (int64_t)kr * a.v_stride[1] + col) : zero8<CT>();
+      const int kr = min(j0 + sr + 128 * r, s.klen - 1);
+      stk[r] = Elem<TIn>::load8(K + (int64_t)kr * a.k_stride[1] + col);
+      stv[r] = Elem<TIn>::load8(V + (int64_t)kr * a.v_stride[1] + col);
     }
   };
   auto store_chunk = [&](int b) {
-    *reinterpret_cast<CT8*>(&Qs[b][sr * LP + sc]) = stq;
-    *reinterpret_cast<CT8*>(&Os[b][sr * LP + sc]) = sto;
+    *reinterpret_cast<CT8*>(&Qs[b][sw(sr, sp)]) = stq;
+    *reinterpret_cast<CT8*>(&Os[b][sw(sr, sp)]) = sto;
 #pragma unroll
     for (int r = 0; r < NX; ++r) {
-      *reinterpret_cast<CT8*>(&Ks[b][(sr + 128 * r) * LP + sc]) = stk[r];
-      *reinterpret_cast<CT8*>(&Vs[b][(sr + 128 * r) * LP + sc]) = stv[r];
+      *reinterpret_cast<CT8*>(&Ks[b][sw(sr + 128 * r, sp)]) = stk[r];
+      *reinterpret_cast<CT8*>(&Vs[b][sw(sr + 128 * r, sp)]) = stv[r];
     }
   };
 
@@ -932,13 +936,15 @@ void bwd_sdp_kernel(const AttnArgs a) {
       CT8 ka[NX], va[NX], qb[2], ob[2];
 #pragma unroll
       for (int x = 0; x < NX; ++x) {
-        ka[x] = lds_row8(Ks[b], LP, kg * 32 * NX + x * 32 + pr, ks * 16 + hh * 8);
-        va[x] = lds_row8(Vs[b], LP, kg * 32 * NX + x * 32 + pr, ks * 16 + hh * 8);
+        const int kr = kg * 32 * NX + x * 32 + pr;
+        ka[x] = *reinterpret_cast<const CT8*>(&Ks[b][sw(kr, 2 * ks + hh)]);
+        va[x] = *reinterpret_cast<const CT8*>(&Vs[b][sw(kr, 2 * ks + hh)]);
       }
 #pragma unroll
       for (int y = 0; y < 2; ++y) {
-        qb[y] = lds_row8(Qs[b], LP, qh * 64 + y * 32 + lq, ks * 16 + hh * 8);
-        ob[y] = lds_row8(Os[b], LP, qh * 64 + y * 32 + lq, ks * 16 + hh * 8);
+        const int qr = qh * 64 + y * 32 + lq;
+        qb[y] = *reinterpret_cast<const CT8*>(&Qs[b][sw(qr, 2 * ks + hh)]);
+        ob[y] = *reinterpret_cast<const CT8*>(&Os[b][sw(qr, 2 * ks + hh)]);
       }
 #pragma unroll
       for (int x = 0; x < NX; ++x)
