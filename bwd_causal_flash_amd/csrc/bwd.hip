@@ -1077,8 +1077,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(const AttnArgs a) {
 
   // Staging through registers.  Row tile: piece p = tid + NT*i is row
   // p / YPR, columns (p % YPR)*8 .. +7, so a wave reads whole rows.  P/dS
-  // half tile: the 8 KB half is contiguous; piece tid is lane tid%64 of
-  // 16-key chunk tid/64: row tid%32, keys 16*(tid/64) + 8*((tid/32)&1).
+  // half tile (8 KB, contiguous; its 16-key chunk t holds row r, keys
+  // 16t + 8h .. +7 at element t*512 + (32h + r)*8): lane i of 16-lane group
+  // g of wave w takes chunk 2(w%4) + i%2, half h = (i/2)%2 and row
+  // 16(w/4) + 4g + i/4, so a wave reads four 256-byte runs and the 16 lanes
+  // of a group store to 16 distinct bank groups of the padded tile (lane
+  // order within a chunk would put rows 4 apart on one bank group).
   auto load_y = [&](const Item& it, CT8 (&r)[NY]) {
     const int h = kvh * a.group + it.hg;
     const TIn* yb = ybase + (int64_t)h * yst[2];
@@ -1097,13 +1101,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(const AttnArgs a) {
       *reinterpret_cast<CT8*>(&Ys[b][(p / YPR) * YP + (p % YPR) * 8]) = r[i];
     }
   };
+  const int x_t = 2 * (wave & 3) + (lane & 1), x_h = (lane >> 1) & 1;
+  const int x_r = 16 * (wave >> 2) + 4 * (lane >> 4) + ((lane >> 2) & 3);
+  const int xsrc_off = x_t * 512 + (32 * x_h + x_r) * 8;
+  const int xoff = x_r * XP + 16 * x_t + 8 * x_h;
   auto load_x = [&](const Item& it) {
     const int h = kvh * a.group + it.hg;
     const int64_t tile = ((int64_t)h * a.ds_nu + ubase + it.ut) * a.ds_nb + (kt - a.kt0);
     return __builtin_nontemporal_load(reinterpret_cast<const CT8*>(
-        xsrc + tile * kDsTileElems + it.qb2 * (kDsTileElems / 2) + tid * 8));
+        xsrc + tile * kDsTileElems + it.qb2 * (kDsTileElems / 2) + xsrc_off));
   };
-  const int xoff = (lane & 31) * XP + 16 * (tid >> 6) + 8 * ((tid >> 5) & 1);
   auto store_x = [&](int b, const CT8& r) { *reinterpret_cast<CT8*>(&Xs[b][xoff]) = r; };
 
   f32x16 acc[NKW][NCW];
