@@ -1060,8 +1060,50 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(const AttnArgs a) {
     while (u >= 0 && !tile_sees_block(a, s, u, kt, nkb, kp0)) --u;
     return u;
   };
+  // When query positions never decrease with the row (THD; BSHD segments
+  // in order), a tile's last visible key block (causal bound) and first one
+  // (left bound) never decrease with the tile either, so the tiles that see
+  // this block are one run [u_lo, u_hi], found once by bisection; the walk
+  // then needs no visibility test per tile (each test reads the segment
+  // table through the scalar cache, whose waits also drain the LDS queue).
+  // Otherwise each step down seeks the next seeing tile.  Both give the
+  // tiles for which tile_sees_block holds.
+  bool mono = true;
+  if (!a.thd)
+    for (int t = 1; t < a.nseg; ++t)
+      mono = mono && a.seg_pos[t] >= a.seg_pos[t - 1] + (a.seg_row[t] - 1 - a.seg_row[t - 1]);
+  auto last_block = [&](int u) {   // causal bound (-1: none), as dq_block_range
+    if (!a.causal) return nkb - 1;
+    int lo, hi;
+    qpos_range(a, s, u * 64, min(u * 64 + 64, s.qlen), lo, hi);
+    if (hi + a.win_r < kp0) return -1;
+    return min((hi + a.win_r - kp0) / 128, nkb - 1);
+  };
+  auto first_block = [&](int u) {   // left bound (nkb: none), as dq_block_range
+    if (!a.left) return 0;
+    int lo, hi;
+    qpos_range(a, s, u * 64, min(u * 64 + 64, s.qlen), lo, hi);
+    const int x = lo - a.win_l - kp0;
+    if (x > s.klen - 1) return nkb;
+    return x <= 0 ? 0 : x / 128;
+  };
+  int u_lo = 0, u_hi = -1;
+  if (mono) {
+    int l = 0, r = nqt;   // first u with last_block(u) >= kt
+    while (l < r) {
+      const int m = (l + r) >> 1;
+      if (last_block(m) >= kt) r = m; else l = m + 1;
+    }
+    u_lo = l;
+    l = 0, r = nqt;       // first u with first_block(u) > kt
+    while (l < r) {
+      const int m = (l + r) >> 1;
+      if (first_block(m) > kt) r = m; else l = m + 1;
+    }
+    u_hi = l - 1;
+  }
   auto first_item = [&]() {
-    Item it{seek_down(nqt - 1), 1, 0};
+    Item it{mono ? (u_lo <= u_hi ? u_hi : -1) : seek_down(nqt - 1), 1, 0};
     if (it.ut >= 0 && it.ut * 64 + 32 >= s.qlen) it.qb2 = 0;   // empty top half
     return it;
   };
@@ -1071,7 +1113,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(const AttnArgs a) {
     it.hg = 0;
     if (--it.qb2 >= 0) return it;
     it.qb2 = 1;   // tiles below the last one are full
-    it.ut = seek_down(it.ut - 1);
+    it.ut = mono ? (it.ut - 1 >= u_lo ? it.ut - 1 : -1) : seek_down(it.ut - 1);
     return it;
   };
 
