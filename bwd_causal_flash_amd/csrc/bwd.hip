@@ -318,7 +318,44 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   // Next (query head, tile) at or after (hg, ut) whose tile sees a key of
   // the block.  Every workgroup walks the tiles in the same order, so the
   // ones that run together on an XCD read each Q / dO tile while it is in L2.
+  // With query positions that never decrease with the row (THD; BSHD
+  // segments in order) the tile bounds never decrease either, so the tiles
+  // that see the block are one run [u_lo, u_hi], found once by bisection,
+  // and the walk needs no per-tile test (each reads the table through the
+  // scalar cache and waits for it while every wave of the CU waits too).
+  bool mono = true;
+  if (!a.thd)
+    for (int t = 1; t < a.nseg; ++t)
+      mono = mono && a.seg_pos[t] >= a.seg_pos[t - 1] + (a.seg_row[t] - 1 - a.seg_row[t - 1]);
+  int u_lo = 0, u_hi = nqt - 1;
+  if (mono) {
+    int l = 0, r = nqt;   // first tile reaching the block (causal bound)
+    while (l < r) {
+      const int m = (l + r) >> 1;
+      const int h0 = tpos[4 * m + 1], h1 = tpos[4 * m + 3];
+      if (!a.causal || (h0 > h1 ? h0 : h1) + bd.wr >= gkpos_lo) r = m; else l = m + 1;
+    }
+    u_lo = l;
+    l = 0, r = nqt;       // first tile past the block's left bound
+    while (l < r) {
+      const int m = (l + r) >> 1;
+      const int l0 = tpos[4 * m], l1 = tpos[4 * m + 2];
+      if (bd.left && (l0 < l1 ? l0 : l1) - bd.wl > gkpos_hi) r = m; else l = m + 1;
+    }
+    u_hi = l - 1;
+  }
   auto seek = [&](int& hg, int& ut) {
+    if (mono) {
+      if (u_lo > u_hi) {
+        hg = a.group;
+      } else if (ut < u_lo) {
+        ut = u_lo;
+      } else if (ut > u_hi) {
+        ++hg;
+        ut = u_lo;
+      }
+      return;
+    }
     while (hg < a.group) {
       if (a.causal || bd.left)
         while (ut < nqt && !tile_sees(ut)) ++ut;
