@@ -187,11 +187,22 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
+      // Products in (k-step, key block) order; the K operand of product i
+      // is read RA products ahead in a ring (the compiler's own schedule
+      // kept one read ahead: −0.5–1.5 % per step with four).
+      constexpr int NP = KS * NKB, RA = 4;
+      CT8 kf[RA];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int i = 0; i < RA; ++i)
+        kf[i] = lds_row8(Ks, KP, (i % NKB) * 32 + kr, (i / NKB) * 16 + hh * 8);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          sacc[kb] = mfma32(lds_row8(Ks, KP, kb * 32 + kr, ks * 16 + hh * 8), qreg[ks], sacc[kb]);
+      for (int i = 0; i < NP; ++i) {
+        sacc[i % NKB] = mfma32(kf[i % RA], qreg[i / NKB], sacc[i % NKB]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int n = i + RA;
+        if (n < NP) kf[i % RA] = lds_row8(Ks, KP, (n % NKB) * 32 + kr, (n / NKB) * 16 + hh * 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
 
@@ -256,10 +267,11 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
     l_run += rs;
 
     __builtin_amdgcn_s_setprio(1);
-    if constexpr (NW == 4 && DVC > 256) {
+    {
       // As for S: the V operands of the BN/16 x NDB products are read RB
-      // products ahead in a ring.
-      constexpr int NPV = (BN / 16) * NDB, RB = 4;
+      // products ahead in a ring (4 with one wave per SIMD, 2 where the
+      // SIMD's other wave covers part of the latency: −0.5–1 % per step).
+      constexpr int NPV = (BN / 16) * NDB, RB = (NW == 4 && DVC > 256) ? 4 : 2;
       CT8 pb[BN / 16];
 #pragma unroll
       for (int st = 0; st < BN / 16; ++st)
@@ -278,17 +290,6 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
         __builtin_amdgcn_sched_barrier(0);
         if (i + RB < NPV) vf[i % RB] = vread(i + RB);
         __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-#pragma unroll
-      for (int st = 0; st < BN / 16; ++st) {
-        CT8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (CT)x[st >> 1][8 * (st & 1) + e];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          oacc[db] = mfma32(lds_tr8(Vs, VP, 16 * st + 8 * (grp >> 1), db * 32 + 16 * (grp & 1), gl),
-                            pb, oacc[db]);
       }
     }
     __builtin_amdgcn_s_setprio(0);
