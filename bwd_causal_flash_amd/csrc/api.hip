@@ -256,8 +256,11 @@ bool keeps_p(const cpa_problem* p) { return p->d_qk + p->d_v > 320; }
 size_t ds_block_bytes(const cpa_problem* p) {
   return ds_part_bytes(p) * (keeps_p(p) ? 2 : 1);
 }
+// Query positions for the key-outer kernel: per 64-row tile the min and max
+// of each 32-row half (16 B), then per row (64 x 4 B per tile), so that the
+// kernel loads a tile's positions instead of searching the segments.
 size_t tile_pos_bytes(const cpa_problem* p) {
-  return align_up((size_t)ds_tile_rows(p) * 16);
+  return align_up((size_t)ds_tile_rows(p) * (16 + 64 * 4));
 }
 size_t bwd_base_bytes(const cpa_problem* p) {
   return kAlign + bwd_delta_bytes(p) + bwd_acc_bytes(p) + tile_pos_bytes(p);

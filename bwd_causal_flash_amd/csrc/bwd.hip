@@ -152,6 +152,11 @@ __device__ __forceinline__ int64_t ds_ubase(const AttnArgs& a, const Seq& s, int
 struct TilePos {
   int lo0, hi0, lo1, hi1;
 };
+// Per-row query positions, after the tile table (row i of the sequence whose
+// tiles start at tile row u0 sits at index 64 * u0 + i).
+__device__ __forceinline__ int* row_pos_table(const AttnArgs& a) {
+  return reinterpret_cast<int*>(static_cast<char*>(a.tile_pos) + a.ds_nu * 16);
+}
 
 __global__ __launch_bounds__(64) void bwd_tiles_kernel(const AttnArgs a) {
   const int z = blockIdx.z;
@@ -168,7 +173,14 @@ __global__ __launch_bounds__(64) void bwd_tiles_kernel(const AttnArgs a) {
     f[2 * hf] = lo;
     f[2 * hf + 1] = hi;
   }
-  reinterpret_cast<TilePos*>(a.tile_pos)[ds_ubase(a, s, z) + ut] = e;
+  const int64_t row = ds_ubase(a, s, z) + ut;
+  reinterpret_cast<TilePos*>(a.tile_pos)[row] = e;
+  // and every row's position (rows past the end extend the last segment)
+  int* rp = row_pos_table(a) + row * 64;
+#pragma unroll 4
+  for (int r = 0; r < 64; r += 4)
+    *reinterpret_cast<int4*>(rp + r) = make_int4(qpos(a, s, ut * 64 + r), qpos(a, s, ut * 64 + r + 1),
+                                                 qpos(a, s, ut * 64 + r + 2), qpos(a, s, ut * 64 + r + 3));
 }
 
 // Row pitch for bf16 tiles read only along rows (16-byte reads): P/8 odd.
@@ -372,6 +384,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   TileStage<BM, DV, TIn, NT, false> dost;
   float pre_l = 0.f, pre_d = 0.f;
   int pre_p = 0;
+  const int* const rowpos = row_pos_table(a) + 64 * ubase;   // this sequence's rows
   const int64_t qseq = a.thd ? s.q_row0 * a.q_stride[1] : (int64_t)z * a.q_stride[0];
   const int64_t oseq = a.thd ? s.q_row0 * a.do_stride[1] : (int64_t)z * a.do_stride[0];
   const int64_t lseq = a.thd ? s.q_row0 : (int64_t)z * a.lse_stride[0];
@@ -387,7 +400,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
       // raw values only: converting here would wait for the loads at once
       pre_l = ok ? a.lse[lseq + (int64_t)h * a.lse_stride[1] + i] : -kInf;
       pre_d = ok ? a.delta[dseq + (int64_t)h * a.delta_stride[1] + i] : 0.f;
-      pre_p = qpos(a, s, i);
+      pre_p = rowpos[i];
     }
   };
 

@@ -203,11 +203,11 @@ cpa_status attn_fwd_accum(const cpa_problem* p, const void* q, const void* k,
                           void* ws, size_t ws_bytes, cpa_stream_t stream);
 
 /* Bytes of workspace attn_bwd needs (host, pure) for its fastest schedule:
- * the error flag, D = rowsum(dO*O), an fp32 dQ accumulator, a small table
- * of query positions per 64-row tile and the dS tiles of the whole key
- * range (16 KiB per query head, 64-row query tile and 128-key block: about
- * 2 * heads_q * S_q * S_k bytes; twice that for head dims 256 and 512,
- * which also keep the P tiles).  Same problem -> same size. */
+ * the error flag, D = rowsum(dO*O), an fp32 dQ accumulator, small tables
+ * of query positions (per 64-row tile and per row) and the dS tiles of the
+ * whole key range (16 KiB per query head, 64-row query tile and 128-key
+ * block: about 2 * heads_q * S_q * S_k bytes; twice that for head dims 256
+ * and 512, which also keep the P tiles).  Same problem -> same size. */
 size_t attn_bwd_workspace_size(const cpa_problem* p);
 
 /* Smallest workspace attn_bwd accepts (host, pure): as above with the

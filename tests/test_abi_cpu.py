@@ -100,15 +100,16 @@ def test_argument_errors_are_rejected_before_launch():
     assert res["xchg_offsets"][1:] == [32768 + 512, 2 * (32768 + 512)]
     assert res["xchg_invalid_offset_is_zero"][1] == 0
     assert res["pack_size_valid"][1] % 256 == 0 and res["pack_size_valid"][1] > 0
-    # flag + D + fp32 dQ accumulator + query-tile position table (4 tiles x
-    # 16 B, padded to 256), then dS tiles: 4 heads x 4 query tiles x 16 KiB
-    # per 128-key block; the problem has 256 keys = 2 blocks.
-    base = 256 + 4 * 256 * 4 + 256 * 4 * 128 * 4 + 256
+    # flag + D + fp32 dQ accumulator + query position tables (4 tiles x
+    # (16 B + 64 rows x 4 B) = 1088 B, padded to 1280), then dS tiles: 4 heads
+    # x 4 query tiles x 16 KiB per 128-key block; the problem has 256 keys =
+    # 2 blocks.
+    base = 256 + 4 * 256 * 4 + 256 * 4 * 128 * 4 + 1280
     block = 4 * 4 * 64 * 128 * 2
     assert res["bwd_workspace_min_bytes"][1] == base + block
     assert res["bwd_workspace_bytes"][1] == base + 2 * block
     # head dim 512: a larger fp32 accumulator, and the P tiles kept beside
     # the dS tiles (twice the tile bytes per key block)
     full, least = res["bwd_workspace_d512"][1:]
-    base512 = 256 + 4 * 256 * 4 + 256 * 4 * 512 * 4 + 256
+    base512 = 256 + 4 * 256 * 4 + 256 * 4 * 512 * 4 + 1280
     assert least == base512 + 2 * block and full == base512 + 4 * block
