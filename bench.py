@@ -196,7 +196,9 @@ class SimpleStep:
         cpa = self.cpa
         cpa.attn_fwd(self.q, self.k, self.v, self.o, self.lse, scale=self.scale, varlen=self.varlen,
                      workspace=self.fwd_ws, stream=stream)
-        kw = dict(scale=self.scale, varlen=self.varlen, workspace=self.bwd_ws, stream=stream)
+        # full workspace, one main and one dq: the dq step writes dq itself
+        kw = dict(scale=self.scale, varlen=self.varlen, workspace=self.bwd_ws, stream=stream,
+                  flags=cpa.CPA_FLAG_DQ_DIRECT)
         args = (self.q, self.k, self.v, self.o, self.dout, self.lse, self.dq, self.dk, self.dv)
         cpa.attn_bwd(*args, step="attn_bwd_pre", **kw)
         if main_events:

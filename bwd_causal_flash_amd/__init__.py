@@ -26,8 +26,8 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 from . import _lib
-from ._lib import (CPA_BF16, CPA_FP16, CPA_FP32, CPA_FLAG_DETERMINISTIC, CpaError,  # noqa: F401
-                   MergeDesc, PackDesc, Problem, STATUS_CODE)
+from ._lib import (CPA_BF16, CPA_FP16, CPA_FP32, CPA_FLAG_DETERMINISTIC,  # noqa: F401
+                   CPA_FLAG_DQ_DIRECT, CpaError, MergeDesc, PackDesc, Problem, STATUS_CODE)
 
 __all__ = [
     "attn_fwd", "attn_bwd", "attn_bwd_static", "bwd_workspace_bytes", "attn_merge_lse", "pack_saved", "unpack_saved",

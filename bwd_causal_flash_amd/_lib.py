@@ -16,6 +16,7 @@ CPA_BF16, CPA_FP32, CPA_FP16 = 0, 1, 2
 CPA_LAYOUT_BSHD, CPA_LAYOUT_THD = 0, 1
 CPA_MAX_SEGMENTS = 8
 CPA_FLAG_DETERMINISTIC = 1
+CPA_FLAG_DQ_DIRECT = 2
 CPA_BWD_STATIC_WORKSPACE_BYTES = 256 << 20
 
 STATUS = {

@@ -405,7 +405,7 @@ cpa_status bwd_prepare(const cpa_problem* p, const void* q, const void* k, const
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return CPA_ERR_NULL;
   // The backward has no atomics, so the result is always deterministic and
   // CPA_FLAG_DETERMINISTIC asks for nothing more.
-  if (flags & ~(uint32_t)CPA_FLAG_DETERMINISTIC) return CPA_ERR_UNSUPPORTED;
+  if (flags & ~(uint32_t)(CPA_FLAG_DETERMINISTIC | CPA_FLAG_DQ_DIRECT)) return CPA_ERR_UNSUPPORTED;
   if (!strides_ok(p->o_stride, 3) || !strides_ok(p->do_stride, 3) ||
       !strides_ok(p->dq_stride, 3) || !strides_ok(p->dk_stride, 3) ||
       !strides_ok(p->dv_stride, 3))
@@ -479,6 +479,9 @@ cpa_status bwd_run(const cpa_problem* p, const void* q, const void* k, const voi
   }
   const int64_t nkb = ds_key_blocks(p);
   if (steps != 15 && (steps & 6) && a.ds_nb < nkb) return CPA_ERR_WORKSPACE;
+  // Single-pass dQ: one band holding every key block, and either the whole
+  // backward in this call or the caller's promise (the flag) for the steps.
+  a.dq_direct = (a.ds_nb >= nkb && (steps == 15 || (flags & CPA_FLAG_DQ_DIRECT))) ? 1 : 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   auto run = [&](int step) {
     return launch_bwd(a, p->d_qk, p->d_v, p->in_dtype, p->out_dtype, step, s) == hipSuccess;
@@ -497,7 +500,7 @@ cpa_status bwd_run(const cpa_problem* p, const void* q, const void* k, const voi
       if ((steps & 4) && !run(2)) return CPA_ERR_LAUNCH;
     }
   }
-  if ((steps & 8) && !run(3)) return CPA_ERR_LAUNCH;
+  if ((steps & 8) && !a.dq_direct && !run(3)) return CPA_ERR_LAUNCH;
   return CPA_OK;
 }
 }  // namespace

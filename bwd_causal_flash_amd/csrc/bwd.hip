@@ -68,6 +68,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a) {
                          (int64_t)h * a.delta_stride[1] + prow;
     a.delta[doff] = acc;
   }
+  if (a.dq_direct) return;   // the dq kernel writes dq itself
   float* accrow = a.dq_acc + (a.thd ? 0 : (int64_t)z * a.acc_stride[0]) +
                   prow * a.acc_stride[1] + (int64_t)h * a.acc_stride[2];
   for (int c = gl; c < DQK / 4; c += G)
@@ -679,7 +680,7 @@ __device__ __forceinline__ void dq_block_range(const AttnArgs& a, const Seq& s, 
 
 // DC: dQ columns per workgroup (the whole head dim up to 256; the 512 dim
 // runs two column chunks, each reading the same dS tiles).
-template <int DQK, int DC, typename TIn>
+template <int DQK, int DC, typename TIn, typename TOut>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   constexpr int BN = 128, NT = 512, NDK = DC / 32;
   using CT = ct_t<TIn>;   // matrix-core operand type
@@ -717,7 +718,36 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   }
   const int kt_begin = max(a.kt0, wg_first);
   const int kt_end = min(wg_last + 1, a.kt0 + a.ds_nb);
-  if (kt_begin >= kt_end) return;   // uniform over the workgroup
+
+  f32x16 acc[NDK];
+#pragma unroll
+  for (int d = 0; d < NDK; ++d)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[d][v] = 0.f;
+  // Single pass (this launch covers every key block and nothing else adds
+  // to dQ): the wave writes dq = scale * acc for its 32 rows, zeros where
+  // the rows see no key, with the conversion the post step would apply.
+  // Lane l holds column c0 + 32 db + l % 32 of rows 8 (v / 4) + 4 (l / 32)
+  // + v % 4 of the wave's 32.
+  const int rbase = ut * 64 + qb2 * 32;
+  auto write_direct = [&]() {
+    TOut* const o = static_cast<TOut*>(a.dq) +
+                    (a.thd ? s.q_row0 * a.dq_stride[1] : (int64_t)z * a.dq_stride[0]) +
+                    (int64_t)h * a.dq_stride[2] + c0 + lq;
+    const int64_t rs = a.dq_stride[1];
+    TOut* const p0 = o + (int64_t)(rbase + 4 * hh) * rs;
+    const bool full = rbase + 32 <= s.qlen;
+#pragma unroll
+    for (int db = 0; db < NDK; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (full || rbase + acc_row(v, hh) < s.qlen)
+          p0[(8 * (v >> 2) + (v & 3)) * rs + db * 32] = (TOut)(acc[db][v] * a.scale);
+  };
+  if (kt_begin >= kt_end) {   // uniform over the workgroup
+    if (a.dq_direct) write_direct();
+    return;
+  }
 
   const TIn* K = static_cast<const TIn*>(a.k);
   const int64_t kbase = (a.thd ? s.k_row0 * a.k_stride[1] : (int64_t)z * a.k_stride[0]) +
@@ -744,12 +774,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
       f[t] = DC == DQK ? __builtin_nontemporal_load(q) : *q;
     }
   };
-
-  f32x16 acc[NDK];
-#pragma unroll
-  for (int d = 0; d < NDK; ++d)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[d][v] = 0.f;
 
   // dS fragments AHEAD key blocks ahead, in AHEAD + 1 register sets used in
   // turn (no register copy between iterations, which would force a wait for
@@ -798,12 +822,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
       if (kt + 1 < kt_end) body(kt + 1, fb, fa);
     }
   }
+  if (a.dq_direct) {
+    write_direct();
+    return;
+  }
   if (max(my_first, kt_begin) > min(my_last, kt_end - 1)) return;   // nothing added
   // Accumulator update: all loads, then all stores (the rows are distinct).
   float* accbase = a.dq_acc + (a.thd ? s.q_row0 * a.acc_stride[1] : (int64_t)z * a.acc_stride[0]) +
                    (int64_t)h * a.acc_stride[2] + c0 + lq;
   const int64_t rs = a.acc_stride[1];
-  const int rbase = ut * 64 + qb2 * 32;
   float* p0 = accbase + (int64_t)(rbase + 4 * hh) * rs;
   const bool full = rbase + 32 <= s.qlen;
 #pragma unroll
@@ -1335,7 +1362,7 @@ static hipError_t bwd_variant(const AttnArgs& a, int step, hipStream_t st) {
   if (step == 2 && krows > 0 && qrows > 0) {
     const int qtiles = (qrows + 63) / 64;
     dim3 g(a.heads_q * (DQK / C::DQ_COLS), (qtiles + 3) / 4, a.nseq);
-    hipLaunchKernelGGL((bwd_dq_kernel<DQK, C::DQ_COLS, TIn>), g, dim3(512), 0, st, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<DQK, C::DQ_COLS, TIn, TOut>), g, dim3(512), 0, st, a);
   }
   if (step == 3 && qrows > 0) {
     constexpr int PB = 256 / pow2_at_least(DQK / 8);

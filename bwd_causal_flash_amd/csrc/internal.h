@@ -56,6 +56,7 @@ struct AttnArgs {
   int left;           // left bound on: key visible only if pos_k >= pos_q - win_l
   int win_l;          // >= 0
   int bottom_right;
+  int dq_direct;      // bwd: the dq kernel writes dq itself (one pass over every key block)
   int nseg;
   int seg_row[CPA_MAX_SEGMENTS];   // positions and rows fit in int32
   int seg_pos[CPA_MAX_SEGMENTS];

@@ -26,7 +26,8 @@ from typing import List, Sequence, Tuple
 
 import torch
 
-from . import attn_bwd, attn_fwd, attn_merge_lse, pack_saved, pack_saved_size, unpack_saved
+from . import (CPA_FLAG_DQ_DIRECT, attn_bwd, attn_fwd, attn_merge_lse, pack_saved,
+               pack_saved_size, unpack_saved)
 
 
 @dataclasses.dataclass
@@ -151,8 +152,10 @@ class RankStep:
         """One backward over all query rows and keys.  ``main_events`` =
         (start, end) HIP events recorded around the key-outer main kernel
         only."""
+        # one main and one dq over every key block with the full workspace:
+        # the dq step writes dq itself (no accumulator clear, no post pass)
         kw = dict(causal=True, scale=self.scale, q_segments=self.segments, k_pos_begin=0,
-                  workspace=self.bwd_ws, stream=stream)
+                  workspace=self.bwd_ws, stream=stream, flags=CPA_FLAG_DQ_DIRECT)
         args = (self.q, self.k, self.v, self.o, self.dout, self.lse, self.dq, self.dk, self.dv)
         attn_bwd(*args, step="attn_bwd_pre", **kw)
         if main_events:

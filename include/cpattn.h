@@ -106,7 +106,7 @@ typedef enum cpa_status {
 enum { CPA_BF16 = 0, CPA_FP32 = 1, CPA_FP16 = 2 };
 enum { CPA_LAYOUT_BSHD = 0, CPA_LAYOUT_THD = 1 };
 enum { CPA_MAX_SEGMENTS = 8 };
-enum { CPA_FLAG_DETERMINISTIC = 1 };
+enum { CPA_FLAG_DETERMINISTIC = 1, CPA_FLAG_DQ_DIRECT = 2 };
 
 /*
  * One attention problem.  Supported head dims (d_qk, d_v): (64, 64),
@@ -231,7 +231,11 @@ size_t attn_bwd_workspace_min(const cpa_problem* p);
  * band split are bitwise those of the full workspace; dQ adds the bands in
  * order, so its rounding depends on the split.  Outputs must not overlap
  * each other or the inputs; ws holds at least attn_bwd_workspace_min(p)
- * bytes (first int32 = THD metadata error flag, as for attn_fwd).
+ * bytes (first int32 = THD metadata error flag, as for attn_fwd).  When ws
+ * holds the whole key range (attn_bwd_workspace_size(p)), the dQ kernel is
+ * the only step adding to dQ, so it writes dq = softmax_scale * dS K itself
+ * (zeros for rows that see no key): the accumulator is neither cleared nor
+ * read, no post step runs, and the result is bitwise the same.
  */
 cpa_status attn_bwd(const cpa_problem* p, const void* q, const void* k,
                     const void* v, const void* o, const void* dout,
@@ -256,6 +260,11 @@ cpa_status attn_bwd(const cpa_problem* p, const void* q, const void* k,
  * accumulate dQ over the blocks of a ring while each main writes its own
  * block's dK, dV.  Called one by one, main and dq need the full
  * attn_bwd_workspace_size(p) (else CPA_ERR_WORKSPACE).
+ * CPA_FLAG_DQ_DIRECT, given to all four steps of one backward that runs
+ * main and dq exactly once, selects the single-pass dQ of attn_bwd above:
+ * pre leaves the accumulator alone, dq writes dq itself, post does
+ * nothing.  (Without it on every step, or with a second dq step in between,
+ * dq is undefined.)
  */
 cpa_status attn_bwd_pre(const cpa_problem* p, const void* q, const void* k,
                         const void* v, const void* o, const void* dout,

@@ -124,7 +124,8 @@ def main():
         p = good_problem(d_qk=d, d_v=d)
         case(f"bwd_deterministic_accepted_d{d}", "CPA_ERR_LAUNCH", bwd(p, flags=1))
     p = good_problem()
-    case("bwd_unknown_flag", "CPA_ERR_UNSUPPORTED", bwd(p, flags=2))
+    case("bwd_dq_direct_flag_accepted", "CPA_ERR_LAUNCH", bwd(p, flags=2))
+    case("bwd_unknown_flag", "CPA_ERR_UNSUPPORTED", bwd(p, flags=4))
     need = lib.attn_bwd_workspace_size(ctypes.byref(p))
     least = lib.attn_bwd_workspace_min(ctypes.byref(p))
     case("bwd_workspace_small", "CPA_ERR_WORKSPACE", bwd(p, wsb=least - 1))

@@ -7,7 +7,9 @@
   accuracy criterion for every split;
 * the ring-step use of the step entry points (the per-block backward of the
   pages' P2P ring): pre once, then main + dq per key block with that
-  block's K, V, dK, dV and k_pos_begin, then post once.
+  block's K, V, dK, dV and k_pos_begin, then post once;
+* the single-pass dQ (whole workspace: the dq kernel writes dq itself) is
+  bitwise the accumulating path's, zeros included.
 
 Every result is checked against the fp64 oracle with the accuracy
 criterion (tests/criteria.py).
@@ -181,3 +183,43 @@ def test_large_head_dims_deterministic_and_banded(d):
     _check(p, *banded, f"d{d}_bands")
     assert torch.equal(_bits(first[1]), _bits(banded[1]))
     assert torch.equal(_bits(first[2]), _bits(banded[2]))
+
+
+@pytest.mark.parametrize("dqk,dv,out", [(128, 128, torch.bfloat16), (192, 128, torch.bfloat16),
+                                         (192, 128, torch.float32), (512, 512, torch.bfloat16)])
+def test_single_pass_dq_matches_accumulated(dqk, dv, out):
+    """With a workspace for every key block, attn_bwd (and the four steps
+    given CPA_FLAG_DQ_DIRECT) let the dq kernel write dq itself: dq, dk, dv
+    are bitwise those of the accumulating steps (pre clears the
+    accumulator, dq adds dS K, post scales).  The keys start at position 200
+    and the queries at 0, so rows 0..199 see no key and their dq must be
+    written as exact zeros; every output starts as NaN."""
+    b_, sq, sk, hq, hkv, kpb = 1, 300, 450, 4, 2, 200
+    scale = 1.0 / math.sqrt(dqk)
+    g = torch.Generator().manual_seed(31 + dqk + dv)
+    d = dev()
+    q, k, v, do = (torch.randn(*sh, generator=g).to(torch.bfloat16).to(d)
+                   for sh in ((b_, sq, hq, dqk), (b_, sk, hkv, dqk), (b_, sk, hkv, dv),
+                              (b_, sq, hq, dv)))
+    say(f"single-pass dq d{dqk}/{dv} {out}: fwd")
+    o, lse = cpa.forward(q, k, v, scale=scale, k_pos_begin=kpb)
+    ws = torch.empty(cpa.bwd_workspace_bytes(q, k, v), dtype=torch.uint8, device=d)
+    common = dict(scale=scale, k_pos_begin=kpb, workspace=ws)
+    ints = torch.int32 if out == torch.float32 else torch.int16
+
+    def nan_outputs():
+        return tuple(torch.full(t.shape, float("nan"), dtype=out, device=d) for t in (q, k, v))
+
+    say(f"single-pass dq d{dqk}/{dv} {out}: attn_bwd")
+    ref = nan_outputs()
+    cpa.attn_bwd(q, k, v, o, do, lse, *ref, **common)
+    for flags in (0, cpa.CPA_FLAG_DQ_DIRECT):
+        say(f"single-pass dq d{dqk}/{dv} {out}: four steps, flags {flags}")
+        got = nan_outputs()
+        for step in ("attn_bwd_pre", "attn_bwd_main", "attn_bwd_dq", "attn_bwd_post"):
+            cpa.attn_bwd(q, k, v, o, do, lse, *got, step=step, flags=flags, **common)
+        torch.cuda.synchronize()
+        for name, x, y in zip(("dq", "dk", "dv"), ref, got):
+            assert torch.equal(x.view(ints), y.view(ints)), (name, flags)
+    assert not ref[0].isnan().any()
+    assert (ref[0][:, :kpb] == 0).all() and (ref[0][:, kpb:] != 0).any()
