@@ -271,7 +271,11 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, *, causal=True, scale=None, q_se
     """Backward into preallocated dq, dk, dv.  Returns the workspace.
 
     ``step`` selects the C entry point: "attn_bwd" (all four steps), or one
-    of "attn_bwd_pre", "attn_bwd_main", "attn_bwd_dq", "attn_bwd_post"."""
+    of "attn_bwd_pre", "attn_bwd_main", "attn_bwd_dq", "attn_bwd_post".
+    ``flags``: CPA_FLAG_DETERMINISTIC (always honoured), CPA_FLAG_DQ_DIRECT
+    (given to all four steps of a backward that runs main and dq once over
+    every key block: the dq step writes dq itself; "attn_bwd" with the full
+    workspace does so without the flag)."""
     if step not in ("attn_bwd", "attn_bwd_pre", "attn_bwd_main", "attn_bwd_dq", "attn_bwd_post"):
         raise ValueError(step)
     if o.dtype != q.dtype or dout.dtype != q.dtype:
