@@ -12,7 +12,8 @@ inputs drawn from N(0, 1).  One step = the whole path on one batch:
     accumulator in the forward kernel's epilogue (7 merges; the last
     writes the bf16 O),
   * pack + unpack of O and the fp32 LSE into 4 head-group segments,
-  * the backward (D, main kernel, dQ, dQ cast) over both chunks and all keys.
+  * the backward (D, main kernel, dQ written by the dq kernel in one pass)
+    over both chunks and all keys.
 Inputs are resident in HBM before the timed region starts.
 
 --workload dense8k | thd_gqa | d512 times the other full-size configurations
