@@ -264,33 +264,27 @@ __device__ __forceinline__ void dma_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Direct global-to-LDS copy of a [ROWS x D] tile of 2-byte elements into an
-// LDS tile of pitch P elements (logical row r at row rperm16(r) when PERM):
-// gfx950's 16-byte global_load_lds, with no staging registers.  Each wave
-// instruction fills 64 consecutive 16-byte LDS slots (lane l the slot at
-// the wave's base + l), so each lane loads the global chunk that belongs
-// in its slot; slots of the row padding load the row's first chunk (never
-// read).  Source rows past `limit` repeat the last row (limit >= 1).
-// NTH = threads of the workgroup; w, lane = the caller's wave and lane.
-template <int ROWS, int D, int P, int NTH, bool PERM, typename T>
-__device__ __forceinline__ void dma_tile(const T* base, int64_t row_stride, int r0, int limit,
+// Direct global-to-LDS copy of a [ROWS x D] tile of 2-byte elements with
+// D = 512 (one 1 KiB row = 64 lanes x 16 bytes) into an LDS tile of pitch P
+// elements: gfx950's 16-byte global_load_lds, with no staging registers,
+// one wave instruction per row.  Lane l copies the row's chunk l to LDS
+// row start + 16 l, so the row address is wave-uniform (scalar registers)
+// and the only per-lane term is the fixed chunk offset; the row padding
+// beyond D is never written (nor read).  Wave w of NW takes rows w, w + NW,
+// ...; source rows past `limit` repeat the last row (limit >= 1).
+template <int ROWS, int D, int P, int NW, typename T>
+__device__ __forceinline__ void dma_rows(const T* base, int64_t row_stride, int r0, int limit,
                                          T* tile, int w, int lane) {
-  static_assert(sizeof(T) == 2 && P % 8 == 0 && D % 8 == 0 && P >= D, "16-byte slots");
-  constexpr int S = P / 8, DS = D / 8, TOT = ROWS * S;
+  static_assert(sizeof(T) == 2 && D == 512 && P >= D && P % 8 == 0 && ROWS % NW == 0,
+                "one 1 KiB row per wave instruction");
 #pragma unroll
-  for (int r = 0; r * NTH < TOT; ++r) {
-    const int s0 = r * NTH + w * 64;   // this wave's first slot (uniform)
-    if (s0 < TOT) {
-      const int sl = s0 + lane;
-      const int prow = sl / S, cs = sl % S;
-      const int lrow = PERM ? rperm16(prow) : prow;
-      const int grow = min(r0 + lrow, limit - 1);
-      const T* g = base + (int64_t)grow * row_stride + (cs < DS ? cs : 0) * 8;
-      if (sl < TOT)
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(uintptr_t)g,
-            (__attribute__((address_space(3))) void*)(tile + s0 * 8), 16, 0, 0);
-    }
+  for (int i = 0; i < ROWS / NW; ++i) {
+    const int r = i * NW + w;                 // uniform
+    const int grow = min(r0 + r, limit - 1);  // uniform
+    const T* g = base + (int64_t)grow * row_stride + lane * 8;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(uintptr_t)g,
+                                     (__attribute__((address_space(3))) void*)(tile + r * P), 16, 0,
+                                     0);
   }
 }
 

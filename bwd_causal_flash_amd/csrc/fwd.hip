@@ -136,10 +136,8 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
   constexpr bool DMA = sizeof(TIn) == 2 && DVC > 256;
   auto dma_kv = [&](int t, int b) {
     if constexpr (DMA) {
-      dma_tile<BN, DQK, KP, NT, false>(Kb, a.k_stride[1], t * BN, s.klen, b ? Kx1 : Kx0, wave,
-                                       lane);
-      dma_tile<BN, DVC, VP, NT, false>(Vb, a.v_stride[1], t * BN, s.klen, b ? Vx1 : Vx0, wave,
-                                       lane);
+      dma_rows<BN, DQK, KP, NW>(Kb, a.k_stride[1], t * BN, s.klen, b ? Kx1 : Kx0, wave, lane);
+      dma_rows<BN, DVC, VP, NW>(Vb, a.v_stride[1], t * BN, s.klen, b ? Vx1 : Vx0, wave, lane);
     }
   };
   if (DMA && t0 < ntiles) dma_kv(t0, 0);
