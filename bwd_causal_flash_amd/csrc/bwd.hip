@@ -205,7 +205,7 @@ struct KvSmem {
   static constexpr int V_OFF = K_OFF + BN * KP * 2;
   static constexpr int BYTES = V_OFF + BN * VP * 2;
   // epilogue: one wave's partial accumulators per key group, fp32
-  static constexpr int RED_BYTES = 4 * DV / 32 * 16 * 64 * 4;
+  static constexpr int RED_BYTES = 4 * (DQK > DV ? DQK : DV) / 32 * 16 * 64 * 4;
   static_assert(BYTES <= 160 * 1024 && RED_BYTES <= BYTES, "LDS budget");
   static_assert(T_OFF <= 65536, "per-tile arrays within the immediate range");
 };
@@ -257,6 +257,13 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   constexpr int NDK = DQK / 32, NDV = DV / 32;
   constexpr int NDKH = NDK / 2;   // dK^T column blocks per query-half wave
   static_assert(NDK % 2 == 0, "dK column split");
+  // Head dims up to 128 leave the registers for all of dK^T in each wave:
+  // a wave then adds dS^T Q over its own 32 query rows, with its dS straight
+  // from registers, so the query halves exchange no dS and a tile needs one
+  // barrier less; the halves' dK partials are summed at the end, as dV's.
+  // Wider heads split dK^T by columns between the halves instead.
+  constexpr bool FULLDK = DQK <= 128;
+  constexpr int NACK = FULLDK ? NDK : NDKH;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   CT* Ks = reinterpret_cast<CT*>(smem + L::K_OFF);
   CT* Vs = reinterpret_cast<CT*>(smem + L::V_OFF);
@@ -300,9 +307,9 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   TileStage<BN, DQK, TIn, NT>::copy(K + kbase, a.k_stride[1], j0, s.klen, Ks, KP, tid);
   TileStage<BN, DV, TIn, NT>::copy(V + vbase, a.v_stride[1], j0, s.klen, Vs, VP, tid);
 
-  f32x16 acck[NDKH], accv[NDV];
+  f32x16 acck[NACK], accv[NDV];
 #pragma unroll
-  for (int d = 0; d < NDKH; ++d)
+  for (int d = 0; d < NACK; ++d)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acck[d][v] = 0.f;
 #pragma unroll
@@ -574,19 +581,39 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      CT8 wd[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        CT8 wd;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wd[e] = (CT)pacc[8 * tt + e];
+        for (int e = 0; e < 8; ++e) wd[tt][e] = (CT)pacc[8 * tt + e];
         // dS^T block of this wave: row = key, column = query row (natural order)
-        *reinterpret_cast<CT8*>(&Tw[lq * TP + 16 * tt + 8 * hh]) = wd;
+        *reinterpret_cast<CT8*>(&Tw[lq * TP + 16 * tt + 8 * hh]) = wd[tt];
+      }
+      if constexpr (FULLDK) {
+        // dK^T += Q^T dS over the wave's 32 rows: wd[tt] is the B operand
+        // (lane = key column, 8 consecutive query rows), the same 16 bytes
+        // a row read of the block just written would return.
+        constexpr int N = 2 * NDK, AHEAD = kDkAhead < N ? kDkAhead : N;
+        CT8 qa[N];
+        auto rd = [&](int i) {
+          const int tt = i / NDK, db = i % NDK;
+          qa[i] = lds_tr8p(Qs, QP, 32 * qh + 16 * tt + 8 * (grp >> 1), db * 32 + 16 * (grp & 1), gl);
+        };
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i) rd(i);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          if (i + AHEAD < N) rd(i + AHEAD);
+          acck[i % NDK] = mfma32(qa[i], wd[i / NDK], acck[i % NDK]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     } else {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
         *reinterpret_cast<CT8*>(&Tw[lq * TP + 16 * tt + 8 * hh]) = zero8<CT>();
     }
+    if constexpr (!FULLDK) {
     __syncthreads();   // both query halves' dS blocks are in LDS
 
     // dK^T column blocks [qh*NDKH, +NDKH) over both query halves; the dS
@@ -620,6 +647,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    }
     // This wave's two dS chunks (zeros when the half is off) go out at the
     // top of the next iteration.
     prev_tile = (((int64_t)h * a.ds_nu + ubase + ut) * a.ds_nb + (kt - a.kt0)) * kDsTileElems;
@@ -628,30 +656,40 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   }
 
   if (prev_tile >= 0) store_prev();
-  // dK: each wave holds complete sums for its column blocks.  dV: the two
-  // query halves' partials are summed through LDS into the qh = 0 waves.
+  // dV, and dK when each wave holds all of it: the two query halves'
+  // partials are summed through LDS into the qh = 0 waves.  Split dK: each
+  // wave holds complete sums for its column blocks.
   auto key_row = [&](void* outp, const int64_t* st) -> TOut* {
     return static_cast<TOut*>(outp) +
            (a.thd ? (s.k_row0 + my_key) * st[1] : (int64_t)z * st[0] + (int64_t)my_key * st[1]) +
            (int64_t)kvh * st[2];
   };
-  if (key_valid) store_key_acc(acck, key_row(a.dk, a.dk_stride) + qh * NDKH * 32, hh, a.scale);
   float* red = reinterpret_cast<float*>(smem);
-  __syncthreads();
-  if (qh == 1) {
+  auto sum_halves = [&](auto& acc) {
+    constexpr int ND = sizeof(acc) / sizeof(acc[0]);
+    __syncthreads();   // the loop's (or the previous sum's) LDS reads are done
+    if (qh == 1) {
 #pragma unroll
-    for (int db = 0; db < NDV; ++db)
+      for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) red[((kg * NDV + db) * 16 + v) * 64 + lane] = accv[db][v];
+        for (int v = 0; v < 16; ++v) red[((kg * ND + db) * 16 + v) * 64 + lane] = acc[db][v];
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db][v] += red[((kg * ND + db) * 16 + v) * 64 + lane];
+    }
+  };
+  if constexpr (FULLDK) {
+    sum_halves(acck);
+    if (qh == 0 && key_valid) store_key_acc(acck, key_row(a.dk, a.dk_stride), hh, a.scale);
+  } else {
+    if (key_valid) store_key_acc(acck, key_row(a.dk, a.dk_stride) + qh * NDKH * 32, hh, a.scale);
   }
-  __syncthreads();
-  if (qh == 0) {
-#pragma unroll
-    for (int db = 0; db < NDV; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) accv[db][v] += red[((kg * NDV + db) * 16 + v) * 64 + lane];
-    if (key_valid) store_key_acc(accv, key_row(a.dv, a.dv_stride), hh, 1.f);
-  }
+  sum_halves(accv);
+  if (qh == 0 && key_valid) store_key_acc(accv, key_row(a.dv, a.dv_stride), hh, 1.f);
 }
 
 // Key blocks [first, last] that query tile ut of sequence s sees (last = -1
