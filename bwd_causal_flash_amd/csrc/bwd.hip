@@ -210,8 +210,6 @@ struct KvSmem {
   static_assert(T_OFF <= 65536, "per-tile arrays within the immediate range");
 };
 
-// Write a key's accumulated row (dK^T or dV^T layout: lane = key column,
-// element v = dimension 8*(v/4) + 4*hh + v%4 of each 32-wide block) times mul.
 // Workgroups go to the 8 XCDs round-robin in launch order, and each XCD
 // has its own L2.  Re-deal a (x, y) grid slice so that XCD c runs the
 // contiguous range [c*N/8, (c+1)*N/8) of x-major indices: the workgroups
@@ -226,6 +224,8 @@ __device__ __forceinline__ void xcd_remap(int& x, int& y) {
   y = t % gy;
 }
 
+// Write a key's accumulated row (dK^T or dV^T layout: lane = key column,
+// element v = dimension 8*(v/4) + 4*hh + v%4 of each 32-wide block) times mul.
 template <int ND, typename TOut>
 __device__ __forceinline__ void store_key_acc(const f32x16 (&acc)[ND], TOut* o, int hh, float mul) {
 #pragma unroll
