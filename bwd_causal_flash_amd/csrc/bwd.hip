@@ -729,17 +729,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int hh = lane >> 5, lq = lane & 31, grp = lane >> 4, gl = lane & 15;
-  // Workgroups go to the 8 XCDs round-robin in launch order (XCD = linear id
-  // % 8), each XCD with its own L2.  With 8 | gridDim.x, XCD c runs the
-  // contiguous range [c X/8, (c+1) X/8) of (head, column chunk) indices:
-  // consecutive query heads share a kv head, so its K tiles are fetched into
-  // as few L2s as possible, and the column chunks of a head, which read the
-  // same dS tiles, run on one XCD.
-  constexpr int NCH = DQK / DC;
-  const int gx = gridDim.x;
-  const int xi = gx % 8 == 0 ? (blockIdx.x % 8) * (gx / 8) + blockIdx.x / 8 : blockIdx.x;
-  const int h = xi / NCH;
-  const int c0 = (xi % NCH) * DC;
+  const int h = blockIdx.x % a.heads_q;
+  const int c0 = (blockIdx.x / a.heads_q) * DC;
   const int kvh = h / a.group;
   const int z = blockIdx.z;
   const Seq s = load_seq(a, z);
@@ -812,8 +803,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
     const CT* p = dst + (int64_t)(kt - a.kt0) * kDsTileElems;
     // With one column chunk the tiles are streamed once: non-temporal, so
     // K keeps the L2.  With two (head dim 512) the other chunk's workgroup
-    // (the neighbouring chunk index: the same XCD, dispatched alongside)
-    // reads the same tiles right after: plain loads leave them in L2 for it.
+    // (blockIdx.x + heads_q: the same XCD when 8 | heads_q, dispatched
+    // alongside) reads the same tiles right after: plain loads leave them
+    // in L2 for it.
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const CT8* q = reinterpret_cast<const CT8*>(p + (loff + 512u * t));
