@@ -38,11 +38,15 @@ template <int DQK, int DVC, int NCH, typename TIn, typename TOut, bool WIN>
 __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(const AttnArgs a) {
   constexpr int NW = fwd_waves<DQK + DVC>(), NT = 64 * NW, BM = 32 * NW;
   // Keys per tile: 32 for head dim 512, whose 128-register Q operand and
-  // 128 accumulator registers per lane leave no room to stage 64-key tiles.
-  constexpr int BN = DQK > 256 ? 32 : 64, NKB = BN / 32;
-  // K/V tiles double-buffered in LDS at every head dim (92 KB at 192/128,
-  // 142 KB at 256, 103 KB at 512 with its 32-key tiles), so a tile costs one
-  // barrier.
+  // 128 accumulator registers per lane leave no room to stage 64-key tiles;
+  // 128 for head dims up to 128 with 2-byte inputs (the barrier, staging and
+  // row max of a tile then serve twice the products; fp32 inputs would
+  // spill), 64 otherwise (two 128-key buffers exceed the LDS at 192/128).
+  constexpr int BN = DQK > 256 ? 32 : (DQK + DVC <= 256 && sizeof(TIn) == 2 ? 128 : 64);
+  constexpr int NKB = BN / 32;
+  // K/V tiles double-buffered in LDS at every head dim (156 KB at 128/128
+  // with 128-key tiles, 92 KB at 192/128, 142 KB at 256, 103 KB at 512 with
+  // its 32-key tiles), so a tile costs one barrier.
   constexpr int NBUF = 2;
   using CT = ct_t<TIn>;   // matrix-core operand type
   using CT8 = vec8<CT>;
