@@ -262,7 +262,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   // from registers, so the query halves exchange no dS and a tile needs one
   // barrier less; the halves' dK partials are summed at the end, as dV's.
   // Wider heads split dK^T by columns between the halves instead.
-  constexpr bool FULLDK = DQK <= 128;
+  constexpr bool FULLDK = DQK <= 128 && !WIN;   // (the band bounds would spill)
   constexpr int NACK = FULLDK ? NDK : NDKH;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   CT* Ks = reinterpret_cast<CT*>(smem + L::K_OFF);
@@ -815,9 +815,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
 
   // dS fragments AHEAD key blocks ahead, in AHEAD + 1 register sets used in
   // turn (no register copy between iterations, which would force a wait for
-  // the prefetched loads).  Wide column chunks keep one block ahead so the
-  // accumulators fit without spilling.
-  constexpr int AHEAD = NDK > 6 ? 1 : 2;
+  // the prefetched loads).  Wide column chunks, and fp32 inputs (whose K
+  // tiles are converted on the way), keep one block ahead so the registers
+  // fit without spilling.
+  constexpr int AHEAD = (NDK > 6 || sizeof(TIn) == 4) ? 1 : 2;
   TileStage<BN, DC, TIn, NT, false> kst;   // dS is exactly zero past the last key
   CT8 fa[8], fb[8], fc[AHEAD == 2 ? 8 : 1];
   // Issue order as at the end of a step (K tile, then one block of dS), so
@@ -914,8 +915,9 @@ __device__ __forceinline__ bool tile_sees_block(const AttnArgs& a, const Seq& s,
   return kt >= f && kt <= l;
 }
 
-// Keys per sdp workgroup: 128 keys x 128 query rows keeps the LDS (2 x 40
-// KiB) and registers (<= 128) small enough for two workgroups per CU.
+// Keys per sdp workgroup: 128 keys x 128 query rows keeps the LDS (two 32
+// KiB sets of chunk buffers) and registers (<= 128) small enough for two
+// workgroups per CU.
 constexpr int kSdpKeys = 128;
 
 template <int D, typename TIn, bool WIN>
@@ -933,10 +935,17 @@ void bwd_sdp_kernel(const AttnArgs a) {
   constexpr int LP = DC;
   static_assert(DC == 32, "four 16-byte pieces per row");
   auto sw = [](int r, int piece) { return r * LP + 8 * (piece ^ ((r >> 2) & 3)); };
-  __shared__ __attribute__((aligned(16))) CT Qs[2][BQ * LP];
-  __shared__ __attribute__((aligned(16))) CT Os[2][BQ * LP];
-  __shared__ __attribute__((aligned(16))) CT Ks[2][BK * LP];
-  __shared__ __attribute__((aligned(16))) CT Vs[2][BK * LP];
+  // Two buffers per operand as separate arrays used in a fixed order, so the
+  // compiler can tell the direct copies into one from the reads of the other.
+  __shared__ __attribute__((aligned(16))) CT Qs0[BQ * LP];
+  __shared__ __attribute__((aligned(16))) CT Qs1[BQ * LP];
+  __shared__ __attribute__((aligned(16))) CT Os0[BQ * LP];
+  __shared__ __attribute__((aligned(16))) CT Os1[BQ * LP];
+  __shared__ __attribute__((aligned(16))) CT Ks0[BK * LP];
+  __shared__ __attribute__((aligned(16))) CT Ks1[BK * LP];
+  __shared__ __attribute__((aligned(16))) CT Vs0[BK * LP];
+  __shared__ __attribute__((aligned(16))) CT Vs1[BK * LP];
+  static_assert(BQ == 128 && BK == 128 && sizeof(CT) == 2, "one copy shape");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int hh = lane >> 5, lq = lane & 31;
@@ -999,32 +1008,51 @@ void bwd_sdp_kernel(const AttnArgs a) {
                  (a.thd ? s.k_row0 * a.v_stride[1] : (int64_t)z * a.v_stride[0]) +
                  (int64_t)kvh * a.v_stride[2];
 
-  // Staging of one 32-column chunk: 128 Q and dO rows, 128*NX K and V
-  // rows, 4 x 16 bytes per row; thread t owns row t/4 (+128) and piece t%4.
-  // Rows past the ends repeat the last row, on one branch-free path: their
-  // products only reach P entries that are zero (LSE = -inf rows, masked
-  // keys), so their values never matter.
-  const int sr = tid >> 2, sp = tid & 3, sc = sp * 8;
-  CT8 stq, sto, stk[NX], stv[NX];
-  auto load_chunk = [&](int c) {
-    const int col = c * DC + sc;
-    const int qr = min(i0 + sr, s.qlen - 1);
-    stq = Elem<TIn>::load8(Q + (int64_t)qr * a.q_stride[1] + col);
-    sto = Elem<TIn>::load8(dO + (int64_t)qr * a.do_stride[1] + col);
+  // Staging of one 32-column chunk straight from global memory into LDS
+  // (gfx950's 16-byte global_load_lds, no staging registers): wave w copies
+  // operand w / 2 (Q, dO, K, V), rows 64 (w % 2) + 16 j + lane / 4 for j =
+  // 0..3, one instruction per 16 rows.  Lane l lands at byte 16 l of the 16
+  // rows, i.e. slot l % 4 of row l / 4, so it loads the piece that slot
+  // holds in the swizzled layout, (l % 4) ^ ((row / 4) % 4) = (l % 4) ^ (l / 16).
+  // Rows past the ends repeat the last row (branch-free), as their products
+  // only reach P entries that are zero.
+  // (fp32 inputs are rounded on the way, so they go through registers.)
+  constexpr bool DMA = sizeof(TIn) == 2;
+  const int op = wave >> 1;
+  const TIn* const src = op == 0 ? Q : op == 1 ? dO : op == 2 ? K : V;
+  const int64_t rstride = op == 0 ? a.q_stride[1] : op == 1 ? a.do_stride[1]
+                        : op == 2 ? a.k_stride[1] : a.v_stride[1];
+  const int rfirst = op < 2 ? i0 : j0, rlim = op < 2 ? s.qlen : s.klen;
+  const int rw = (wave & 1) * 64;
+  int64_t goff[4];
 #pragma unroll
-    for (int r = 0; r < NX; ++r) {
-      const int kr = min(j0 + sr + 128 * r, s.klen - 1);
-      stk[r] = Elem<TIn>::load8(K + (int64_t)kr * a.k_stride[1] + col);
-      stv[r] = Elem<TIn>::load8(V + (int64_t)kr * a.v_stride[1] + col);
+  for (int j = 0; j < 4; ++j) {
+    const int grow = min(rfirst + rw + 16 * j + (lane >> 2), rlim - 1);
+    goff[j] = (int64_t)grow * rstride + 8 * ((lane & 3) ^ ((lane >> 4) & 3));
+  }
+  CT* const dst0 = op == 0 ? Qs0 : op == 1 ? Os0 : op == 2 ? Ks0 : Vs0;
+  CT* const dst1 = op == 0 ? Qs1 : op == 1 ? Os1 : op == 2 ? Ks1 : Vs1;
+  CT8 stg[4];
+  auto copy_chunk = [&](int c, int b) {
+    if constexpr (DMA) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(uintptr_t)(src + goff[j] + c * DC),
+            (__attribute__((address_space(3))) void*)((b ? dst1 : dst0) + (rw + 16 * j) * LP), 16,
+            0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) stg[j] = Elem<TIn>::load8(src + goff[j] + c * DC);
     }
   };
+  // register path: the staged chunk goes to LDS at the end of the step
   auto store_chunk = [&](int b) {
-    *reinterpret_cast<CT8*>(&Qs[b][sw(sr, sp)]) = stq;
-    *reinterpret_cast<CT8*>(&Os[b][sw(sr, sp)]) = sto;
+    if constexpr (!DMA) {
 #pragma unroll
-    for (int r = 0; r < NX; ++r) {
-      *reinterpret_cast<CT8*>(&Ks[b][sw(sr + 128 * r, sp)]) = stk[r];
-      *reinterpret_cast<CT8*>(&Vs[b][sw(sr + 128 * r, sp)]) = stv[r];
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<CT8*>((b ? dst1 : dst0) + (rw + 16 * j) * LP + 8 * (lane & 3) +
+                                (lane >> 2) * LP) = stg[j];
     }
   };
 
@@ -1037,12 +1065,18 @@ void bwd_sdp_kernel(const AttnArgs a) {
       for (int v = 0; v < 16; ++v) { sacc[x][y][v] = 0.f; pacc[x][y][v] = 0.f; }
 
   const int pr = perm32(lq);
-  load_chunk(0);
+  copy_chunk(0, 0);
   store_chunk(0);
-  __syncthreads();
+  dma_barrier();
+#pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int b = c & 1;
-    if (c + 1 < NC) load_chunk(c + 1);
+    if (c + 1 < NC) copy_chunk(c + 1, b ^ 1);
+    asm volatile("" ::: "memory");   // the copies stay ahead of this chunk's LDS reads
+    const CT* const Qb = b ? Qs1 : Qs0;
+    const CT* const Ob = b ? Os1 : Os0;
+    const CT* const Kb = b ? Ks1 : Ks0;
+    const CT* const Vb = b ? Vs1 : Vs0;
     // Raised issue priority over the burst of products (two workgroups
     // share each CU; the other one's softmax and staging fill the gaps).
     __builtin_amdgcn_s_setprio(1);
@@ -1052,14 +1086,14 @@ void bwd_sdp_kernel(const AttnArgs a) {
 #pragma unroll
       for (int x = 0; x < NX; ++x) {
         const int kr = kg * 32 * NX + x * 32 + pr;
-        ka[x] = *reinterpret_cast<const CT8*>(&Ks[b][sw(kr, 2 * ks + hh)]);
-        va[x] = *reinterpret_cast<const CT8*>(&Vs[b][sw(kr, 2 * ks + hh)]);
+        ka[x] = *reinterpret_cast<const CT8*>(&Kb[sw(kr, 2 * ks + hh)]);
+        va[x] = *reinterpret_cast<const CT8*>(&Vb[sw(kr, 2 * ks + hh)]);
       }
 #pragma unroll
       for (int y = 0; y < 2; ++y) {
         const int qr = qh * 64 + y * 32 + lq;
-        qb[y] = *reinterpret_cast<const CT8*>(&Qs[b][sw(qr, 2 * ks + hh)]);
-        ob[y] = *reinterpret_cast<const CT8*>(&Os[b][sw(qr, 2 * ks + hh)]);
+        qb[y] = *reinterpret_cast<const CT8*>(&Qb[sw(qr, 2 * ks + hh)]);
+        ob[y] = *reinterpret_cast<const CT8*>(&Ob[sw(qr, 2 * ks + hh)]);
       }
 #pragma unroll
       for (int x = 0; x < NX; ++x)
@@ -1071,7 +1105,9 @@ void bwd_sdp_kernel(const AttnArgs a) {
     }
     __builtin_amdgcn_s_setprio(0);
     if (c + 1 < NC) store_chunk(b ^ 1);
-    __syncthreads();
+    // this wave's copies of chunk c + 1 have landed, and every wave is done
+    // with buffer b, which takes chunk c + 2 next
+    dma_barrier();
   }
 
   // Epilogue: lane = query row (qh*64 + y*32 + lq), element v = key
@@ -1398,9 +1434,12 @@ static hipError_t bwd_variant(const AttnArgs& a, int step, hipStream_t st) {
     }
   }
   if (step == 2 && krows > 0 && qrows > 0) {
+    // fp32 inputs take 128-column chunks from head dim 256 on: their K tiles
+    // are converted on the way into LDS, and wider chunks would spill.
+    constexpr int DC = (sizeof(TIn) == 4 && DQK >= 256) ? 128 : C::DQ_COLS;
     const int qtiles = (qrows + 63) / 64;
-    dim3 g(a.heads_q * (DQK / C::DQ_COLS), (qtiles + 3) / 4, a.nseq);
-    hipLaunchKernelGGL((bwd_dq_kernel<DQK, C::DQ_COLS, TIn, TOut>), g, dim3(512), 0, st, a);
+    dim3 g(a.heads_q * (DQK / DC), (qtiles + 3) / 4, a.nseq);
+    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DC, TIn, TOut>), g, dim3(512), 0, st, a);
   }
   if (step == 3 && qrows > 0) {
     constexpr int PB = 256 / pow2_at_least(DQK / 8);

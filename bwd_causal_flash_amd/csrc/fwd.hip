@@ -177,7 +177,7 @@ __global__ __launch_bounds__(64 * fwd_waves<DQK + DVC>(), 1) void fwd_kernel(con
       // compiler, short of registers, otherwise waits on each read right
       // before its product).
       static_assert(NKB == 1, "one key block");
-      constexpr int RA = 6;
+      constexpr int RA = WIN ? 4 : 6;   // (the band bounds take registers too)
       CT8 kf[RA];
 #pragma unroll
       for (int i = 0; i < RA; ++i) kf[i] = lds_row8(Ks, KP, kr, i * 16 + hh * 8);
@@ -415,7 +415,7 @@ static hipError_t fwd_variant(const AttnArgs& a, hipStream_t st) {
   // output (K/V copied straight into LDS), so the scores of a row tile are
   // computed once.  fp32 inputs, which are rounded on the way through
   // registers, keep two 256-wide column chunks (one workgroup each).
-  constexpr int DVC = (DV > 256 && sizeof(TIn) != 2) ? 256 : DV;
+  constexpr int DVC = (DV > 128 && DQK > 192 && sizeof(TIn) != 2) ? 128 : DV;
   constexpr int NCH = DV / DVC;
   const int qrows = a.thd ? a.max_q : (int)a.seqlen_q;
   constexpr int NT = 64 * fwd_waves<DQK + DVC>(), BM = NT / 2;

@@ -35,9 +35,15 @@ CASES = [
     ("d192_kv_block_partial_fp32out", 1, 200, 256, 2, 2, 192, 128, "bf16", "fp32", True,
      [(0, 700)], 512),
     ("d64_fp32_in_bf16_out", 1, 190, 190, 2, 1, 64, 64, "fp32", "bf16", True, None, 0),
-    # all keys in one partial key tile (64 keys; 32 at head dim 512)
+    # all keys in one partial key tile (64 keys; 128 at head dims up to 128
+    # with 2-byte inputs, 32 at head dim 512)
     ("d192_128_one_key_tile", 1, 70, 40, 2, 2, 192, 128, "bf16", "bf16", True, None, 0),
+    ("d128_one_key_tile", 1, 90, 100, 2, 2, 128, 128, "bf16", "bf16", True, None, 0),
     ("d512_one_key_tile", 1, 33, 20, 2, 1, 512, 512, "bf16", "bf16", True, None, 0),
+    # fp32 inputs through the head dim 256/512 kernels (rounded to bf16 on
+    # the way into LDS, where 2-byte inputs are copied in directly)
+    ("d256_fp32_in_ragged", 1, 150, 170, 2, 1, 256, 256, "fp32", "bf16", True, None, 0),
+    ("d512_fp32_io", 1, 130, 130, 2, 2, 512, 512, "fp32", "fp32", True, None, 0),
 ]
 
 DT = {"bf16": torch.bfloat16, "fp32": torch.float32}

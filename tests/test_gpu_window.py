@@ -171,3 +171,42 @@ def test_window_thd_documents():
         criteria.check(name, a[real], ref["true"][b][real], ref["naive"][b][real], grad=True,
                        log=log, out_bf16=True)
     print("thd window", {k_: round(v_["ratio"], 3) for k_, v_ in log.items() if "ratio" in v_})
+
+
+# fp32 inputs (rounded to bf16 on the way into the kernels) and fp32 outputs
+# through the banded kernels of each head-dim family: the fp32-input staging
+# paths and the fp32-output epilogues of the windowed kernels.
+# name, Sq, Sk, Hq, Hkv, Dqk, Dv, causal, window, segments, k_pos_begin, in, out
+FP32_CASES = [
+    ("d192_fp32_io_left300", 256, 512, 4, 2, 192, 128, True, (300, -1), None, 0, "fp32", "fp32"),
+    ("d128_fp32_in_band_70_40", 200, 260, 2, 2, 128, 128, False, (70, 40), None, 0,
+     "fp32", "bf16"),
+    ("d256_fp32_io_left90", 200, 200, 2, 1, 256, 256, True, (90, -1), None, 0, "fp32", "fp32"),
+    ("d512_fp32_io_left64", 130, 130, 2, 2, 512, 512, True, (64, -1), None, 0, "fp32", "fp32"),
+    ("d512_bf16_in_fp32_out_left64", 150, 150, 2, 1, 512, 512, True, (64, -1), None, 0,
+     "bf16", "fp32"),
+]
+_DT = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+@pytest.mark.parametrize("case", FP32_CASES, ids=lambda c: c[0])
+def test_window_fp32_io(case):
+    name, sq, sk, hq, hkv, dqk, dv, causal, win, segs, kp0, idt, odt = case
+    q, k, v, do = _draw(case, 400 + FP32_CASES.index(case))
+    ref = _oracle(case[:11], q, k, v, do)
+    d = dev()
+    qi, ki, vi, doi = (x.to(_DT[idt]).to(d) for x in (q, k, v, do))
+    kw = dict(causal=causal, scale=1.0 / math.sqrt(dqk), q_segments=segs, k_pos_begin=kp0,
+              window=win)
+    say(f"window fp32 fwd {name}")
+    o, lse = cpa.forward(qi, ki, vi, out_dtype=_DT[odt], **kw)
+    say(f"window fp32 bwd {name}")
+    dq, dk, dv_ = cpa.backward(qi, ki, vi, o.to(_DT[idt]), doi, lse, out_dtype=_DT[odt], **kw)
+    torch.cuda.synchronize()
+    ob = odt == "bf16"
+    log = {}
+    criteria.check("O", o, ref["true"]["o"], ref["naive"]["o"], log=log, out_bf16=ob)
+    criteria.check_lse("LSE", lse, ref["true"]["lse"], ref["naive"]["lse"], log=log)
+    for g, val in (("dq", dq), ("dk", dk), ("dv", dv_)):
+        criteria.check(g, val, ref["true"][g], ref["naive"][g], grad=True, log=log, out_bf16=ob)
+    print(name, {k_: round(v_["ratio"], 3) for k_, v_ in log.items() if "ratio" in v_})
