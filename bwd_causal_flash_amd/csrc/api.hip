@@ -88,7 +88,8 @@ GridRows grid_rows(const cpa_problem* p) {
 bool fwd_grids_ok(const cpa_problem* p) {
   const GridRows g = grid_rows(p);
   const bool big = p->d_qk + p->d_v > 320;
-  const int64_t bm = big ? 128 : 256, nch = p->d_v > 256 ? 2 : 1;
+  // (column chunks: up to d_v / 128 where fp32 inputs split the output)
+  const int64_t bm = big ? 128 : 256, nch = p->d_v > 128 && p->d_qk > 192 ? p->d_v / 128 : 1;
   return cdiv(g.qrows, bm) <= kGridYZ && (int64_t)p->heads_q * nch * (2 * bm) <= kGridX;
 }
 int64_t pow2_at_least(int64_t x) { return x <= 8 ? 8 : x <= 16 ? 16 : x <= 32 ? 32 : 64; }
@@ -97,8 +98,9 @@ bool bwd_grids_ok(const cpa_problem* p) {
   const int64_t hq = p->heads_q, hkv = p->heads_kv;
   const int64_t kblocks = cdiv(g.krows, 128), qtiles = cdiv(g.qrows, 64);
   const bool big = p->d_qk + p->d_v > 320;
-  const int64_t dq_chunks = p->d_qk > 256 ? p->d_qk / 256 : 1;
-  if (g.qrows * hq * (p->d_v / 8) + 256 > kGridX) return false;               // pre
+  const int64_t dq_chunks = p->d_qk >= 256 ? p->d_qk / 128 : 1;   // (fp32: 128 columns)
+  const int64_t pre_rows = p->layout == CPA_LAYOUT_THD ? p->seqlen_q : g.qrows;   // THD: packed
+  if (pre_rows * hq * (p->d_v / 8) + 256 > kGridX) return false;               // pre
   if (g.qrows * hq * pow2_at_least(p->d_qk / 8) + 256 > kGridX) return false;  // post
   if (cdiv(qtiles, 64) * 64 > kGridX) return false;                            // tile table
   if (kblocks > kGridYZ || cdiv(qtiles, 4) > kGridYZ) return false;            // main, dq

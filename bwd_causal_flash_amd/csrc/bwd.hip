@@ -38,18 +38,22 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a) {
   constexpr int G = DV / 8;            // lanes per (row, head)
   constexpr int PER_BLOCK = 256 / G;
   if (!a.thd && (blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *a.err_flag = 0;
+  // BSHD: one grid slice per batch entry.  THD: one pass over all packed
+  // rows (D and the accumulator are indexed by packed row, so no document
+  // lookup is needed; the padding rows' entries are workspace never read),
+  // instead of a slice per document sized for the longest one.
   const int z = blockIdx.z;
-  const Seq s = load_seq(a, z);
+  const int64_t nrows = a.thd ? a.seqlen_q : load_seq(a, z).qlen;
   const int gid = threadIdx.x / G, gl = threadIdx.x % G;
   const int64_t pair = (int64_t)blockIdx.x * PER_BLOCK + gid;
   const int64_t row = pair / a.heads_q;
   const int h = (int)(pair % a.heads_q);
-  const bool valid = row < s.qlen;
+  const bool valid = row < nrows;
   const TIn* O = static_cast<const TIn*>(a.o);
   const TIn* dO = static_cast<const TIn*>(a.dout);
   float acc = 0.f;
   if (valid) {
-    const int64_t prow = a.thd ? s.q_row0 + row : row;
+    const int64_t prow = row;
     const int64_t ob = (a.thd ? 0 : (int64_t)z * a.o_stride[0]) + prow * a.o_stride[1] +
                        (int64_t)h * a.o_stride[2] + gl * 8;
     const int64_t db = (a.thd ? 0 : (int64_t)z * a.do_stride[0]) + prow * a.do_stride[1] +
@@ -62,7 +66,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a) {
 #pragma unroll
   for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, G);
   if (!valid) return;
-  const int64_t prow = a.thd ? s.q_row0 + row : row;
+  const int64_t prow = row;
   if (gl == 0) {
     const int64_t doff = (a.thd ? 0 : (int64_t)z * a.delta_stride[0]) +
                          (int64_t)h * a.delta_stride[1] + prow;
@@ -1403,8 +1407,8 @@ static hipError_t bwd_variant(const AttnArgs& a, int step, hipStream_t st) {
   if (a.nseq == 0) return hipSuccess;
   if (step == 0 && qrows > 0) {
     constexpr int PB = 256 / (DV / 8);
-    const int64_t pairs = (int64_t)qrows * a.heads_q;
-    dim3 g((unsigned)((pairs + PB - 1) / PB), 1, a.nseq);
+    const int64_t pairs = (a.thd ? a.seqlen_q : (int64_t)qrows) * a.heads_q;
+    dim3 g((unsigned)((pairs + PB - 1) / PB), 1, a.thd ? 1 : a.nseq);
     hipLaunchKernelGGL((bwd_pre_kernel<DV, DQK, TIn>), g, dim3(256), 0, st, a);
     if constexpr (C::KV_KERNEL) {
       const int qtiles = (qrows + 63) / 64;
