@@ -339,14 +339,18 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
     return (!a.causal || (h0 > h1 ? h0 : h1) + bd.wr >= gkpos_lo) &&
            (!bd.left || (l0 < l1 ? l0 : l1) - bd.wl <= gkpos_hi);
   };
-  // Next (query head, tile) at or after (hg, ut) whose tile sees a key of
-  // the block.  Every workgroup walks the tiles in the same order, so the
-  // ones that run together on an XCD read each Q / dO tile while it is in L2.
-  // With query positions that never decrease with the row (THD; BSHD
-  // segments in order) the tile bounds never decrease either, so the tiles
-  // that see the block are one run [u_lo, u_hi], found once by bisection,
-  // and the walk needs no per-tile test (each reads the table through the
-  // scalar cache and waits for it while every wave of the CU waits too).
+  // Next (query head, tile) whose tile sees a key of the block.  With query
+  // positions that never decrease with the row (THD; BSHD segments in
+  // order) the tile bounds never decrease either, so the tiles that see the
+  // block are one run [u_lo, u_hi], found once by bisection, and the walk
+  // needs no per-tile test (each reads the table through the scalar cache
+  // and waits for it while every wave of the CU waits too).  Each head's run
+  // is walked from u_hi down: the runs of the key blocks end at the same
+  // tile (the last one, causally), so the workgroups that run together on
+  // an XCD start on the same tile and read each Q / dO tile while it is in
+  // L2 (walked upwards, blocks near the start of a sequence, which see more
+  // of it, would each begin at a different tile).  Otherwise the tiles are
+  // tested one by one, upwards.
   bool mono = true;
   if (!a.thd)
     for (int t = 1; t < a.nseg; ++t)
@@ -372,11 +376,11 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
     if (mono) {
       if (u_lo > u_hi) {
         hg = a.group;
-      } else if (ut < u_lo) {
-        ut = u_lo;
       } else if (ut > u_hi) {
+        ut = u_hi;
+      } else if (ut < u_lo) {
         ++hg;
-        ut = u_lo;
+        ut = u_hi;
       }
       return;
     }
@@ -419,7 +423,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
   // this lane's 16 bytes of the wave's first chunk (qb2 = qh, t = 2*kg)
   const int64_t chunk_off = ((int64_t)(qh * 8 + 2 * kg) * 64 + lane) * 8;
 
-  int hg = 0, ut = 0;
+  int hg = 0, ut = mono ? nqt : 0;
   seek(hg, ut);
   if (hg < a.group) fetch(hg, ut);
   // A tile's two dS chunks are stored at the top of the next iteration,
@@ -454,7 +458,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(const AttnArgs a) {
     }
     asm volatile("" :: "v"(sd0), "v"(sd1));   // the previous stores' registers
     if (prev_tile >= 0) store_prev();
-    int nhg = hg, nut = ut + 1;
+    int nhg = hg, nut = mono ? ut - 1 : ut + 1;
     seek(nhg, nut);
     __syncthreads();
 
