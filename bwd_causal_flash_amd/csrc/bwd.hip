@@ -831,23 +831,29 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   CT8 fa[8], fb[8], fc[AHEAD == 2 ? 8 : 1];
   // Issue order as at the end of a step (K tile, then one block of dS), so
   // the loop head sees the same loads in flight from both of its entries.
-  load_frags(kt_begin, fa);
-  kst.load(K + kbase, a.k_stride[1], kt_begin * BN, s.klen, tid);
-  kst.store(Ks + (kt_begin & 1) * BN * KP, KP, tid);
-  kst.load(K + kbase, a.k_stride[1], min(kt_begin + 1, kt_end - 1) * BN, s.klen, tid);
-  if (AHEAD == 2) load_frags(min(kt_begin + 1, kt_end - 1), fb);
-  // One barrier per block: block kt's K tile sits in buffer kt & 1 (stored
-  // during the previous step), and the step stores block kt + 1's tile into
+  // Step i handles key block blk(i), from the last block down: the key
+  // kernel writes the late blocks' dS last, so their tiles are the ones
+  // most likely still in the memory-side cache.
+  const int nblk = kt_end - kt_begin;
+  auto blk = [&](int i) { return kt_end - 1 - (i < nblk ? i : nblk - 1); };
+  load_frags(blk(0), fa);
+  kst.load(K + kbase, a.k_stride[1], blk(0) * BN, s.klen, tid);
+  kst.store(Ks, KP, tid);
+  kst.load(K + kbase, a.k_stride[1], blk(1) * BN, s.klen, tid);
+  if (AHEAD == 2) load_frags(blk(1), fb);
+  // One barrier per block: step i's K tile sits in buffer i & 1 (stored
+  // during the previous step), and the step stores step i + 1's tile into
   // the other buffer, which every wave finished reading before the barrier.
-  auto body = [&](int kt, const CT8 (&cur)[8], CT8 (&nn)[8]) {
+  auto body = [&](int i, const CT8 (&cur)[8], CT8 (&nn)[8]) {
     __syncthreads();
-    kst.store(Ks + ((kt + 1) & 1) * BN * KP, KP, tid);
-    // Both prefetches are unconditional (clamped to the last block, whose
+    kst.store(Ks + ((i + 1) & 1) * BN * KP, KP, tid);
+    // Both prefetches are unconditional (clamped to the last step, whose
     // data is then unused), so every path issues the same loads and the
     // wait for the K tile above does not also wait for the dS prefetch.
-    kst.load(K + kbase, a.k_stride[1], min(kt + 2, kt_end - 1) * BN, s.klen, tid);
-    load_frags(min(kt + AHEAD, kt_end - 1), nn);
-    const CT* Kc = Ks + (kt & 1) * BN * KP;
+    kst.load(K + kbase, a.k_stride[1], blk(i + 2) * BN, s.klen, tid);
+    load_frags(blk(i + AHEAD), nn);
+    const CT* Kc = Ks + (i & 1) * BN * KP;
+    const int kt = blk(i);
     if (kt >= my_first && kt <= my_last) {
 #pragma unroll
       for (int t = 0; t < 8; ++t)
@@ -858,15 +864,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
     }
   };
   if constexpr (AHEAD == 2) {
-    for (int kt = kt_begin; kt < kt_end; kt += 3) {
-      body(kt, fa, fc);
-      if (kt + 1 < kt_end) body(kt + 1, fb, fa);
-      if (kt + 2 < kt_end) body(kt + 2, fc, fb);
+    for (int i = 0; i < nblk; i += 3) {
+      body(i, fa, fc);
+      if (i + 1 < nblk) body(i + 1, fb, fa);
+      if (i + 2 < nblk) body(i + 2, fc, fb);
     }
   } else {
-    for (int kt = kt_begin; kt < kt_end; kt += 2) {
-      body(kt, fa, fb);
-      if (kt + 1 < kt_end) body(kt + 1, fb, fa);
+    for (int i = 0; i < nblk; i += 2) {
+      body(i, fa, fb);
+      if (i + 1 < nblk) body(i + 1, fb, fa);
     }
   }
   if (a.dq_direct) {
