@@ -742,9 +742,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   const int kvh = h / a.group;
   const int z = blockIdx.z;
   const Seq s = load_seq(a, z);
-  // Heaviest tiles first (the last query tiles see the most key blocks):
-  // workgroups dispatched together then walk the K blocks from the first
-  // one at the same pace and share them in L2.
+  // Heaviest tiles first (the last query tiles see the most key blocks), so
+  // the launch ends on light workgroups; the key blocks are walked from the
+  // last one down (see the loop below).
   const int ut0 = 4 * (int)(gridDim.y - 1 - blockIdx.y);
   const int ut = ut0 + (wave >> 1);
   const int qb2 = wave & 1;
