@@ -724,8 +724,9 @@ __device__ __forceinline__ void dq_block_range(const AttnArgs& a, const Seq& s, 
   }
 }
 
-// DC: dQ columns per workgroup (the whole head dim up to 256; the 512 dim
-// runs two column chunks, each reading the same dS tiles).
+// DC: dQ columns per workgroup (the whole head dim up to 256 and 256 of
+// 512 with 2-byte inputs, 128 for fp32 inputs from head dim 256 on); the
+// column chunks of a head each read the same dS tiles.
 template <int DQK, int DC, typename TIn, typename TOut>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const AttnArgs a) {
   constexpr int BN = 128, NT = 512, NDK = DC / 32;
