@@ -138,8 +138,8 @@ def test_thd_one_percent_scale_error_is_rejected():
 
 def test_thd_malformed_metadata_sets_flag_and_skips_sequence():
     """A sequence whose visible length exceeds its physical span is treated
-    as empty (nothing read or written) and the workspace flag is raised; the
-    other sequences are still computed."""
+    as empty (none of its outputs written, nothing read out of bounds) and
+    the workspace flag is raised; the other sequences are still computed."""
     d = dev()
     hq, dd = 2, 64
     cu = np.array([0, 64, 128], np.int32)
