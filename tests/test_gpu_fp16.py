@@ -133,3 +133,54 @@ def test_fp16_merge_and_pack():
     torch.cuda.synchronize()
     assert torch.equal(o2.view(torch.int16), o.view(torch.int16))
     assert torch.equal(l2.view(torch.int32), l.view(torch.int32))
+
+
+def test_fp16_thd_documents_and_padding():
+    """Packed THD with fp16 I/O: seven documents at a 64-row pitch (one
+    empty, one of one row, GQA 4/2, D128), NaN in every padding input row,
+    sentinels in every padding output row; real rows meet the criterion
+    against the fp16-rounded oracle and the padding rows stay untouched."""
+    used = np.array([37, 0, 130, 1, 200, 64, 5], np.int32)
+    pitch = 64
+    cu = np.concatenate([[0], np.cumsum([max(1, (n + pitch - 1) // pitch) * pitch
+                                         for n in used])]).astype(np.int32)
+    T, hq, hkv, dd = int(cu[-1]), 4, 2, 128
+    g = torch.Generator().manual_seed(71)
+    q, k, v, do = (torch.randn(T, h_, dd, generator=g) for h_ in (hq, hkv, hkv, hq))
+    pad = np.concatenate([np.arange(cu[n] + used[n], cu[n + 1]) for n in range(len(used))]
+                         ).astype(np.int64)
+    d = dev()
+    qi, ki, vi, doi = (x.to(H).to(d) for x in (q, k, v, do))
+    for t in (qi, ki, vi, doi):
+        t[pad] = float("nan")
+    vl = cpa.Varlen(torch.tensor(cu, device=d), torch.tensor(cu, device=d),
+                    torch.tensor(used, device=d), torch.tensor(used, device=d),
+                    int(used.max()), int(used.max()))
+    sent = 0x7E01   # a NaN pattern the kernels never produce
+    fill = lambda shape: torch.full(shape, sent, dtype=torch.int16, device=d).view(H)
+    o, dq, dk, dv_ = fill((T, hq, dd)), fill((T, hq, dd)), fill((T, hkv, dd)), fill((T, hkv, dd))
+    lse = torch.empty(hq, T, dtype=torch.float32, device=d)
+    scale = 1 / math.sqrt(dd)
+    say("fp16 thd fwd")
+    cpa.attn_fwd(qi, ki, vi, o, lse, varlen=vl, scale=scale)
+    say("fp16 thd bwd")
+    cpa.attn_bwd(qi, ki, vi, o, doi, lse, dq, dk, dv_, varlen=vl, scale=scale)
+    torch.cuda.synchronize()
+    for t in (o, dq, dk, dv_):
+        assert (t.view(torch.int16).cpu().numpy()[pad] == np.int16(sent)).all()
+    ref = {}
+    for kind, f in (("true", true64), ("naive", naive16)):
+        oo, ll = oracle.thd_forward(f(q), f(k), f(v), scale, cu, cu, used, used)
+        a, b_, c = oracle.thd_backward(f(q), f(k), f(v), f(do), scale, cu, cu, used, used)
+        ref[kind] = dict(o=oo, lse=ll, dq=a, dk=b_, dv=c)
+    real = np.ones(T, bool)
+    real[pad] = False
+    log = {}
+    for name, val, h_ in (("O", o, hq), ("dq", dq, hq), ("dk", dk, hkv), ("dv", dv_, hkv)):
+        key = "o" if name == "O" else name
+        criteria.check(name, val, ref["true"][key], ref["naive"][key], grad=name != "O",
+                       mask=np.broadcast_to(real[:, None, None], (T, h_, dd)), log=log,
+                       out_bf16="fp16")
+    criteria.check_lse("LSE", lse, ref["true"]["lse"], ref["naive"]["lse"],
+                       mask=np.broadcast_to(real[None], (hq, T)), log=log)
+    print("fp16 thd", {k_: round(v_["ratio"], 3) for k_, v_ in log.items() if "ratio" in v_})
