@@ -158,3 +158,57 @@ def test_thd_malformed_metadata_sets_flag_and_skips_sequence():
     assert cpa.workspace_error_flag(ws) == 1
     assert (bits(o)[64:] == np.int16(SENT_BF16)).all()
     assert not (bits(o)[:40] == np.int16(SENT_BF16)).any()
+
+
+@pytest.mark.parametrize("d", [256, 512])
+def test_thd_large_head_dims(d):
+    """Packed THD through the head-dim 256/512 kernels (scores and dS tiles
+    materialised per document): five documents at a 64-row pitch (one
+    empty, one of one row, one longer than a 128-row tile), GQA 4/2, NaN in
+    the padding input rows, padding output rows untouched."""
+    used = np.array([150, 0, 1, 70, 260], np.int32)
+    pitch = 64
+    cu = np.concatenate([[0], np.cumsum([max(1, (n + pitch - 1) // pitch) * pitch
+                                         for n in used])]).astype(np.int32)
+    T, hq, hkv = int(cu[-1]), 4, 2
+    g = torch.Generator().manual_seed(80 + d)
+    q, k, v, do = (torch.randn(T, h_, d, generator=g) for h_ in (hq, hkv, hkv, hq))
+    pad = _pad_rows(cu, used)
+    dv0 = dev()
+    qi, ki, vi, doi = (x.to(torch.bfloat16).to(dv0) for x in (q, k, v, do))
+    for t in (qi, ki, vi, doi):
+        t[pad] = float("nan")
+    vl = cpa.Varlen(torch.tensor(cu, device=dv0), torch.tensor(cu, device=dv0),
+                    torch.tensor(used, device=dv0), torch.tensor(used, device=dv0),
+                    int(used.max()), int(used.max()))
+    o = _sentinel((T, hq, d), torch.bfloat16, dv0)
+    lse = _sentinel((hq, T), torch.float32, dv0)
+    dq = _sentinel((T, hq, d), torch.bfloat16, dv0)
+    dk = _sentinel((T, hkv, d), torch.bfloat16, dv0)
+    dvv = _sentinel((T, hkv, d), torch.bfloat16, dv0)
+    scale = 1 / math.sqrt(d)
+    say(f"thd d{d} fwd")
+    ws = cpa.attn_fwd(qi, ki, vi, o, lse, varlen=vl, scale=scale)
+    say(f"thd d{d} bwd")
+    ws2 = cpa.attn_bwd(qi, ki, vi, o, doi, lse, dq, dk, dvv, varlen=vl, scale=scale)
+    torch.cuda.synchronize()
+    assert cpa.workspace_error_flag(ws) == 0 and cpa.workspace_error_flag(ws2) == 0
+    for t in (o, dq, dk, dvv):
+        assert (bits(t)[pad] == np.int16(SENT_BF16)).all()
+    assert (bits(lse)[:, pad] == np.int32(SENT_F32)).all()
+    ref = {}
+    for kind, f in (("true", true64), ("naive", naive64)):
+        oo, ll = oracle.thd_forward(f(q), f(k), f(v), scale, cu, cu, used, used)
+        a, b_, c = oracle.thd_backward(f(q), f(k), f(v), f(do), scale, cu, cu, used, used)
+        ref[kind] = dict(o=oo, lse=ll, dq=a, dk=b_, dv=c)
+    real = np.ones(T, bool)
+    real[pad] = False
+    log = {}
+    for name, val, h_ in (("O", o, hq), ("dq", dq, hq), ("dk", dk, hkv), ("dv", dvv, hkv)):
+        key = "o" if name == "O" else name
+        criteria.check(name, val, ref["true"][key], ref["naive"][key], grad=name != "O",
+                       mask=np.broadcast_to(real[:, None, None], (T, h_, d)), log=log,
+                       out_bf16=True)
+    criteria.check_lse("LSE", lse, ref["true"]["lse"], ref["naive"]["lse"],
+                       mask=np.broadcast_to(real[None], (hq, T)), log=log)
+    print(f"thd d{d}", {k_: round(v_["ratio"], 3) for k_, v_ in log.items() if "ratio" in v_})
