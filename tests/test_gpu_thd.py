@@ -160,19 +160,21 @@ def test_thd_malformed_metadata_sets_flag_and_skips_sequence():
     assert not (bits(o)[:40] == np.int16(SENT_BF16)).any()
 
 
-@pytest.mark.parametrize("d", [256, 512])
-def test_thd_large_head_dims(d):
-    """Packed THD through the head-dim 256/512 kernels (scores and dS tiles
-    materialised per document): five documents at a 64-row pitch (one
-    empty, one of one row, one longer than a 128-row tile), GQA 4/2, NaN in
-    the padding input rows, padding output rows untouched."""
+@pytest.mark.parametrize("dqk,d", [(192, 128), (256, 256), (512, 512)])
+def test_thd_large_head_dims(dqk, d):
+    """Packed THD at head dims 192/128 (the key-outer kernel of the CP rank
+    shape) and 256/512 (scores and dS tiles materialised per document): five
+    documents at a 64-row pitch (one empty, one of one row, one longer than
+    a 128-row tile), GQA 4/2, NaN in the padding input rows, padding output
+    rows untouched."""
     used = np.array([150, 0, 1, 70, 260], np.int32)
     pitch = 64
     cu = np.concatenate([[0], np.cumsum([max(1, (n + pitch - 1) // pitch) * pitch
                                          for n in used])]).astype(np.int32)
     T, hq, hkv = int(cu[-1]), 4, 2
-    g = torch.Generator().manual_seed(80 + d)
-    q, k, v, do = (torch.randn(T, h_, d, generator=g) for h_ in (hq, hkv, hkv, hq))
+    g = torch.Generator().manual_seed(80 + dqk + d)
+    q, k, v, do = (torch.randn(T, h_, w_, generator=g)
+                   for h_, w_ in ((hq, dqk), (hkv, dqk), (hkv, d), (hq, d)))
     pad = _pad_rows(cu, used)
     dv0 = dev()
     qi, ki, vi, doi = (x.to(torch.bfloat16).to(dv0) for x in (q, k, v, do))
@@ -183,13 +185,13 @@ def test_thd_large_head_dims(d):
                     int(used.max()), int(used.max()))
     o = _sentinel((T, hq, d), torch.bfloat16, dv0)
     lse = _sentinel((hq, T), torch.float32, dv0)
-    dq = _sentinel((T, hq, d), torch.bfloat16, dv0)
-    dk = _sentinel((T, hkv, d), torch.bfloat16, dv0)
+    dq = _sentinel((T, hq, dqk), torch.bfloat16, dv0)
+    dk = _sentinel((T, hkv, dqk), torch.bfloat16, dv0)
     dvv = _sentinel((T, hkv, d), torch.bfloat16, dv0)
-    scale = 1 / math.sqrt(d)
-    say(f"thd d{d} fwd")
+    scale = 1 / math.sqrt(dqk)
+    say(f"thd d{dqk}/{d} fwd")
     ws = cpa.attn_fwd(qi, ki, vi, o, lse, varlen=vl, scale=scale)
-    say(f"thd d{d} bwd")
+    say(f"thd d{dqk}/{d} bwd")
     ws2 = cpa.attn_bwd(qi, ki, vi, o, doi, lse, dq, dk, dvv, varlen=vl, scale=scale)
     torch.cuda.synchronize()
     assert cpa.workspace_error_flag(ws) == 0 and cpa.workspace_error_flag(ws2) == 0
@@ -204,11 +206,12 @@ def test_thd_large_head_dims(d):
     real = np.ones(T, bool)
     real[pad] = False
     log = {}
-    for name, val, h_ in (("O", o, hq), ("dq", dq, hq), ("dk", dk, hkv), ("dv", dvv, hkv)):
+    for name, val, h_, w_ in (("O", o, hq, d), ("dq", dq, hq, dqk), ("dk", dk, hkv, dqk),
+                              ("dv", dvv, hkv, d)):
         key = "o" if name == "O" else name
         criteria.check(name, val, ref["true"][key], ref["naive"][key], grad=name != "O",
-                       mask=np.broadcast_to(real[:, None, None], (T, h_, d)), log=log,
+                       mask=np.broadcast_to(real[:, None, None], (T, h_, w_)), log=log,
                        out_bf16=True)
     criteria.check_lse("LSE", lse, ref["true"]["lse"], ref["naive"]["lse"],
                        mask=np.broadcast_to(real[None], (hq, T)), log=log)
-    print(f"thd d{d}", {k_: round(v_["ratio"], 3) for k_, v_ in log.items() if "ratio" in v_})
+    print(f"thd d{dqk}/{d}", {k_: round(v_["ratio"], 3) for k_, v_ in log.items() if "ratio" in v_})
