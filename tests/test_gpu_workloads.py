@@ -92,7 +92,7 @@ def test_cp4_rank_pipeline():
     into their chunk's accumulator in the forward epilogue, the backward over
     both chunks, and the pack/unpack round trip, exactly as the benchmark
     runs them; the merged forward agrees with partials + separate merges to
-    one bf16 ulp, and the step matches the unsplit oracle on one head."""
+    one bf16 ulp, and the step matches the unsplit oracle on two heads."""
     w = workloads.CONFIGS["cp4_rank"]
     x = workloads.draw_inputs(w)
     d = dev()
@@ -123,23 +123,26 @@ def test_cp4_rank_pipeline():
     assert np.array_equal(bits(rs.lse_recv), bits(rs.lse))
     segs = [(c[0], c[2]) for c in chunks]
     qp = oracle.positions_from_segments(w.seqlen_q, segs)
-    h = 7
-    sl = slice(h, h + 1)
-    ref = {}
-    for kind, f in (("true", true64), ("naive", naive64)):
-        a = [f(x[n][0, :, sl]) for n in ("q", "k", "v", "do")]
-        oo, ll = oracle.forward(a[0], a[1], a[2], w.scale, qp)
-        gq, gk, gv = oracle.backward(*a, w.scale, qp)
-        ref[kind] = dict(o=oo, lse=ll, dq=gq, dk=gk, dv=gv)
-    g = dict(o=rs.o[0, :, sl], dq=rs.dq[0, :, sl], dk=rs.dk[0, :, sl], dv=rs.dv[0, :, sl])
-    log = {}
-    _check_all(log, g, ref["true"], ref["naive"], out_bf16=True)
-    criteria.check_lse("lse", rs.lse[0, sl], ref["true"]["lse"], ref["naive"]["lse"], log=log)
-    _report(f"cp4_rank head {h}", log)
-    # keys beyond the last position any query holds get exact zeros: none
-    # here (chunk 7 ends at 32767), but blocks only chunk 7 sees must still
-    # be nonzero for this head
-    assert float(rs.dk[0, 8192:, h].float().abs().max()) > 0
+    # heads 7 and 30 (no GQA here: kv head = query head), whose key blocks
+    # the key kernel runs on different XCDs
+    for h in (7, 30):
+        sl = slice(h, h + 1)
+        ref = {}
+        for kind, f in (("true", true64), ("naive", naive64)):
+            a = [f(x[n][0, :, sl]) for n in ("q", "k", "v", "do")]
+            oo, ll = oracle.forward(a[0], a[1], a[2], w.scale, qp)
+            gq, gk, gv = oracle.backward(*a, w.scale, qp)
+            ref[kind] = dict(o=oo, lse=ll, dq=gq, dk=gk, dv=gv)
+        g = dict(o=rs.o[0, :, sl], dq=rs.dq[0, :, sl], dk=rs.dk[0, :, sl], dv=rs.dv[0, :, sl])
+        log = {}
+        _check_all(log, g, ref["true"], ref["naive"], out_bf16=True)
+        criteria.check_lse("lse", rs.lse[0, sl], ref["true"]["lse"], ref["naive"]["lse"],
+                           log=log)
+        _report(f"cp4_rank head {h}", log)
+        # keys beyond the last position any query holds get exact zeros:
+        # none here (chunk 7 ends at 32767), but blocks only chunk 7 sees
+        # must still be nonzero for this head
+        assert float(rs.dk[0, 8192:, h].float().abs().max()) > 0
 
 
 def test_thd_gqa_full():
